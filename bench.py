@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunk-attention hot path on one MI355X.
+
+Workload: the Wan-1.3B-shaped layer -- 12 heads, d = 128, a 3-frame query
+chunk (4680 tokens) against a 21-frame KV cache (32760 tokens), bf16 inputs
+N(0,1) with a per-head scale in [0.5, 2] on Q and K, seed 0, resident in HBM.
+
+One step = one pass over every step of the path on that batch:
+  1. dense chunk attention -> O (bf16), LSE
+  2. local branch (sink + chunk frames) and history branch (frames 1..17) as
+     block-list attention with float32 outputs, then the LSE merge -> O, LSE
+  3. block-sparse path: block means of Q and K, chunk-mean query, top-C
+     persistent history blocks, top-K local blocks (K = 12.5 % of 75),
+     block-list assembly, block-list attention -> O, LSE
+
+`value` is the step's algorithmic attention FLOPs (4 d per query-key score
+over every key set attended) divided by the step time.  The roofline entry
+is the dense attention kernel (the dominant kernel), timed with HIP events on
+the launch stream over the timed steps.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "kv_cache_attention_chunk_amd", "csrc", "attn_fwd.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_dense_wan_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per dense launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("attn_fwd_sha256_16") != src_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    dense workload: all 12 heads, the first R query rows, R sized to take
+    about target_s seconds.  Returns the baseline record."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    Q, K, V = w.q.f32, w.k.f32, w.v.f32
+    t0 = time.perf_counter()
+    oracle.chunk_attn_dense(Q, K, V, w.scale, rows=np.arange(16), heads=[0])
+    per_row_head = (time.perf_counter() - t0) / 16
+    rows = int(max(16, min(w.Nq, target_s / max(per_row_head * w.H, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.chunk_attn_dense(Q, K, V, w.scale, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * rows * w.Nkv * w.H
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"dense attention, all {w.H} heads, first {rows} of {w.Nq} query rows vs "
+                      f"{w.Nkv} keys, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--topk-ratio", type=float, default=0.125)
+    ap.add_argument("--only", choices=["step", "dense"], default="step",
+                    help="'dense' times the dense kernel alone (for counter runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import kv_cache_attention_chunk_amd as ca
+    from kv_cache_attention_chunk_amd import workloads as wl
+    from kv_cache_attention_chunk_amd import _lib
+    _lib.lib()
+
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    w = wl.wan_dense(seed=0)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    dev = lambda t: torch.from_numpy(t.bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    B, H, Nq, Nkv, d = w.B, w.H, w.Nq, w.Nkv, w.d
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    o_dense = torch.empty_like(q)
+    l_dense = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    branch = []
+    for key in ("local_blocks", "history_blocks"):
+        blocks = np.array(w.meta[key], np.int32)
+        branch.append((i32(np.arange(B * H + 1) * len(blocks)), i32(np.tile(blocks, B * H)),
+                       torch.empty((B, Nq, H, d), dtype=torch.float32, device="cuda"),
+                       torch.empty((B, H, Nq), dtype=torch.float32, device="cuda"), len(blocks)))
+    o_merge = torch.empty_like(q)
+    l_merge = torch.empty_like(l_dense)
+    lay = wl.sparse_layout(w, args.topk_ratio)
+
+    def dense():
+        ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_dense, lse=l_dense)
+
+    def merged():
+        for ip, ix, ob, lb, _ in branch:
+            ca.chunk_attn_fwd(q, k, v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
+                              q_block=Nq, q_seg=Nq, scale=w.scale, out_dtype=torch.float32,
+                              out=ob, lse=lb)
+        ca.lse_merge(branch[0][2], branch[0][3], branch[1][2], branch[1][3], out=o_merge,
+                     out_lse=l_merge)
+
+    def sparse():
+        return ca.block_sparse_fwd(q, k, v, sink_begin=0, sink_count=lay["sink_count"],
+                                   hist_begin=lay["hist_begin"], hist_count=lay["hist_count"],
+                                   C=lay["C"], local_begin=lay["local_begin"],
+                                   local_count=lay["local_count"], K=lay["K"], block=64,
+                                   seg=1560, scale=w.scale)
+
+    # algorithmic FLOPs: 4 d per (query, key) score of every key set attended
+    f_dense = 4.0 * d * Nq * Nkv * B * H
+    f_merge = 4.0 * d * Nq * B * H * sum(
+        int(np.minimum(64, 1560 - 64 * (np.array(w.meta[key]) % 25)).sum())
+        for key in ("local_blocks", "history_blocks"))
+    _, _, info = sparse()
+    torch.cuda.synchronize()
+    ip = info["indptr"].cpu().numpy()
+    ix = info["indices"].cpu().numpy()[:ip[-1]]
+    def block_len(j):           # frame-aligned tiling: 25 blocks per 1560-token frame
+        r = j % 25
+        return np.minimum(64, 1560 - 64 * r)
+    toks = np.array([block_len(ix[ip[r]:ip[r + 1]]).sum() for r in range(len(ip) - 1)])
+    nqb = ca.num_blocks(Nq, 64, 1560)
+    qlen = np.tile(block_len(np.arange(nqb)), B * H)
+    f_sparse = 4.0 * d * float((toks * qlen).sum())
+    f_step = f_dense + f_merge + f_sparse if args.only == "step" else f_dense
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dense()
+        if args.only == "step":
+            merged()
+            sparse()
+    torch.cuda.synchronize()
+
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(n):
+        ev[i][0].record(stream)
+        dense()
+        ev[i][1].record(stream)
+        if args.only == "step":
+            merged()
+            ev[i][2].record(stream)
+            sparse()
+            ev[i][3].record(stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    total_ms = g0.elapsed_time(g1)
+    ms_step = total_ms / n
+    t_dense = sum(e[0].elapsed_time(e[1]) for e in ev) / n
+    res = {"dense_ms": t_dense}
+    if args.only == "step":
+        res["merge_variant_ms"] = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+        res["sparse_path_ms"] = sum(e[2].elapsed_time(e[3]) for e in ev) / n
+    log(f"timed {n} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / n:.3f}), {res}")
+
+    achieved = f_dense / (t_dense * 1e-3) / 1e12
+    kv_bytes = 2.0 * Nkv * H * d * 2 * B
+    traffic = traffic_from_counters()
+    out = {
+        "metric": "attn TFLOP/s + KV GB/s (% roofline), 4680q×32760kv chunk, 12 heads d128",
+        "value": round(f_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan1.3b-shaped chunk attention layer: H=12, d=128, "
+                               "Nq=4680 (3 frames), Nkv=32760 (21 frames), bf16 N(0,1), "
+                               "per-head Q/K scale U[0.5,2], seed 0",
+                   "global_batch": B, "seq_len": Nkv, "parallelism": "none",
+                   "step": ("dense + local/history merge + block-sparse(K=%d, C=%d)"
+                            % (lay["K"], lay["C"])) if args.only == "step" else "dense only",
+                   "step_gflop": round(f_step / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_fwd_kernel<128,4,dense,bf16>",
+                     "avg_launch_ms": round(t_dense, 4)},
+        "kv_gbs": {"dense": round(kv_bytes / (t_dense * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(kv_bytes / (t_dense * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "breakdown_ms": {k_: round(v_, 4) for k_, v_ in res.items()},
+        "phase_tflops": {"dense": round(achieved, 1)},
+    }
+    if args.only == "step":
+        out["phase_tflops"]["merge_variant"] = round(f_merge / (res["merge_variant_ms"] * 1e-3) / 1e12, 1)
+        out["phase_tflops"]["sparse_path"] = round(f_sparse / (res["sparse_path_ms"] * 1e-3) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

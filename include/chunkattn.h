@@ -1,0 +1,205 @@
+/*
+ * chunkattn — chunk attention of a streaming video generator's new latent-frame
+ * chunk against its KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Every tensor argument is a DEVICE pointer owned by the caller
+ * unless marked "host".  Every call is asynchronous on `stream` (a hipStream_t;
+ * NULL = the null stream), never synchronises, never allocates device memory
+ * and keeps no state between calls besides the thread-local error text.
+ *
+ * Element types: CA_BF16 = bfloat16 (round-to-nearest-even on output),
+ * CA_F32 = IEEE float32.  LSE is always float32, natural log.
+ *
+ * Layouts.  Q, K, V and O are 4-D [B, N, H, d] described by a host array of
+ * three element strides {stride_b, stride_n, stride_h}; the d axis is
+ * contiguous (stride 1).  LSE is a contiguous float32 [B, H, Nq] array.
+ *
+ * Alignment: base pointers 16-byte aligned; every stride must keep each
+ * row start 16-byte aligned (a multiple of 8 elements for bf16, of 4 for f32).
+ *
+ * Errors.  Arguments are checked on the host before any device call; a bad
+ * argument returns CA_EINVAL / CA_EUNSUPPORTED / CA_ERANGE and launches
+ * nothing.  No visible GPU returns CA_ENODEV.  A failed launch returns CA_EHIP.
+ * ca_last_error() then holds a message for the calling thread.  Outputs are
+ * undefined after an error.  Contents of device index arrays (CSR ids,
+ * cu_seqlens) cannot be checked without synchronising: ids outside the valid
+ * range and spans outside the flat buffers are skipped by the kernels (they
+ * contribute no keys), they never cause an out-of-bounds access.
+ */
+#ifndef CHUNKATTN_H
+#define CHUNKATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CA_ABI_VERSION 1
+
+enum ca_status {
+  CA_OK = 0,
+  CA_EINVAL = 1,        /* null or misaligned pointer, bad shape or stride */
+  CA_EUNSUPPORTED = 2,  /* head dim or dtype the kernels do not cover */
+  CA_ERANGE = 3,        /* K larger than the candidates, tiling too large */
+  CA_ENODEV = 4,        /* no HIP device visible */
+  CA_EHIP = 5           /* a HIP launch failed; see ca_last_error() */
+};
+
+enum ca_dtype { CA_BF16 = 0, CA_F32 = 1 };
+
+/* per-head cache mode for ca_chunk_attn_mixed_fwd */
+enum ca_head_mode { CA_MODE_DENSE = 0, CA_MODE_BLOCKS = 1, CA_MODE_VARLEN = 2 };
+
+int ca_abi_version(void);
+const char* ca_status_str(int status);
+const char* ca_last_error(void);
+
+/*
+ * Number of blocks of the frame-aligned tiling of n_tokens: the token axis is
+ * cut into segments of seg_len tokens (the last may be shorter) and each
+ * segment into blocks of block_size tokens (the last block of a segment takes
+ * the remainder).  Block id j covers tokens [start_j, start_j + len_j).
+ * Blocks are the spatio-temporal blocks of the Sparse Forcing page, section 2
+ * item 2 (blockified compression); with seg_len = 1560 a latent frame is 24
+ * blocks of 64 plus one block of 24.  Host-only; returns -1 on bad sizes.
+ */
+int ca_num_blocks(int n_tokens, int block_size, int seg_len);
+
+/*
+ * Chunk attention, dense or block-list cache.  For each (b, h) and query row i
+ * over its key set I:
+ *   O[b,i,h,:] = sum_{j in I} softmax_j(scale * q_i . k_j) v_j
+ *   LSE[b,h,i] = ln sum_{j in I} exp(scale * q_i . k_j)
+ * (attention with its LSE state: ISPA page, section 2 item 1, decomposable
+ * attention; block lists: Sparse Forcing page, section 2 item 3, PBSA — dense
+ * over persistent blocks, top-K blocks of the local window).
+ *
+ *   q            bf16 [B, Nq, H, d], strides q_strides (host, 3 elements)
+ *   k, v         bf16 [B, Nkv, H, d], both with strides kv_strides (host);
+ *                may be NULL when Nkv = 0 (every key set empty)
+ *   d            64 or 128
+ *   kv_indptr,   NULL, NULL  -> dense: I = all Nkv cached tokens.
+ *   kv_indices   else CSR over rows (b*H + h)*NQB + qb, NQB =
+ *                ca_num_blocks(Nq, q_block, q_seg): row r lists KV block ids
+ *                (tiling kv_block, kv_seg of the Nkv axis) whose tokens are the
+ *                key set of the rows of query block qb.  int32, device.
+ *                kv_indptr has B*H*NQB + 1 entries, nondecreasing from 0.
+ *                Ids must be distinct within a row; order is free.
+ *   kv_nnz       number of entries of kv_indices; row spans are clamped to it.
+ *   kv_block     1..64; kv_seg >= 1; q_block >= 1; q_seg >= 1 (block mode)
+ *   scale        softmax scale (1/sqrt(d) for the pages' models)
+ *   o            [B, Nq, H, d] of o_dtype (CA_BF16 or CA_F32), strides o_strides
+ *   lse          float32 [B, H, Nq]; an empty key set gives O = 0, LSE = -inf
+ */
+int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
+                      int B, int H, int Nq, int Nkv, int d,
+                      const int64_t* q_strides, const int64_t* kv_strides,
+                      const int64_t* o_strides,
+                      const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
+                      int kv_block, int kv_seg, int q_block, int q_seg,
+                      float scale, void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * Chunk attention over ragged per-head caches (Pyramid Forcing page, section
+ * 3, ragged-cache attention): head (b, h) owns rows
+ * [cu_seqlens[b*H+h], cu_seqlens[b*H+h+1]) of the flat K/V buffers, no padding.
+ *
+ *   k_flat, v_flat  bf16 [total_kv, d], row stride kv_row_stride elements;
+ *                   may be NULL when total_kv = 0
+ *   cu_seqlens      int32 [B*H + 1], device, nondecreasing, cu[0] = 0,
+ *                   cu[B*H] <= total_kv
+ *   cu_seqlens_host optional host copy (NULL allowed): when given, heads are
+ *                   scheduled longest first.
+ * Other arguments as in ca_chunk_attn_fwd.
+ */
+int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_flat,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int total_kv, int B, int H, int Nq, int d,
+                             const int64_t* q_strides, int64_t kv_row_stride,
+                             const int64_t* o_strides, float scale,
+                             void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * Mixed per-head cache modes in one call (Pyramid Forcing page, section 3:
+ * heads with different cache layouts served together to cut launches).
+ * head_mode (host, int32 [B*H]) picks CA_MODE_DENSE (k, v dense cache),
+ * CA_MODE_BLOCKS (k, v + the CSR, as in ca_chunk_attn_fwd; rows of other heads
+ * are ignored) or CA_MODE_VARLEN (k_flat, v_flat + cu_seqlens, as in
+ * ca_chunk_attn_varlen_fwd; other heads' spans are ignored).  Pointers of a
+ * mode no head uses may be NULL.
+ */
+int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v,
+                            int B, int H, int Nq, int Nkv, int d,
+                            const int64_t* q_strides, const int64_t* kv_strides,
+                            const int64_t* o_strides, const int32_t* head_mode,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int kv_nnz, int kv_block, int kv_seg, int q_block, int q_seg,
+                            const void* k_flat, const void* v_flat,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                            int total_kv, int64_t kv_row_stride, float scale,
+                            void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * LSE merge of two attention results over disjoint key sets (ISPA page,
+ * section 2 item 1: local and history branches recombined afterwards):
+ *   M = max(L1, L2), w_k = exp(L_k - M), LSE = M + ln(w1 + w2),
+ *   O = (w1 O1 + w2 O2) / (w1 + w2);  both branches -inf -> O = 0, LSE = -inf.
+ *   o1, o2   [B, N, H, d] of in_dtype, strides o1_strides / o2_strides (host)
+ *   lse1,2   float32 [B, H, N]
+ *   o, lse   outputs, out_dtype / float32.  o may alias o1 (same strides and
+ *            dtype) and lse may alias lse1; no other overlap is allowed.
+ *   d        8, 16, 32, 64, 128, 256 or 512
+ */
+int ca_lse_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                 int in_dtype, void* o, float* lse, int out_dtype,
+                 int B, int H, int N, int d,
+                 const int64_t* o1_strides, const int64_t* o2_strides,
+                 const int64_t* o_strides, void* stream);
+
+/*
+ * Block representatives (Sparse Forcing page, section 2 item 2: each block is
+ * compressed to one representative token for coarse scoring): the mean of
+ * each block's tokens, accumulated in float32.
+ *   x    bf16 [B, N, H, d], strides x_strides (host); d a multiple of 8, <= 512
+ *   out  float32 [B, H, NB, d] contiguous, NB = ca_num_blocks(N, block, seg)
+ */
+int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_strides,
+                  int block_size, int seg_len, float* out, void* stream);
+
+/*
+ * Coarse block scores and top-K (Sparse Forcing page, section 2 items 1-2:
+ * scoring on block representatives, top-C persistent blocks, top-K local
+ * blocks).  score(qb, c) = <q_mean[b,h,qb,:], k_mean[b,h,c,:]> in float32 for
+ * candidates c in [cand_begin, cand_begin + cand_count); the K highest per
+ * (b, h, qb) are kept, equal scores resolved toward the lower block id, and
+ * written in ascending id order.
+ *   q_mean   float32 [B, H, NQB, d] contiguous; k_mean float32 [B, H, NKB, d]
+ *   out_idx  int32 [B, H, NQB, K] (absolute block ids, ascending)
+ *   out_score optional float32 [B, H, NQB, K] (score of each out_idx entry)
+ *   limits   1 <= K <= cand_count <= 4096, cand range inside [0, NKB), d <= 512
+ */
+int ca_block_score_topk(const float* q_mean, const float* k_mean,
+                        int B, int H, int NQB, int NKB, int d,
+                        int cand_begin, int cand_count, int K,
+                        int32_t* out_idx, float* out_score, void* stream);
+
+/*
+ * PBSA block lists (Sparse Forcing page, section 2 item 3): CSR row
+ * (b*H + h)*NQB + qb = sorted union, duplicates removed, of the sink blocks
+ * [sink_begin, sink_begin + sink_count), persistent[b,h,:] (C ids, ascending,
+ * may be NULL with C = 0) and topk_offset + topk[b,h,qb,:] (K ids, ascending,
+ * may be NULL with K = 0).
+ *   indptr   int32 [B*H*NQB + 1]   indices int32, room for
+ *            B*H*NQB*(sink_count + C + K) entries.
+ * B*H*NQB at most 65536.
+ */
+int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
+                      const int32_t* persistent, int C, const int32_t* topk, int K,
+                      int topk_offset, int32_t* indptr, int32_t* indices, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKATTN_H */

@@ -1,0 +1,17 @@
+"""MI355X-native chunk attention over a streaming video generator's KV cache.
+
+The calls below bind the C ABI of libchunkattn.so (include/chunkattn.h):
+dense / block-list / ragged / mixed-mode chunk attention emitting O and LSE,
+the LSE merge of a local and a history branch, block means, coarse block
+scoring with top-K, and PBSA block-list assembly.  Importing this package does
+not load the library; the first call does, and fails if it is not built.
+"""
+from .api import (  # noqa: F401
+    block_mean, block_score_topk, block_sparse_fwd, build_kv_index, chunk_attn_fwd,
+    chunk_attn_mixed_fwd, chunk_attn_varlen_fwd, lse_merge, num_blocks,
+)
+
+__all__ = [
+    "chunk_attn_fwd", "chunk_attn_varlen_fwd", "chunk_attn_mixed_fwd", "lse_merge",
+    "block_mean", "block_score_topk", "build_kv_index", "block_sparse_fwd", "num_blocks",
+]

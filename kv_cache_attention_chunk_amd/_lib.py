@@ -1,0 +1,91 @@
+"""ctypes declarations of the libchunkattn.so C ABI (include/chunkattn.h).
+
+The library is loaded on first use from this package's directory.  A missing
+library is an error: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libchunkattn.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "chunkattn.h")
+
+CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
+CA_BF16, CA_F32 = 0, 1
+CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_i64 = ctypes.c_int64
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.c_void_p   # device or host int32 pointers are passed as addresses
+
+SIGNATURES = {
+    "ca_abi_version": (_i, []),
+    "ca_status_str": (ctypes.c_char_p, [_i]),
+    "ca_last_error": (ctypes.c_char_p, []),
+    "ca_num_blocks": (_i, [_i, _i, _i]),
+    "ca_chunk_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
+                               _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p]),
+    "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
+                                      _i64p, _i64, _i64p, _f, _p, _i, _p, _p]),
+    "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
+                                     _i32p, _i32p, _i32p, _i, _i, _i, _i, _i, _p, _p,
+                                     _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _p]),
+    "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
+                          _i64p, _i64p, _i64p, _p]),
+    "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p]),
+    "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "ca_build_kv_index": (_i, [_i, _i, _i, _i, _i, _i32p, _i, _i32p, _i, _i, _p, _p, _p]),
+}
+
+_LIB = None
+
+
+def header_functions():
+    """Names of the functions include/chunkattn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ca_\w+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m kv_cache_attention_chunk_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.ca_abi_version() != 1:
+            raise RuntimeError("libchunkattn ABI version mismatch")
+        _LIB = L
+    return _LIB
+
+
+class ChunkAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status == CA_OK:
+        return
+    msg = lib().ca_last_error().decode(errors="replace")
+    if status in (CA_EINVAL, CA_ERANGE):
+        raise ValueError(f"chunkattn: {msg} (status {status})")
+    if status == CA_EUNSUPPORTED:
+        raise NotImplementedError(f"chunkattn: {msg}")
+    raise ChunkAttnError(status, f"chunkattn: {msg}")
+
+
+def strides3(s) -> ctypes.Array:
+    return (ctypes.c_int64 * 3)(*[int(x) for x in s])

@@ -1,0 +1,298 @@
+"""PyTorch-facing binding of the chunkattn C ABI.
+
+Argument marshalling only: tensors supply device pointers, strides and the
+current HIP stream; outputs are allocated with torch when not given; every
+step of the computation runs in the HIP kernels of libchunkattn.so.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import CA_BF16, CA_F32, check, lib, strides3
+
+_DT = {torch.bfloat16: CA_BF16, torch.float32: CA_F32}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _bshd(name: str, t: torch.Tensor, dtype=torch.bfloat16):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, N, H, d]")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.numel() and t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous last dim")
+    return t
+
+
+def _st(t: torch.Tensor):
+    """(b, n, h) element strides; an empty tensor reports contiguous ones."""
+    if t.numel() == 0:
+        B, N, H, d = t.shape
+        return strides3((N * H * d, H * d, d))
+    return strides3(t.stride()[:3])
+
+
+def _i32(name: str, t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    return t
+
+
+def _out(B, N, H, d, dtype, device, out):
+    if out is None:
+        return torch.empty((B, N, H, d), dtype=dtype, device=device)
+    _bshd("out", out, dtype)
+    if tuple(out.shape) != (B, N, H, d):
+        raise ValueError("out has the wrong shape")
+    return out
+
+
+def _lse_out(B, H, N, device, lse):
+    if lse is None:
+        return torch.empty((B, H, N), dtype=torch.float32, device=device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    return lse
+
+
+def _check_indptr(indptr, BH, Nq, q_block, q_seg):
+    if indptr is None:
+        return
+    rows = BH * num_blocks(Nq, q_block, q_seg or max(Nq, 1))
+    if indptr.numel() != rows + 1:
+        raise ValueError(f"kv_indptr must have B*H*NQB + 1 = {rows + 1} entries")
+
+
+def num_blocks(n_tokens: int, block_size: int, seg_len: int) -> int:
+    r = lib().ca_num_blocks(n_tokens, block_size, seg_len)
+    if r < 0:
+        raise ValueError("bad tiling")
+    return r
+
+
+def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                   kv_indptr: Optional[torch.Tensor] = None,
+                   kv_indices: Optional[torch.Tensor] = None,
+                   kv_block: int = 64, kv_seg: Optional[int] = None,
+                   q_block: int = 64, q_seg: Optional[int] = None,
+                   scale: Optional[float] = None, out_dtype=None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk attention against a dense cache, or against per-query-block
+    block lists (CSR kv_indptr / kv_indices) when given.  Returns (O, LSE).
+    The output dtype is out_dtype, else out's dtype, else bf16."""
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    _bshd("q", q), _bshd("k", k), _bshd("v", v)
+    B, Nq, H, d = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, d) or k.shape != v.shape:
+        raise ValueError("k, v must be [B, Nkv, H, d] matching q")
+    if k.numel() and k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    _i32("kv_indptr", kv_indptr), _i32("kv_indices", kv_indices)
+    _check_indptr(kv_indptr, B * H, Nq, q_block, q_seg)
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nnz = 0 if kv_indices is None else kv_indices.numel()
+    st = lib().ca_chunk_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d,
+        _st(q), _st(k), _st(o),
+        _ptr(kv_indptr), _ptr(kv_indices), nnz, kv_block, kv_seg or max(Nkv, 1),
+        q_block, q_seg or max(Nq, 1), sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+    check(st)
+    return o, l
+
+
+def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.Tensor,
+                          cu_seqlens: torch.Tensor, *, cu_seqlens_host: Optional[np.ndarray] = None,
+                          scale: Optional[float] = None, out_dtype=None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk attention against ragged per-head caches flattened into
+    k_flat / v_flat [total, d] with cu_seqlens [B*H + 1] boundaries."""
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    _bshd("q", q)
+    B, Nq, H, d = q.shape
+    for n, t in (("k_flat", k_flat), ("v_flat", v_flat)):
+        if t.dim() != 2 or t.dtype != torch.bfloat16 or not t.is_cuda or t.shape[1] != d or \
+                (t.numel() and t.stride(1) != 1):
+            raise ValueError(f"{n} must be a bf16 GPU tensor [total, d]")
+    if k_flat.shape != v_flat.shape or (k_flat.numel() and k_flat.stride() != v_flat.stride()):
+        raise ValueError("k_flat and v_flat must match in shape and strides")
+    _i32("cu_seqlens", cu_seqlens)
+    if cu_seqlens.numel() != B * H + 1:
+        raise ValueError("cu_seqlens must have B*H + 1 entries")
+    host = None
+    if cu_seqlens_host is not None:
+        host = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().ca_chunk_attn_varlen_fwd(
+        q.data_ptr(), k_flat.data_ptr(), v_flat.data_ptr(), cu_seqlens.data_ptr(),
+        None if host is None else host.ctypes.data, k_flat.shape[0], B, H, Nq, d,
+        _st(q), k_flat.stride(0) if k_flat.numel() else d, _st(o), sc,
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+    check(st)
+    return o, l
+
+
+def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indptr=None,
+                         kv_indices=None, kv_block: int = 64, kv_seg: Optional[int] = None,
+                         q_block: int = 64, q_seg: Optional[int] = None, k_flat=None, v_flat=None,
+                         cu_seqlens=None, cu_seqlens_host=None, scale: Optional[float] = None,
+                         out_dtype=None, out=None, lse=None):
+    """Per-head cache modes (0 dense, 1 block lists, 2 ragged) in one call."""
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    _bshd("q", q)
+    B, Nq, H, d = q.shape
+    mode = np.ascontiguousarray(head_mode, dtype=np.int32).reshape(-1)
+    if mode.size != B * H:
+        raise ValueError("head_mode must have B*H entries")
+    Nkv = 0
+    if k is not None:
+        _bshd("k", k), _bshd("v", v)
+        Nkv = k.shape[1]
+        if k.stride() != v.stride():
+            raise ValueError("k and v must share strides")
+    _i32("kv_indptr", kv_indptr), _i32("kv_indices", kv_indices), _i32("cu_seqlens", cu_seqlens)
+    _check_indptr(kv_indptr, B * H, Nq, q_block, q_seg)
+    if cu_seqlens is not None and cu_seqlens.numel() != B * H + 1:
+        raise ValueError("cu_seqlens must have B*H + 1 entries")
+    host = None if cu_seqlens_host is None else np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kvs = _st(k) if k is not None else strides3((0, 0, 0))
+    st = lib().ca_chunk_attn_mixed_fwd(
+        q.data_ptr(), _ptr(k), _ptr(v), B, H, Nq, Nkv, d, _st(q), kvs,
+        _st(o), mode.ctypes.data, _ptr(kv_indptr), _ptr(kv_indices),
+        0 if kv_indices is None else kv_indices.numel(), kv_block, kv_seg or max(Nkv, 1),
+        q_block, q_seg or max(Nq, 1), _ptr(k_flat), _ptr(v_flat), _ptr(cu_seqlens),
+        None if host is None else host.ctypes.data,
+        0 if k_flat is None else k_flat.shape[0], d if k_flat is None else k_flat.stride(0),
+        sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+    check(st)
+    return o, l
+
+
+def lse_merge(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor, *,
+              out_dtype=None, out: Optional[torch.Tensor] = None,
+              out_lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Recombine two attention branches over disjoint key sets via their LSE."""
+    if o1.dtype != o2.dtype or o1.dtype not in _DT:
+        raise TypeError("o1 and o2 must share a bf16 or float32 dtype")
+    _bshd("o1", o1, o1.dtype), _bshd("o2", o2, o2.dtype)
+    if o1.shape != o2.shape:
+        raise ValueError("o1 and o2 shapes differ")
+    B, N, H, d = o1.shape
+    for n, t in (("lse1", lse1), ("lse2", lse2)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous float32 [B, H, N]")
+    od = out_dtype or (out.dtype if out is not None else o1.dtype)
+    o = _out(B, N, H, d, od, o1.device, out)
+    l = _lse_out(B, H, N, o1.device, out_lse)
+    st = lib().ca_lse_merge(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(),
+                            _DT[o1.dtype], o.data_ptr(), l.data_ptr(), _DT[od], B, H, N, d,
+                            _st(o1), _st(o2),
+                            _st(o), _stream())
+    check(st)
+    return o, l
+
+
+def block_mean(x: torch.Tensor, block_size: int = 64, seg_len: Optional[int] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block representatives: mean of each block's tokens -> float32 [B, H, NB, d]."""
+    _bshd("x", x)
+    B, N, H, d = x.shape
+    seg = seg_len or max(N, 1)
+    nb = num_blocks(N, block_size, seg)
+    if out is None:
+        out = torch.empty((B, H, nb, d), dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, nb, d) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, H, NB, d]")
+    st = lib().ca_block_mean(x.data_ptr(), B, N, H, d, _st(x), block_size, seg,
+                             out.data_ptr(), _stream())
+    check(st)
+    return out
+
+
+def block_score_topk(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *, cand_begin: int = 0,
+                     cand_count: Optional[int] = None, return_scores: bool = False):
+    """Top-K candidate blocks per query block by representative dot product;
+    ids ascending, ties toward the lower id."""
+    for n, t in (("q_mean", q_mean), ("k_mean", k_mean)):
+        if t.dtype != torch.float32 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 GPU tensor [B, H, N, d]")
+    B, H, NQB, d = q_mean.shape
+    NKB = k_mean.shape[2]
+    if tuple(k_mean.shape) != (B, H, NKB, d):
+        raise ValueError("k_mean shape mismatch")
+    cc = NKB - cand_begin if cand_count is None else cand_count
+    idx = torch.empty((B, H, NQB, K), dtype=torch.int32, device=q_mean.device)
+    sc = torch.empty((B, H, NQB, K), dtype=torch.float32, device=q_mean.device) if return_scores else None
+    st = lib().ca_block_score_topk(q_mean.data_ptr(), k_mean.data_ptr(), B, H, NQB, NKB, d,
+                                   cand_begin, cc, K, idx.data_ptr(), _ptr(sc), _stream())
+    check(st)
+    return (idx, sc) if return_scores else idx
+
+
+def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
+                   persistent: Optional[torch.Tensor], topk: Optional[torch.Tensor],
+                   topk_offset: int = 0, device=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """PBSA block lists: CSR rows = sorted union of sink, persistent, top-K."""
+    C = 0 if persistent is None else persistent.shape[-1]
+    K = 0 if topk is None else topk.shape[-1]
+    _i32("persistent", persistent), _i32("topk", topk)
+    dev = device or (persistent.device if persistent is not None else topk.device)
+    rows = B * H * NQB
+    indptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    indices = torch.empty(max(rows * (sink_count + C + K), 1), dtype=torch.int32, device=dev)
+    st = lib().ca_build_kv_index(B, H, NQB, sink_begin, sink_count, _ptr(persistent), C, _ptr(topk),
+                                 K, topk_offset, indptr.data_ptr(), indices.data_ptr(), _stream())
+    check(st)
+    return indptr, indices
+
+
+def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_begin: int,
+                     sink_count: int, hist_begin: int, hist_count: int, C: int,
+                     local_begin: int, local_count: int, K: int, block: int = 64,
+                     seg: Optional[int] = None, k_mean: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, out_dtype=torch.bfloat16):
+    """The block-sparse path in the Sparse Forcing order: block means of Q and
+    K, persistent blocks = top-C history blocks against the chunk-mean query,
+    top-K local-window blocks per query block, PBSA block lists, attention.
+    `k_mean` may carry precomputed key-block means (resident cache state).
+    Returns (O, LSE, info) with the selected ids and the CSR in `info`."""
+    B, Nq, H, d = q.shape
+    seg = seg or Nq
+    qm = block_mean(q, block, seg)
+    km = block_mean(k, block, seg) if k_mean is None else k_mean
+    cm = block_mean(q, Nq, Nq)
+    pers = block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count) if C else None
+    loc = block_score_topk(qm, km, K, cand_begin=local_begin, cand_count=local_count) if K else None
+    nqb = qm.shape[2]
+    indptr, indices = build_kv_index(B, H, nqb, sink_begin, sink_count,
+                                     None if pers is None else pers[:, :, 0, :].contiguous(),
+                                     loc, 0, device=q.device)
+    o, l = chunk_attn_fwd(q, k, v, kv_indptr=indptr, kv_indices=indices, kv_block=block,
+                          kv_seg=seg, q_block=block, q_seg=seg, scale=scale, out_dtype=out_dtype)
+    return o, l, {"q_mean": qm, "k_mean": km, "chunk_mean": cm, "persistent": pers,
+                  "local": loc, "indptr": indptr, "indices": indices}

@@ -1,0 +1,411 @@
+// C ABI of chunkattn: argument checks, work decomposition and kernel dispatch.
+// Every check runs on the host before any device call; nothing here
+// synchronises or allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "chunkattn.h"
+#include "common.h"
+
+using namespace chunkattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Host-side block count of the frame-aligned tiling.
+int num_blocks(int n, int block, int seg) {
+  if (n < 0 || block <= 0 || seg <= 0) return -1;
+  const int bps = (seg + block - 1) / block;
+  const int full = n / seg;
+  const int rest = n - full * seg;
+  return full * bps + (rest + block - 1) / block;
+}
+
+int check_device() {
+  int n = 0;
+  const hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0) return fail(CA_ENODEV, "no HIP device visible");
+  return CA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Strides of a bf16/f32 [B, N, H, d] tensor: non-negative, 16-byte row starts.
+int check_strides(const char* name, const int64_t* s, int elem_align) {
+  if (!s) return fail(CA_EINVAL, "%s_strides is NULL", name);
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0) return fail(CA_EINVAL, "%s_strides[%d] < 0", name, i);
+    if (s[i] % elem_align) return fail(CA_EINVAL, "%s_strides[%d] not a multiple of %d", name, i, elem_align);
+  }
+  return CA_OK;
+}
+
+struct Common {
+  int B, H, Nq, d;
+  const void* q;
+  const int64_t* qs;
+  const int64_t* os;
+  void* o;
+  int o_dtype;
+  float* lse;
+  float scale;
+};
+
+int check_common(const Common& c) {
+  if (c.B < 0 || c.H < 0 || c.Nq < 0) return fail(CA_EINVAL, "negative size");
+  if ((int64_t)c.B * c.H > 32767) return fail(CA_ERANGE, "B*H above 32767");
+  if (c.d != 64 && c.d != 128) return fail(CA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", c.d);
+  if (c.o_dtype != CA_BF16 && c.o_dtype != CA_F32) return fail(CA_EUNSUPPORTED, "o_dtype %d", c.o_dtype);
+  if (!c.q || !c.o || !c.lse) return fail(CA_EINVAL, "q, o and lse must be non-NULL");
+  if (!aligned16(c.q) || !aligned16(c.o) || !aligned16(c.lse)) return fail(CA_EINVAL, "q, o, lse must be 16-byte aligned");
+  if (int r = check_strides("q", c.qs, 8)) return r;
+  if (int r = check_strides("o", c.os, c.o_dtype == CA_BF16 ? 8 : 4)) return r;
+  if (!(std::isfinite(c.scale))) return fail(CA_EINVAL, "scale not finite");
+  return CA_OK;
+}
+
+void fill_common(AttnParams& p, const Common& c) {
+  p.q = static_cast<const uint16_t*>(c.q);
+  p.o = c.o;
+  p.lse = c.lse;
+  p.qs_b = c.qs[0]; p.qs_n = c.qs[1]; p.qs_h = c.qs[2];
+  p.os_b = c.os[0]; p.os_n = c.os[1]; p.os_h = c.os[2];
+  p.B = c.B; p.H = c.H; p.Nq = c.Nq;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+}
+
+constexpr int kDenseWaves = 4;            // 128 query rows per workgroup
+
+// Launch over a list of heads (or all heads when `heads` is empty), splitting
+// the list into launches of at most kMaxHeadsPerLaunch heads.
+int launch_heads(int mode, const Common& c, AttnParams& p, const std::vector<int>& heads,
+                 hipStream_t stream) {
+  const bool all = heads.empty();
+  const int nh = all ? c.B * c.H : (int)heads.size();
+  int nwaves = kDenseWaves;
+  if (mode == MODE_BLOCKS) {
+    // one workgroup per query block (or 128-row slice of one)
+    int maxq = std::min(std::min(p.q_block, p.q_seg), std::max(c.Nq, 1));
+    nwaves = maxq <= 64 ? 2 : 4;
+    p.q_sub = (maxq + nwaves * 32 - 1) / (nwaves * 32);
+  } else {
+    p.n_qtiles = (c.Nq + kDenseWaves * 32 - 1) / (kDenseWaves * 32);
+  }
+  for (int h0 = 0; h0 < nh; h0 += kMaxHeadsPerLaunch) {
+    const int n = std::min(kMaxHeadsPerLaunch, nh - h0);
+    p.n_heads = n;
+    p.use_list = (all && h0 == 0) ? 0 : 1;
+    if (p.use_list)
+      for (int i = 0; i < n; ++i) p.heads[i] = (int16_t)(all ? h0 + i : heads[h0 + i]);
+    const int64_t per = mode == MODE_BLOCKS ? (int64_t)p.nqb * p.q_sub : p.n_qtiles;
+    const int64_t items = per * n;
+    if (items > 0x7FFFFFFF) return fail(CA_ERANGE, "too many work items");
+    p.n_items = (int)items;
+    const hipError_t e = launch_attention(mode, c.d, nwaves, c.o_dtype == CA_F32, p, stream);
+    if (e != hipSuccess) return launched(e, "chunk attention launch");
+  }
+  return ok();
+}
+
+int check_csr(const int32_t* indptr, const int32_t* indices, int nnz, int kv_block, int kv_seg,
+              int q_block, int q_seg) {
+  if (!indptr || !indices) return fail(CA_EINVAL, "kv_indptr and kv_indices must both be given");
+  if (nnz < 0) return fail(CA_EINVAL, "kv_nnz < 0");
+  if (kv_block < 1 || kv_block > kTileKeys) return fail(CA_ERANGE, "kv_block %d outside 1..%d", kv_block, kTileKeys);
+  if (kv_seg < 1 || q_block < 1 || q_seg < 1) return fail(CA_EINVAL, "tiling sizes must be >= 1");
+  return CA_OK;
+}
+
+void fill_blocks(AttnParams& p, int Nq, int Nkv, const int32_t* indptr, const int32_t* indices,
+                 int nnz, int kv_block, int kv_seg, int q_block, int q_seg) {
+  p.indptr = indptr;
+  p.indices = indices;
+  p.nnz = nnz;
+  p.kv_block = kv_block;
+  p.kv_seg = kv_seg;
+  p.kv_bps = (kv_seg + kv_block - 1) / kv_block;
+  p.nkb = num_blocks(Nkv, kv_block, kv_seg);
+  p.q_block = q_block;
+  p.q_seg = q_seg;
+  p.q_bps = (q_seg + q_block - 1) / q_block;
+  p.nqb = num_blocks(Nq, q_block, q_seg);
+}
+
+std::vector<int> longest_first(const int32_t* cu_host, const std::vector<int>& heads) {
+  std::vector<int> order = heads;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return (cu_host[a + 1] - cu_host[a]) > (cu_host[b + 1] - cu_host[b]);
+  });
+  return order;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ca_abi_version(void) { return CA_ABI_VERSION; }
+
+const char* ca_status_str(int status) {
+  switch (status) {
+    case CA_OK: return "ok";
+    case CA_EINVAL: return "invalid argument";
+    case CA_EUNSUPPORTED: return "unsupported configuration";
+    case CA_ERANGE: return "value out of range";
+    case CA_ENODEV: return "no HIP device";
+    case CA_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* ca_last_error(void) { return g_last_error.c_str(); }
+
+int ca_num_blocks(int n_tokens, int block_size, int seg_len) {
+  return num_blocks(n_tokens, block_size, seg_len);
+}
+
+int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv,
+                      int d, const int64_t* q_strides, const int64_t* kv_strides,
+                      const int64_t* o_strides, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, int kv_nnz, int kv_block, int kv_seg,
+                      int q_block, int q_seg, float scale, void* o, int o_dtype, float* lse,
+                      void* stream) {
+  Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
+  if (int r = check_common(c)) return r;
+  if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
+  if (Nkv > 0 && (!k || !v)) return fail(CA_EINVAL, "k and v must be non-NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
+  if (int r = check_strides("kv", kv_strides, 8)) return r;
+  const bool blocks = kv_indptr || kv_indices;
+  if (blocks) {
+    if (int r = check_csr(kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+  }
+  if (int r = check_device()) return r;
+  if ((int64_t)B * H * Nq == 0) return ok();
+  static thread_local AttnParams p;
+  p = AttnParams{};
+  fill_common(p, c);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+  p.Nkv = Nkv;
+  if (blocks) {
+    fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
+    return launch_heads(MODE_BLOCKS, c, p, {}, static_cast<hipStream_t>(stream));
+  }
+  return launch_heads(MODE_DENSE, c, p, {}, static_cast<hipStream_t>(stream));
+}
+
+int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_flat,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int total_kv, int B, int H, int Nq, int d, const int64_t* q_strides,
+                             int64_t kv_row_stride, const int64_t* o_strides, float scale,
+                             void* o, int o_dtype, float* lse, void* stream) {
+  Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
+  if (int r = check_common(c)) return r;
+  if (!cu_seqlens) return fail(CA_EINVAL, "cu_seqlens must be non-NULL");
+  if (total_kv > 0 && (!k_flat || !v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be non-NULL");
+  if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
+  if (total_kv < 0) return fail(CA_EINVAL, "total_kv < 0");
+  if (kv_row_stride < d || kv_row_stride % 8) return fail(CA_EINVAL, "kv_row_stride must be >= d and a multiple of 8");
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0) return fail(CA_EINVAL, "cu_seqlens[0] != 0");
+    for (int i = 0; i < B * H; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return fail(CA_EINVAL, "cu_seqlens decreasing at %d", i);
+    if (cu_seqlens_host[B * H] > total_kv) return fail(CA_ERANGE, "cu_seqlens[B*H] > total_kv");
+  }
+  if (int r = check_device()) return r;
+  if ((int64_t)B * H * Nq == 0) return ok();
+  static thread_local AttnParams p;
+  p = AttnParams{};
+  fill_common(p, c);
+  p.k = static_cast<const uint16_t*>(k_flat);
+  p.v = static_cast<const uint16_t*>(v_flat);
+  p.ks_b = 0; p.ks_n = kv_row_stride; p.ks_h = 0;
+  p.cu = cu_seqlens;
+  p.total_kv = total_kv;
+  std::vector<int> heads;
+  if (cu_seqlens_host) {
+    std::vector<int> all(B * H);
+    std::iota(all.begin(), all.end(), 0);
+    heads = longest_first(cu_seqlens_host, all);
+  }
+  return launch_heads(MODE_VARLEN, c, p, heads, static_cast<hipStream_t>(stream));
+}
+
+int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq,
+                            int Nkv, int d, const int64_t* q_strides, const int64_t* kv_strides,
+                            const int64_t* o_strides, const int32_t* head_mode,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
+                            int kv_block, int kv_seg, int q_block, int q_seg,
+                            const void* k_flat, const void* v_flat, const int32_t* cu_seqlens,
+                            const int32_t* cu_seqlens_host, int total_kv, int64_t kv_row_stride,
+                            float scale, void* o, int o_dtype, float* lse, void* stream) {
+  Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
+  if (int r = check_common(c)) return r;
+  if (!head_mode) return fail(CA_EINVAL, "head_mode is NULL");
+  std::vector<int> hd, hb, hv;
+  for (int i = 0; i < B * H; ++i) {
+    switch (head_mode[i]) {
+      case CA_MODE_DENSE: hd.push_back(i); break;
+      case CA_MODE_BLOCKS: hb.push_back(i); break;
+      case CA_MODE_VARLEN: hv.push_back(i); break;
+      default: return fail(CA_EINVAL, "head_mode[%d] = %d", i, head_mode[i]);
+    }
+  }
+  if (!hd.empty() || !hb.empty()) {
+    if (!k || !v) return fail(CA_EINVAL, "k and v must be non-NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
+    if (int r = check_strides("kv", kv_strides, 8)) return r;
+    if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
+  }
+  if (!hb.empty()) {
+    if (int r = check_csr(kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+  }
+  if (!hv.empty()) {
+    if (!k_flat || !v_flat || !cu_seqlens) return fail(CA_EINVAL, "k_flat, v_flat, cu_seqlens must be non-NULL");
+    if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
+    if (total_kv < 0) return fail(CA_EINVAL, "total_kv < 0");
+    if (kv_row_stride < d || kv_row_stride % 8) return fail(CA_EINVAL, "kv_row_stride must be >= d and a multiple of 8");
+  }
+  if (int r = check_device()) return r;
+  if ((int64_t)B * H * Nq == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  static thread_local AttnParams p;
+  if (!hv.empty()) {
+    p = AttnParams{};
+    fill_common(p, c);
+    p.k = static_cast<const uint16_t*>(k_flat);
+    p.v = static_cast<const uint16_t*>(v_flat);
+    p.ks_n = kv_row_stride;
+    p.cu = cu_seqlens;
+    p.total_kv = total_kv;
+    if (cu_seqlens_host) hv = longest_first(cu_seqlens_host, hv);
+    if (int r = launch_heads(MODE_VARLEN, c, p, hv, s)) return r;
+  }
+  if (!hd.empty()) {
+    p = AttnParams{};
+    fill_common(p, c);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+    p.Nkv = Nkv;
+    if (int r = launch_heads(MODE_DENSE, c, p, hd, s)) return r;
+  }
+  if (!hb.empty()) {
+    p = AttnParams{};
+    fill_common(p, c);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+    p.Nkv = Nkv;
+    fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
+    if (int r = launch_heads(MODE_BLOCKS, c, p, hb, s)) return r;
+  }
+  return ok();
+}
+
+int ca_lse_merge(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                 int in_dtype, void* o, float* lse, int out_dtype, int B, int H, int N, int d,
+                 const int64_t* o1_strides, const int64_t* o2_strides, const int64_t* o_strides,
+                 void* stream) {
+  if (B < 0 || H < 0 || N < 0) return fail(CA_EINVAL, "negative size");
+  if (d != 8 && d != 16 && d != 32 && d != 64 && d != 128 && d != 256 && d != 512)
+    return fail(CA_EUNSUPPORTED, "head dim %d (supported: 8..512, powers of two)", d);
+  if ((in_dtype != CA_BF16 && in_dtype != CA_F32) || (out_dtype != CA_BF16 && out_dtype != CA_F32))
+    return fail(CA_EUNSUPPORTED, "dtype");
+  if (!o1 || !o2 || !lse1 || !lse2 || !o || !lse) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(o1) || !aligned16(o2) || !aligned16(o)) return fail(CA_EINVAL, "o1, o2, o must be 16-byte aligned");
+  const int ia = in_dtype == CA_BF16 ? 8 : 4, oa = out_dtype == CA_BF16 ? 8 : 4;
+  if (int r = check_strides("o1", o1_strides, ia)) return r;
+  if (int r = check_strides("o2", o2_strides, ia)) return r;
+  if (int r = check_strides("o", o_strides, oa)) return r;
+  if (o == o2 || lse == lse2) return fail(CA_EINVAL, "outputs may alias only o1 / lse1");
+  if (o == o1 && (in_dtype != out_dtype || o1_strides[0] != o_strides[0] ||
+                  o1_strides[1] != o_strides[1] || o1_strides[2] != o_strides[2]))
+    return fail(CA_EINVAL, "o aliases o1 with a different dtype or strides");
+  if (int r = check_device()) return r;
+  return launched(launch_lse_merge(o1, lse1, o2, lse2, in_dtype == CA_F32, o, lse,
+                                   out_dtype == CA_F32, B, H, N, d, o1_strides, o2_strides,
+                                   o_strides, static_cast<hipStream_t>(stream)),
+                  "lse_merge launch");
+}
+
+int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_strides,
+                  int block_size, int seg_len, float* out, void* stream) {
+  if (B < 0 || N < 0 || H < 0) return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 8 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 8, <= 512)", d);
+  if (block_size < 1 || seg_len < 1) return fail(CA_EINVAL, "block_size and seg_len must be >= 1");
+  if (!x || !out) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(x)) return fail(CA_EINVAL, "x must be 16-byte aligned");
+  if (int r = check_strides("x", x_strides, 8)) return r;
+  if ((int64_t)B * H > 65535) return fail(CA_ERANGE, "B*H above 65535");
+  const int nb = num_blocks(N, block_size, seg_len);
+  if (int r = check_device()) return r;
+  return launched(launch_block_mean(static_cast<const uint16_t*>(x), B, N, H, d, x_strides,
+                                    block_size, seg_len, (seg_len + block_size - 1) / block_size,
+                                    nb, out, static_cast<hipStream_t>(stream)),
+                  "block_mean launch");
+}
+
+int ca_block_score_topk(const float* q_mean, const float* k_mean, int B, int H, int NQB, int NKB,
+                        int d, int cand_begin, int cand_count, int K, int32_t* out_idx,
+                        float* out_score, void* stream) {
+  if (B < 0 || H < 0 || NQB < 0 || NKB < 0) return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 4 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 4, <= 512)", d);
+  if (!q_mean || !k_mean || !out_idx) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(q_mean) || !aligned16(k_mean)) return fail(CA_EINVAL, "means must be 16-byte aligned");
+  if (cand_count < 1 || cand_count > 4096) return fail(CA_ERANGE, "cand_count %d outside 1..4096", cand_count);
+  if (cand_begin < 0 || cand_begin + cand_count > NKB) return fail(CA_ERANGE, "candidate range outside [0, NKB)");
+  if (K < 1 || K > cand_count) return fail(CA_ERANGE, "K=%d outside 1..cand_count", K);
+  if ((int64_t)B * H > 65535 || NQB > 0x7FFFFFFF) return fail(CA_ERANGE, "grid too large");
+  if (int r = check_device()) return r;
+  return launched(launch_score_topk(q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
+                                    out_idx, out_score, static_cast<hipStream_t>(stream)),
+                  "block_score_topk launch");
+}
+
+int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
+                      const int32_t* persistent, int C, const int32_t* topk, int K,
+                      int topk_offset, int32_t* indptr, int32_t* indices, void* stream) {
+  if (B < 0 || H < 0 || NQB < 0 || sink_count < 0 || C < 0 || K < 0 || sink_begin < 0)
+    return fail(CA_EINVAL, "negative size");
+  if ((int64_t)B * H * NQB > 65536) return fail(CA_ERANGE, "more than 65536 rows");
+  if (!indptr || !indices) return fail(CA_EINVAL, "indptr and indices must be non-NULL");
+  if ((C > 0 && !persistent) || (K > 0 && !topk)) return fail(CA_EINVAL, "persistent/topk NULL with nonzero count");
+  if ((int64_t)B * H * NQB * ((int64_t)sink_count + C + K) > 0x7FFFFFFF) return fail(CA_ERANGE, "too many entries");
+  if (int r = check_device()) return r;
+  return launched(launch_build_kv_index(B * H * NQB, sink_begin, sink_count, C ? persistent : nullptr,
+                                        C, NQB, K ? topk : nullptr, K, topk_offset, indptr, indices,
+                                        static_cast<hipStream_t>(stream)),
+                  "build_kv_index launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal declarations shared by the chunkattn HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace chunkattn {
+
+// Vector types used with the gfx950 MFMA builtins and 16-byte memory ops.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) float f32x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+enum Mode { MODE_DENSE = 0, MODE_BLOCKS = 1, MODE_VARLEN = 2 };
+
+constexpr int kMaxHeadsPerLaunch = 1024;
+constexpr int kTileKeys = 64;     // keys per KV tile (and max KV block size)
+
+// Kernel arguments of the fused attention kernel (passed by value).
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  int64_t qs_b, qs_n, qs_h;
+  int64_t ks_b, ks_n, ks_h;   // varlen: ks_n = flat row stride, ks_b = ks_h = 0
+  int64_t os_b, os_n, os_h;
+  int B, H, Nq, Nkv;
+  float scale_log2;           // softmax scale * log2(e)
+  // block-list mode
+  const int32_t* indptr;
+  const int32_t* indices;
+  int nnz;                    // entries of indices; row spans are clamped to it
+  int kv_block, kv_seg, kv_bps, nkb;
+  int q_block, q_seg, q_bps, nqb, q_sub;
+  // ragged mode
+  const int32_t* cu;
+  int total_kv;
+  // work decomposition
+  int n_qtiles;               // query tiles per head (dense / ragged)
+  int n_items;                // logical work items of this launch
+  int n_heads;                // heads covered by this launch
+  int use_list;               // heads[] maps launch-local head -> b*H + h
+  int16_t heads[kMaxHeadsPerLaunch];
+};
+
+// Launchers implemented in attn_fwd.hip / select.hip / merge.hip.
+hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32,
+                            const AttnParams& p, hipStream_t stream);
+hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
+                             const int64_t* xs, int block, int seg, int bps, int nb,
+                             float* out, hipStream_t stream);
+hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int NQB,
+                             int NKB, int d, int cand_begin, int cand_count, int K,
+                             int32_t* out_idx, float* out_score, hipStream_t stream);
+hipError_t launch_build_kv_index(int rows, int sink_begin, int sink_count,
+                                 const int32_t* persistent, int C, int NQB,
+                                 const int32_t* topk, int K, int topk_offset,
+                                 int32_t* indptr, int32_t* indices, hipStream_t stream);
+hipError_t launch_lse_merge(const void* o1, const float* l1, const void* o2,
+                            const float* l2, int in_f32, void* o, float* l, int out_f32,
+                            int B, int H, int N, int d, const int64_t* s1,
+                            const int64_t* s2, const int64_t* so, hipStream_t stream);
+
+// Map a hardware block index to a logical work item so that consecutive
+// logical items run on the same XCD (workgroups are dispatched to the 8 XCDs
+// round-robin; each XCD has its own L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int per = nblocks / kXcd;
+  const int rem = nblocks % kXcd;
+  const int x = bid % kXcd;
+  const int j = bid / kXcd;
+  return x * per + (x < rem ? x : rem) + j;
+}
+
+// Start and length of block `id` of the frame-aligned tiling of n tokens
+// (segments of `seg` tokens, `bps` blocks of `block` tokens per segment).
+__host__ __device__ __forceinline__ void block_span(int id, int n, int block, int seg,
+                                                    int bps, int& start, int& len) {
+  const int s = id / bps;
+  const int j = id - s * bps;
+  const int seg_start = s * seg;
+  int seg_len = n - seg_start;
+  seg_len = seg_len < seg ? seg_len : seg;
+  start = seg_start + j * block;
+  const int rest = seg_len - j * block;
+  len = rest < block ? rest : block;
+  if (len < 0) len = 0;
+}
+
+}  // namespace chunkattn

@@ -48,12 +48,16 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 @dataclasses.dataclass
 class Bf16Tensor:
-    """A bf16 tensor kept both as raw bits and as its exact float32 value."""
+    """A bf16 tensor kept both as raw bits and as its exact float32 value
+    (computed once, on first use)."""
     bits: np.ndarray
+    _f32: Optional[np.ndarray] = dataclasses.field(default=None, repr=False, compare=False)
 
     @property
     def f32(self) -> np.ndarray:
-        return bf16_to_f32(self.bits)
+        if self._f32 is None:
+            self._f32 = bf16_to_f32(self.bits)
+        return self._f32
 
     @property
     def shape(self):

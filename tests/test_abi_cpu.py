@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host before touching a device (CPU only)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_attention_chunk_amd import _lib
+from kv_cache_attention_chunk_amd._lib import (CA_EINVAL, CA_ENODEV, CA_ERANGE, CA_EUNSUPPORTED,
+                                               strides3)
+
+FAKE = 0x10000          # 16-byte aligned dummy address; never dereferenced
+S = strides3((4680 * 12 * 128, 12 * 128, 128))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _lib.header_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(L):
+    assert L.ca_abi_version() == 1
+    for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"range"),
+                       (4, b"device"), (5, b"HIP")]:
+        assert word in L.ca_status_str(code)
+
+
+def test_num_blocks(L):
+    assert L.ca_num_blocks(32760, 64, 1560) == 525
+    assert L.ca_num_blocks(4680, 64, 1560) == 75
+    assert L.ca_num_blocks(1024, 64, 1024) == 16
+    assert L.ca_num_blocks(100, 64, 60) == 2
+    assert L.ca_num_blocks(0, 64, 1560) == 0
+    assert L.ca_num_blocks(10, 0, 5) == -1
+
+
+def fwd(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=12, Nq=4680, Nkv=32760, d=128, qs=S, kvs=S, os=S,
+             indptr=None, indices=None, nnz=0, kb=64, ks=1560, qb=64, qseg=1560, scale=0.088,
+             o=FAKE, odt=0, lse=FAKE, stream=None)
+    a.update(kw)
+    return L.ca_chunk_attn_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["Nq"], a["Nkv"], a["d"],
+                               a["qs"], a["kvs"], a["os"], a["indptr"], a["indices"], a["nnz"],
+                               a["kb"], a["ks"], a["qb"], a["qseg"], a["scale"], a["o"], a["odt"],
+                               a["lse"], a["stream"])
+
+
+def test_attention_argument_errors(L):
+    assert fwd(L, q=None) == CA_EINVAL
+    assert fwd(L, q=FAKE + 8) == CA_EINVAL
+    assert fwd(L, d=96) == CA_EUNSUPPORTED
+    assert fwd(L, odt=7) == CA_EUNSUPPORTED
+    assert fwd(L, B=-1) == CA_EINVAL
+    assert fwd(L, qs=strides3((1, 3, 128))) == CA_EINVAL
+    assert fwd(L, indptr=FAKE) == CA_EINVAL                 # indices missing
+    assert fwd(L, indptr=FAKE, indices=FAKE, kb=65) == CA_ERANGE
+    assert fwd(L, indptr=FAKE, indices=FAKE, nnz=-1) == CA_EINVAL
+    assert fwd(L, scale=float("nan")) == CA_EINVAL
+    fwd(L, d=96)
+    assert b"head dim 96" in L.ca_last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="a GPU is visible")
+def test_no_device_reports_enodev(L):
+    assert fwd(L) == CA_ENODEV
+    assert fwd(L, indptr=FAKE, indices=FAKE, nnz=10) == CA_ENODEV
+    assert b"no HIP device" in L.ca_last_error()
+
+
+def test_varlen_host_checks(L):
+    cu = np.array([0, 10, 5], dtype=np.int32)
+    st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu.ctypes.data, 100, 1, 2, 16, 64,
+                                    strides3((16 * 2 * 64, 128, 64)), 64,
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None)
+    assert st == CA_EINVAL
+    cu = np.array([0, 10, 500], dtype=np.int32)
+    st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu.ctypes.data, 100, 1, 2, 16, 64,
+                                    strides3((16 * 2 * 64, 128, 64)), 64,
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None)
+    assert st == CA_ERANGE
+    st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, None, 100, 1, 2, 16, 64,
+                                    strides3((16 * 2 * 64, 128, 64)), 60,
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None)
+    assert st == CA_EINVAL
+
+
+def test_mixed_mode_checks(L):
+    bad = np.array([0, 3], dtype=np.int32)
+    st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, bad.ctypes.data,
+                                   None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
+                                   0.1, FAKE, 0, FAKE, None)
+    assert st == CA_EINVAL
+    blocks = np.array([1, 1], dtype=np.int32)
+    st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, blocks.ctypes.data,
+                                   None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
+                                   0.1, FAKE, 0, FAKE, None)
+    assert st == CA_EINVAL        # block heads without a CSR
+
+
+def test_merge_mean_topk_index_checks(L):
+    s = strides3((1024, 128, 64))
+    m = lambda **kw: L.ca_lse_merge(kw.get("o1", FAKE), FAKE, FAKE + 4096, FAKE, kw.get("idt", 1),
+                                    kw.get("o", FAKE + 8192), FAKE + 256, kw.get("odt", 0),
+                                    1, 2, 8, kw.get("d", 64), s, s, kw.get("os", s), None)
+    assert m(d=48) == CA_EUNSUPPORTED
+    assert m(idt=3) == CA_EUNSUPPORTED
+    assert m(o1=None) == CA_EINVAL
+    assert m(o=FAKE + 4096) == CA_EINVAL                      # aliases o2
+    assert m(o=FAKE, odt=0) == CA_EINVAL                      # aliases o1 with another dtype
+    assert L.ca_block_mean(FAKE, 1, 100, 2, 12, s, 64, 100, FAKE, None) == CA_EUNSUPPORTED
+    assert L.ca_block_mean(FAKE, 1, 100, 2, 64, s, 0, 100, FAKE, None) == CA_EINVAL
+    t = lambda **kw: L.ca_block_score_topk(FAKE, FAKE, 1, 2, 75, 525, 128, kw.get("cb", 450),
+                                           kw.get("cc", 75), kw.get("K", 10), FAKE, None, None)
+    assert t(K=0) == CA_ERANGE
+    assert t(K=76) == CA_ERANGE
+    assert t(cb=451) == CA_ERANGE
+    assert t(cc=5000) == CA_ERANGE
+    assert L.ca_build_kv_index(1, 2, 75, 0, 25, None, 32, FAKE, 10, 0, FAKE, FAKE, None) == CA_EINVAL
+    assert L.ca_build_kv_index(1, 1000, 75, 0, 25, FAKE, 32, FAKE, 10, 0, FAKE, FAKE, None) == CA_ERANGE
+
+
+def test_binding_rejects_cpu_tensors():
+    import kv_cache_attention_chunk_amd as ca
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ca.chunk_attn_fwd(q, q, q)

@@ -1,0 +1,449 @@
+"""GPU parity: every HIP kernel against the CPU oracle on the same seeded
+inputs (O max-abs 1e-2, LSE max-abs 1e-3, block ids exact except near-ties).
+
+Small cases span several 64-key tiles, ragged query/key tails, 24-token tail
+blocks, empty key sets, d = 64 and 128 and strided head-subset views; the
+workload-sized cases run the library exactly as the benchmark does and are
+checked on sampled query rows that the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_attention_chunk_amd as ca
+from kv_cache_attention_chunk_amd import workloads as wl
+import oracle as orc
+from helpers import assert_lse, assert_o, compare_topk, i32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _loaded():
+    from kv_cache_attention_chunk_amd import _lib
+    _lib.lib()          # raises if the HIP library is missing
+
+
+def _gen(seed, B, N, H, d, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return wl.Bf16Tensor.from_f32(rng.standard_normal((B, N, H, d), dtype=np.float32) * scale)
+
+
+# ---------------------------------------------------------------------------
+# workload of the tiny dense chunk (256 q vs 1024 kv, 2 heads, d 64)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tiny_dense(out_dtype):
+    say(f"tiny dense {out_dtype}")
+    w = wl.tiny_dense(seed=0)
+    o, l = ca.chunk_attn_fwd(to_dev(w.q), to_dev(w.k), to_dev(w.v), scale=w.scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale)
+    assert_o(o, Or, out_dtype == torch.bfloat16, "tiny dense")
+    assert_lse(l, Lr, "tiny dense")
+
+
+@pytest.mark.parametrize("q_block", [64, 256])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_local_history_merge(q_block, seed):
+    say(f"tiny local/history merge q_block={q_block} seed={seed}")
+    w = wl.tiny_dense(seed=seed)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    nqb = w.Nq // q_block
+    rows = w.B * w.H * nqb
+    branches = []
+    for blocks in (w.meta["local_blocks"], w.meta["history_blocks"]):
+        indptr = np.arange(rows + 1, dtype=np.int32) * len(blocks)
+        indices = np.tile(np.array(blocks, np.int32), rows)
+        o, l = ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(indptr), kv_indices=i32(indices),
+                                 kv_block=64, kv_seg=w.Nkv, q_block=q_block, q_seg=w.Nq,
+                                 scale=w.scale, out_dtype=torch.float32)
+        Or, Lr = orc.chunk_attn_blocks(w.q.f32, w.k.f32, w.v.f32, indptr, indices, 64, w.Nkv,
+                                       q_block, w.Nq, w.scale)
+        torch.cuda.synchronize()
+        assert_o(o, Or, False, "branch")
+        assert_lse(l, Lr, "branch")
+        branches.append((o, l))
+    om, lm = ca.lse_merge(branches[0][0], branches[0][1], branches[1][0], branches[1][1],
+                          out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Od, Ld = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale)
+    assert_o(om, Od, True, "merged vs dense")
+    assert_lse(lm, Ld, "merged vs dense")
+
+
+# ---------------------------------------------------------------------------
+# dense mode: ragged sizes, d 64 / 128, batch > 1, strided views, empty caches
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,Nq,Nkv,d,sc", [
+    (2, 3, 200, 1000, 128, 1.0), (1, 2, 129, 63, 64, 1.5), (1, 1, 33, 1, 128, 2.0),
+    (1, 2, 64, 0, 64, 1.0), (2, 2, 300, 777, 64, 0.7), (1, 3, 1, 130, 128, 1.0),
+])
+def test_dense_shapes(B, H, Nq, Nkv, d, sc):
+    say(f"dense B={B} H={H} Nq={Nq} Nkv={Nkv} d={d}")
+    Q, K, V = _gen(1, B, Nq, H, d, sc), _gen(2, B, Nkv, H, d, sc), _gen(3, B, Nkv, H, d)
+    o, l = ca.chunk_attn_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_dense(Q.f32, K.f32, V.f32, 1 / math.sqrt(d))
+    assert_o(o, Or, True, "dense")
+    assert_lse(l, Lr, "dense")
+
+
+def test_dense_strided_head_subset_views():
+    say("dense strided views")
+    B, Nq, Nkv, H, d = 1, 150, 300, 6, 128
+    Q, K, V = _gen(4, B, Nq, H, d), _gen(5, B, Nkv, H, d), _gen(6, B, Nkv, H, d)
+    q, k, v = to_dev(Q)[:, :, 1::2], to_dev(K)[:, :, 1::2], to_dev(V)[:, :, 1::2]
+    out = torch.full((B, Nq, 5, d), 7.0, dtype=torch.float32, device="cuda")
+    o, l = ca.chunk_attn_fwd(q, k, v, out=out[:, :, 1:4], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_dense(Q.f32[:, :, 1::2], K.f32[:, :, 1::2], V.f32[:, :, 1::2], 1 / math.sqrt(d))
+    assert_o(o, Or, False, "strided")
+    assert_lse(l, Lr, "strided")
+    assert torch.all(out[:, :, 0] == 7.0) and torch.all(out[:, :, 4] == 7.0)
+
+
+def test_dense_output_guard_bands_and_determinism():
+    say("dense guard bands + determinism")
+    B, Nq, Nkv, H, d = 1, 130, 200, 2, 64
+    Q, K, V = _gen(7, B, Nq, H, d), _gen(8, B, Nkv, H, d), _gen(9, B, Nkv, H, d)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    buf = torch.full((B * Nq * H * d + 2048,), -3.0, dtype=torch.bfloat16, device="cuda")
+    o = buf[1024:1024 + B * Nq * H * d].view(B, Nq, H, d)
+    lbuf = torch.full((B * H * Nq + 128,), 5.0, dtype=torch.float32, device="cuda")
+    lse = lbuf[64:64 + B * H * Nq].view(B, H, Nq)
+    ca.chunk_attn_fwd(q, k, v, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:1024] == -3.0) and torch.all(buf[-1024:] == -3.0)
+    assert torch.all(lbuf[:64] == 5.0) and torch.all(lbuf[-64:] == 5.0)
+    o2, l2 = ca.chunk_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+
+
+# ---------------------------------------------------------------------------
+# block-list mode (PBSA): frame-aligned tiling with tail blocks, empty rows
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,seed", [(128, 0), (64, 1), (128, 2)])
+def test_blocks_random_lists(d, seed):
+    say(f"blocks random lists d={d} seed={seed}")
+    B, H, Nq, Nkv, seg, blk = 2, 2, 200, 500, 100, 64      # tiles of 64 + 36 per segment
+    Q, K, V = _gen(10 + seed, B, Nq, H, d), _gen(20 + seed, B, Nkv, H, d), _gen(30 + seed, B, Nkv, H, d)
+    nkb = orc.block_spans(Nkv, blk, seg).shape[0]
+    nqb = orc.block_spans(Nq, blk, seg).shape[0]
+    rng = np.random.default_rng(seed)
+    indptr, indices = wl.random_csr(rng, B * H * nqb, nkb, nkb)
+    o, l = ca.chunk_attn_fwd(to_dev(Q), to_dev(K), to_dev(V), kv_indptr=i32(indptr),
+                             kv_indices=i32(indices if len(indices) else np.zeros(1)),
+                             kv_block=blk, kv_seg=seg, q_block=blk, q_seg=seg)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_blocks(Q.f32, K.f32, V.f32, indptr, indices, blk, seg, blk, seg,
+                                   1 / math.sqrt(d))
+    assert_o(o, Or, True, "blocks")
+    assert_lse(l, Lr, "blocks")
+
+
+def test_blocks_unsorted_lists_and_small_blocks():
+    say("blocks unsorted lists, 24-token blocks")
+    B, H, Nq, Nkv, d = 1, 3, 96, 480, 128
+    Q, K, V = _gen(41, B, Nq, H, d), _gen(42, B, Nkv, H, d), _gen(43, B, Nkv, H, d)
+    blk, seg = 24, 480
+    nkb = Nkv // blk
+    rng = np.random.default_rng(3)
+    lists = [rng.permutation(nkb)[:rng.integers(0, nkb)] for _ in range(B * H * 4)]
+    indptr = np.zeros(len(lists) + 1, np.int32)
+    indptr[1:] = np.cumsum([len(x) for x in lists])
+    indices = np.concatenate(lists).astype(np.int32)
+    o, l = ca.chunk_attn_fwd(to_dev(Q), to_dev(K), to_dev(V), kv_indptr=i32(indptr),
+                             kv_indices=i32(indices), kv_block=blk, kv_seg=seg, q_block=24, q_seg=Nq)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_blocks(Q.f32, K.f32, V.f32, indptr, indices, blk, seg, 24, Nq, 1 / math.sqrt(d))
+    assert_o(o, Or, True, "blocks unsorted")
+    assert_lse(l, Lr, "blocks unsorted")
+
+
+# ---------------------------------------------------------------------------
+# ragged mode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("host_cu", [False, True])
+def test_varlen_small(host_cu):
+    say(f"varlen small host_cu={host_cu}")
+    w = wl.ragged(seed=5, H=5, d=128, frames_q=2, frames_kv=21, frame_tokens=40)
+    cu = w.cu_seqlens.copy()
+    # make head 1 empty and head 3 end on a ragged length
+    lens = np.diff(cu)
+    lens[1] = 0
+    lens[3] = 77
+    cu2 = np.zeros_like(cu)
+    cu2[1:] = np.cumsum(lens)
+    Kf = wl.Bf16Tensor(w.k_flat.bits[:cu2[-1]].copy())
+    Vf = wl.Bf16Tensor(w.v_flat.bits[:cu2[-1]].copy())
+    o, l = ca.chunk_attn_varlen_fwd(to_dev(w.q), to_dev(Kf), to_dev(Vf), i32(cu2),
+                                    cu_seqlens_host=cu2 if host_cu else None)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_varlen(w.q.f32, Kf.f32, Vf.f32, cu2, w.scale)
+    assert_o(o, Or, True, "varlen")
+    assert_lse(l, Lr, "varlen")
+
+
+def test_mixed_small():
+    say("mixed small")
+    w = wl.mixed(seed=3, H=6, d=64, frames_q=2, frames_kv=8, frame_tokens=100, topk_ratio=0.5)
+    lay = dict(w.meta["sparse"])
+    lay["C"] = 3
+    sel = orc.sparse_selection(w.q.f32, w.k.f32, w.q_block, w.q_seg, w.kv_block, w.kv_seg, lay)
+    o, l = ca.chunk_attn_mixed_fwd(
+        to_dev(w.q), w.head_mode, k=to_dev(w.k), v=to_dev(w.v), kv_indptr=i32(sel["indptr"]),
+        kv_indices=i32(sel["indices"]), kv_block=64, kv_seg=100, q_block=64, q_seg=100,
+        k_flat=to_dev(w.k_flat), v_flat=to_dev(w.v_flat), cu_seqlens=i32(w.cu_seqlens),
+        cu_seqlens_host=w.cu_seqlens)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    lg = l.cpu().numpy()
+    for h in range(w.H):
+        if w.head_mode[h] == 0:
+            Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale, heads=[h])
+        elif w.head_mode[h] == 1:
+            Or, Lr = orc.chunk_attn_blocks(w.q.f32, w.k.f32, w.v.f32, sel["indptr"], sel["indices"],
+                                           64, 100, 64, 100, w.scale, heads=[h])
+        else:
+            Or, Lr = orc.chunk_attn_varlen(w.q.f32, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens,
+                                           w.scale, heads=[h])
+        assert_o(torch.from_numpy(og[:, :, h:h + 1]), Or, True, f"mixed head {h}")
+        assert_lse(torch.from_numpy(lg[:, h:h + 1]), Lr, f"mixed head {h}")
+
+
+# ---------------------------------------------------------------------------
+# LSE merge kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("idt,odt", [(torch.float32, torch.bfloat16), (torch.bfloat16, torch.bfloat16),
+                                     (torch.float32, torch.float32), (torch.bfloat16, torch.float32)])
+def test_lse_merge_kernel(idt, odt):
+    say(f"lse_merge {idt}->{odt}")
+    rng = np.random.default_rng(9)
+    B, N, H, d = 2, 37, 3, 128
+    o1 = torch.from_numpy(rng.standard_normal((B, N, H, d), dtype=np.float32)).to(idt).cuda()
+    o2 = torch.from_numpy(rng.standard_normal((B, N, H, d), dtype=np.float32)).to(idt).cuda()
+    l1 = rng.standard_normal((B, H, N)).astype(np.float32) * 5
+    l2 = rng.standard_normal((B, H, N)).astype(np.float32) * 5
+    l1[0, 0, :4] = -np.inf
+    l2[0, 0, 2:6] = -np.inf
+    l2[1, 2, 7] = l1[1, 2, 7]
+    o, l = ca.lse_merge(o1, torch.from_numpy(l1).cuda(), o2, torch.from_numpy(l2).cuda(), out_dtype=odt)
+    torch.cuda.synchronize()
+    Or, Lr = orc.lse_merge_bshd(o1.float().cpu().numpy(), l1, o2.float().cpu().numpy(), l2)
+    assert_o(o, Or, odt == torch.bfloat16, "merge")
+    assert_lse(l, Lr, "merge")
+    # in place into o1 / lse1
+    if idt == odt:
+        lt = torch.from_numpy(l1).cuda()
+        ca.lse_merge(o1, lt, o2, torch.from_numpy(l2).cuda(), out=o1, out_lse=lt)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.float(), o.float()) and torch.equal(lt, l)
+
+
+# ---------------------------------------------------------------------------
+# block means, scores + top-K, block lists
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,N,seg", [(128, 1560 * 2, 1560), (64, 300, 100), (128, 100, 100)])
+def test_block_mean_kernel(d, N, seg):
+    say(f"block_mean d={d} N={N} seg={seg}")
+    X = _gen(50, 2, N, 3, d, 2.0)
+    m = ca.block_mean(to_dev(X), 64, seg)
+    torch.cuda.synchronize()
+    ref = orc.block_mean(X.f32, 64, seg)
+    np.testing.assert_allclose(m.cpu().numpy(), ref, rtol=0, atol=2e-6)
+
+
+def test_topk_planted_ties_and_full():
+    say("topk planted")
+    d = 128
+    q = np.zeros((1, 2, 3, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 2, 90, d), np.float32)
+    rng = np.random.default_rng(0)
+    k[..., 0] = rng.integers(0, 20, size=(1, 2, 90)).astype(np.float32)   # many exact ties
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda()
+    for K, cb, cc in [(5, 10, 75), (1, 0, 90), (75, 15, 75), (32, 3, 80)]:
+        idx, sc = ca.block_score_topk(qt, kt, K, cand_begin=cb, cand_count=cc, return_scores=True)
+        torch.cuda.synchronize()
+        ref = orc.block_score_topk(q, k, cb, cc, K)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])     # exact ties: lower id wins
+        np.testing.assert_array_equal(sc.cpu().numpy(), ref["score"])
+
+
+def test_topk_random_and_index_build():
+    say("topk random + build_kv_index")
+    rng = np.random.default_rng(1)
+    qm = rng.standard_normal((1, 4, 75, 128)).astype(np.float32) / 8
+    km = rng.standard_normal((1, 4, 525, 128)).astype(np.float32) / 8
+    cm = qm.mean(axis=2, keepdims=True).astype(np.float32)
+    qt, kt, ct = (torch.from_numpy(x).cuda() for x in (qm, km, cm))
+    pers = ca.block_score_topk(ct, kt, 32, cand_begin=25, cand_count=425)
+    loc = ca.block_score_topk(qt, kt, 10, cand_begin=450, cand_count=75)
+    torch.cuda.synchronize()
+    rp = orc.block_score_topk(cm, km, 25, 425, 32)
+    rl = orc.block_score_topk(qm, km, 450, 75, 10)
+    ties = compare_topk(pers, rp) + compare_topk(loc, rl)
+    say(f"top-K rows differing at near-ties: {ties}")
+    indptr, indices = ca.build_kv_index(1, 4, 75, 0, 25, pers[:, :, 0, :].contiguous(), loc, 0)
+    torch.cuda.synchronize()
+    ip_ref, ix_ref = orc.build_kv_index(1, 4, 75, 0, 25, pers.cpu().numpy()[:, :, 0, :], loc.cpu().numpy(), 0)
+    np.testing.assert_array_equal(indptr.cpu().numpy(), ip_ref)
+    np.testing.assert_array_equal(indices.cpu().numpy()[:len(ix_ref)], ix_ref)
+
+
+def test_build_kv_index_dedup_and_offset():
+    say("build_kv_index dedup/offset")
+    pers = np.array([[[1, 2, 30], [0, 5, 6]]], np.int32)                    # [1, 2, 3]
+    topk = np.array([[[[0, 29]], [[3, 4]]]], np.int32).repeat(2, axis=2)   # [1, 2, 2, 2]
+    topk = np.ascontiguousarray(topk.reshape(1, 2, 2, 2))
+    ip, ix = ca.build_kv_index(1, 2, 2, 0, 3, i32(pers), i32(topk), 1)
+    torch.cuda.synchronize()
+    ipr, ixr = orc.build_kv_index(1, 2, 2, 0, 3, pers, topk, 1)
+    np.testing.assert_array_equal(ip.cpu().numpy(), ipr)
+    np.testing.assert_array_equal(ix.cpu().numpy()[:len(ixr)], ixr)
+
+
+# ---------------------------------------------------------------------------
+# workload-sized cases, exactly as the benchmark runs them, on sampled rows
+# ---------------------------------------------------------------------------
+WAN_ROWS = np.r_[0:32, 120:136, 2000:2008, 4600:4616, 4664:4680]
+
+
+@pytest.fixture(scope="module")
+def wan():
+    return wl.wan_dense(seed=0)
+
+
+@pytest.fixture(scope="module")
+def wan_dev(wan):
+    return to_dev(wan.q), to_dev(wan.k), to_dev(wan.v)
+
+
+def test_wan_dense_full_size(wan, wan_dev):
+    say("wan dense 12x4680x32760 d128")
+    q, k, v = wan_dev
+    o, l = ca.chunk_attn_fwd(q, k, v, scale=wan.scale)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale, rows=WAN_ROWS)
+    assert_o(o[:, WAN_ROWS], Or, True, "wan dense")
+    assert_lse(l[:, :, WAN_ROWS], Lr, "wan dense")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+
+
+def test_wan_local_history_merge_full_size(wan, wan_dev):
+    say("wan local/history merge")
+    q, k, v = wan_dev
+    outs = []
+    for key in ("local_blocks", "history_blocks"):
+        blocks = np.array(wan.meta[key], np.int32)
+        ip = np.arange(wan.H + 1, dtype=np.int32) * len(blocks)
+        ix = np.tile(blocks, wan.H)
+        outs.append(ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(ip), kv_indices=i32(ix), kv_block=64,
+                                      kv_seg=1560, q_block=wan.Nq, q_seg=wan.Nq, scale=wan.scale,
+                                      out_dtype=torch.float32))
+    om, lm = ca.lse_merge(outs[0][0], outs[0][1], outs[1][0], outs[1][1], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Or, Lr = orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale, rows=WAN_ROWS)
+    assert_o(om[:, WAN_ROWS], Or, True, "wan merge")
+    assert_lse(lm[:, :, WAN_ROWS], Lr, "wan merge")
+
+
+@pytest.mark.parametrize("ratio", [0.25, 0.125, 0.0625])
+def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
+    say(f"wan block-sparse ratio={ratio}")
+    q, k, v = wan_dev
+    lay = wl.sparse_layout(wan, ratio)
+    o, l, info = ca.block_sparse_fwd(q, k, v, sink_begin=0, sink_count=lay["sink_count"],
+                                     hist_begin=lay["hist_begin"], hist_count=lay["hist_count"],
+                                     C=lay["C"], local_begin=lay["local_begin"],
+                                     local_count=lay["local_count"], K=lay["K"], block=64,
+                                     seg=1560, scale=wan.scale)
+    torch.cuda.synchronize()
+    sel = orc.sparse_selection(wan.q.f32, wan.k.f32, 64, 1560, 64, 1560, lay)
+    np.testing.assert_allclose(info["q_mean"].cpu().numpy(), sel["q_mean"], rtol=0, atol=5e-6)
+    np.testing.assert_allclose(info["k_mean"].cpu().numpy(), sel["k_mean"], rtol=0, atol=5e-6)
+    ties = compare_topk(info["persistent"], sel["persistent"]) + compare_topk(info["local"], sel["local"])
+    say(f"top-K rows differing at near-ties: {ties}")
+    ip = info["indptr"].cpu().numpy()
+    ix = info["indices"].cpu().numpy()[:ip[-1]]
+    if ties == 0:
+        np.testing.assert_array_equal(ip, sel["indptr"])
+        np.testing.assert_array_equal(ix, sel["indices"])
+    # attention over the selected lists (as built on the GPU, checked above)
+    rows = np.r_[0:64, 1536:1560, 4616:4680]
+    Or, Lr = orc.chunk_attn_blocks(wan.q.f32, wan.k.f32, wan.v.f32, ip, ix, 64, 1560, 64, 1560,
+                                   wan.scale, rows=rows)
+    assert_o(o[:, rows], Or, True, "wan sparse")
+    assert_lse(l[:, :, rows], Lr, "wan sparse")
+
+
+def test_ragged_full_size():
+    say("ragged 12 heads, cu_seqlens")
+    w = wl.ragged(seed=0)
+    o, l = ca.chunk_attn_varlen_fwd(to_dev(w.q), to_dev(w.k_flat), to_dev(w.v_flat), i32(w.cu_seqlens),
+                                    cu_seqlens_host=w.cu_seqlens, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = np.r_[0:40, 4640:4680]
+    Or, Lr = orc.chunk_attn_varlen(w.q.f32, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens, w.scale, rows=rows)
+    assert_o(o[:, rows], Or, True, "ragged")
+    assert_lse(l[:, :, rows], Lr, "ragged")
+
+
+def test_mixed_40_heads_full_size():
+    say("mixed 40 heads")
+    w = wl.mixed(seed=0)
+    lay = w.meta["sparse"]
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    sparse_heads = [h for h in range(w.H) if w.head_mode[h] == 1]
+    # selection for the block-sparse heads runs on the GPU over those heads' views
+    hsel = torch.tensor(sparse_heads, device="cuda")
+    qs, ks = q.index_select(2, hsel).contiguous(), k.index_select(2, hsel).contiguous()
+    qm, km, cm = ca.block_mean(qs, 64, 1560), ca.block_mean(ks, 64, 1560), ca.block_mean(qs, w.Nq, w.Nq)
+    pers = ca.block_score_topk(cm, km, lay["C"], cand_begin=lay["hist_begin"], cand_count=lay["hist_count"])
+    loc = ca.block_score_topk(qm, km, lay["K"], cand_begin=lay["local_begin"], cand_count=lay["local_count"])
+    ip_s, ix_s = ca.build_kv_index(1, len(sparse_heads), 75, 0, lay["sink_count"],
+                                   pers[:, :, 0, :].contiguous(), loc, 0)
+    torch.cuda.synchronize()
+    # scatter the per-sparse-head rows into a CSR over all 40 heads (other heads empty)
+    ip_s, ix_s = ip_s.cpu().numpy(), ix_s.cpu().numpy()
+    lists = []
+    for h in range(w.H):
+        for qb in range(75):
+            if w.head_mode[h] == 1:
+                r = sparse_heads.index(h) * 75 + qb
+                lists.append(ix_s[ip_s[r]:ip_s[r + 1]])
+            else:
+                lists.append(np.zeros(0, np.int32))
+    ip = np.zeros(len(lists) + 1, np.int32)
+    ip[1:] = np.cumsum([len(x) for x in lists])
+    ix = np.concatenate(lists).astype(np.int32)
+    o, l = ca.chunk_attn_mixed_fwd(q, w.head_mode, k=k, v=v, kv_indptr=i32(ip), kv_indices=i32(ix),
+                                   kv_block=64, kv_seg=1560, q_block=64, q_seg=1560,
+                                   k_flat=to_dev(w.k_flat), v_flat=to_dev(w.v_flat),
+                                   cu_seqlens=i32(w.cu_seqlens), cu_seqlens_host=w.cu_seqlens,
+                                   scale=w.scale)
+    torch.cuda.synchronize()
+    rows = np.r_[0:16, 1540:1560, 4664:4680]
+    og, lg = o[:, rows].float().cpu().numpy(), l[:, :, rows].cpu().numpy()
+    for mode in range(3):
+        hs = [h for h in range(w.H) if w.head_mode[h] == mode]
+        if mode == 0:
+            Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale, rows=rows, heads=hs)
+        elif mode == 1:
+            Or, Lr = orc.chunk_attn_blocks(w.q.f32, w.k.f32, w.v.f32, ip, ix, 64, 1560, 64, 1560,
+                                           w.scale, rows=rows, heads=hs)
+        else:
+            Or, Lr = orc.chunk_attn_varlen(w.q.f32, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens,
+                                           w.scale, rows=rows, heads=hs)
+        assert_o(torch.from_numpy(og[:, :, hs]), Or, True, f"mixed mode {mode}")
+        assert_lse(torch.from_numpy(lg[:, hs]), Lr, f"mixed mode {mode}")
