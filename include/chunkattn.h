@@ -88,7 +88,7 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  *                Ids must be distinct within a row; order is free.
  *   kv_nnz       number of entries of kv_indices; row spans are clamped to it.
  *   kv_block     1..64; kv_seg >= 1; q_block >= 1; q_seg >= 1 (block mode)
- *   scale        softmax scale (1/sqrt(d) for the pages' models)
+ *   scale        softmax scale, finite and > 0 (1/sqrt(d) for the pages' models)
  *   o            [B, Nq, H, d] of o_dtype (CA_BF16 or CA_F32), strides o_strides
  *   lse          float32 [B, H, Nq]; an empty key set gives O = 0, LSE = -inf
  */

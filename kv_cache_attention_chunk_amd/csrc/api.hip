@@ -88,7 +88,7 @@ int check_common(const Common& c) {
   if (!aligned16(c.q) || !aligned16(c.o) || !aligned16(c.lse)) return fail(CA_EINVAL, "q, o, lse must be 16-byte aligned");
   if (int r = check_strides("q", c.qs, 8)) return r;
   if (int r = check_strides("o", c.os, c.o_dtype == CA_BF16 ? 8 : 4)) return r;
-  if (!(std::isfinite(c.scale))) return fail(CA_EINVAL, "scale not finite");
+  if (!(std::isfinite(c.scale) && c.scale > 0.f)) return fail(CA_EINVAL, "scale must be finite and > 0");
   return CA_OK;
 }
 

@@ -27,7 +27,6 @@ namespace chunkattn {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
@@ -59,6 +58,22 @@ struct TileStage {
 
   __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb,
                                        int64_t stride, int len, int tid) {
+    if (len == kTileKeys) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int c = tid + i * NT;
+        kr[i] = ld16(kb + (c / L::CPR) * stride + (c % L::CPR) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int b = tid + i * NT;
+        if (NV * NT > NVB && b >= NVB) continue;
+        const uint16_t* src = vb + 4 * (b / L::CPR) * stride + (b % L::CPR) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[i][e] = ld16(src + e * stride);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int c = tid + i * NT;
@@ -111,8 +126,11 @@ struct TileStage {
   }
 };
 
+// Two waves per SIMD: caps VGPR + AGPR at 256 per lane so that two 4-wave
+// workgroups share a CU and one wave's softmax overlaps the other's MFMAs.
 template <int D, int NW, int MODE, bool OF32>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_kernel(const AttnParams p) {
   using L = Layout<D>;
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
@@ -256,29 +274,38 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnParams p) {
       }
     }
 
-    // online softmax (log2 domain); key of s[kt][i] = 32kt + 8(i/4) + 4hg + i%4
+    // online softmax in the log2 domain; key of s[kt][i] = 32kt + 8(i/4) + 4hg + i%4.
+    // Row max of the raw scores (scale > 0 keeps the order), one exchange
+    // with lane^32 (the other half of the same query column).
+    if (len_cur < kTileKeys) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
+          if (key >= len_cur) s[kt][i] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kt][i] * p.scale_log2;
-        if (len_cur < kTileKeys) {
-          const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
-          if (key >= len_cur) x = -INFINITY;
-        }
-        s[kt][i] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+    // The exponent base m is the exact running row max, so the largest weight
+    // of a row is exactly 1 and survives the bf16 rounding of P unchanged.
+    // The O accumulator is rescaled only when some row of the wave found a
+    // new max in this tile (a minority of tiles once a few have been seen).
+    const bool grow = mx > m;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
+    const float m_use = m == -INFINITY ? 0.f : m;
 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -287,7 +314,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnParams p) {
         f32x8_t pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(s[kt][8 * u + e] - m_use);
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + e], p.scale_log2, -m_use));
           l += pe;
           pf[e] = pe;
         }
