@@ -89,8 +89,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--topk-ratio", type=float, default=0.125)
-    ap.add_argument("--only", choices=["step", "dense"], default="step",
-                    help="'dense' times the dense kernel alone (for counter runs)")
+    ap.add_argument("--only", choices=["step", "dense", "copy"], default="step",
+                    help="'dense' times the dense kernel alone (for counter runs); 'copy' "
+                         "runs a plain 1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -109,6 +110,23 @@ def main():
     _lib.lib()
 
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        n_bytes = 1 << 30
+        x = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes,
+                          "ms": ms, "GBps_read+write": 2 * n_bytes / (ms * 1e-3) / 1e9}))
+        return
     t0 = time.perf_counter()
     w = wl.wan_dense(seed=0)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")

@@ -4,17 +4,20 @@
 // key set in 64-token tiles:
 //   * K and V tiles go global -> registers -> LDS, double buffered; the next
 //     tile's global loads are in flight while the current tile is computed.
-//     K is stored row-major (+16 B row pad); V is stored transposed,
-//     V^T[d][key] (+16 B row pad), with the key quads of each 16-key group
-//     permuted so that one 16-byte LDS read yields the 8 keys an MFMA lane
-//     needs.
+//     Both are stored row-major [key][d] with 16-byte row writes; the row
+//     pads (16 B for K, 64 B for V) keep every LDS read pattern below free of
+//     bank conflicts.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K tile rows (keys), B =
 //     Q^T held in registers for the whole loop (lane = query column).  The
 //     accumulator layout puts one query per lane column, so the row max and
 //     row sum over keys are in-lane except for one exchange with lane^32.
-//   * online softmax in the log2 domain (scale*log2e folded into one multiply),
-//     P rounded to bf16, then O^T += V^T P^T with the same MFMA: A = V^T from
-//     LDS, B = P^T straight from the S^T accumulator registers (no shuffle).
+//   * online softmax in the log2 domain (scale*log2e folded into one FMA),
+//     P rounded to bf16, then O^T += V^T P^T with the same MFMA: B = P^T
+//     straight from the S^T accumulator registers (no shuffle), A = V^T read
+//     with gfx950's transposing LDS load (ds_read_b64_tr_b16): within each
+//     16-lane group, lane i receives element i%4 of the 8-byte chunks
+//     addressed by lanes i/4 + 4e (e = 0..3), so pointing the source lanes at
+//     4 key rows x 4 column quads yields 4 consecutive keys of one d per lane.
 //   * epilogue: O = acc / l, LSE = ln2 * (m + log2 l); an empty key set gives
 //     O = 0, LSE = -inf.
 // The three cache modes differ only in where tile t's keys come from: the
@@ -31,9 +34,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
 struct Layout {
-  static constexpr int KROW = D + 8;               // bf16 per K row in LDS
-  static constexpr int VROW = kTileKeys + 8;       // bf16 per V^T row in LDS
-  static constexpr int STAGE = kTileKeys * KROW + D * VROW;
+  static constexpr int KROW = D + 8;               // bf16 per K row in LDS (+16 B)
+  static constexpr int VROW = D + 32;              // bf16 per V row in LDS (+64 B)
+  static constexpr int STAGE = kTileKeys * (KROW + VROW);
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
 };
 
@@ -41,90 +44,50 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4_t& v, int e) {
-  const uint32_t w = v[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 // Global -> register staging of one K/V tile and register -> LDS store.
+// Thread c of the workgroup moves 16-byte chunks c, c + NT, ... of each
+// 64 x D tile (row = chunk / (D/8)); rows past the tile length are zero.
 template <int D, int NT>
 struct TileStage {
   using L = Layout<D>;
-  static constexpr int NK = (kTileKeys * L::CPR) / NT;           // K chunks / thread
-  static constexpr int NVB = 16 * L::CPR;                         // (4-key, 8-d) blocks
-  static constexpr int NV = (NVB + NT - 1) / NT;                  // V blocks / thread
-  u32x4_t kr[NK];
-  u32x4_t vr[NV][4];
+  static constexpr int N = (kTileKeys * L::CPR) / NT;            // chunks / thread
+  u32x4_t kr[N];
+  u32x4_t vr[N];
 
   __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb,
                                        int64_t stride, int len, int tid) {
-    if (len == kTileKeys) {
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int c = tid + i * NT;
-        kr[i] = ld16(kb + (c / L::CPR) * stride + (c % L::CPR) * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int b = tid + i * NT;
-        if (NV * NT > NVB && b >= NVB) continue;
-        const uint16_t* src = vb + 4 * (b / L::CPR) * stride + (b % L::CPR) * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[i][e] = ld16(src + e * stride);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
+    for (int i = 0; i < N; ++i) {
       const int c = tid + i * NT;
       const int row = c / L::CPR;
-      const int col = c % L::CPR;
-      kr[i] = row < len ? ld16(kb + row * stride + col * 8) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int b = tid + i * NT;
-      const int kq = b / L::CPR;
-      const int dc = b % L::CPR;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        vr[i][e] = (b < NVB && row < len) ? ld16(vb + row * stride + dc * 8)
-                                          : u32x4_t{0, 0, 0, 0};
-      }
+      const int64_t off = row * stride + (c % L::CPR) * 8;
+      const bool ok = len == kTileKeys || row < len;
+      kr[i] = ok ? ld16(kb + off) : u32x4_t{0, 0, 0, 0};
+      vr[i] = ok ? ld16(vb + off) : u32x4_t{0, 0, 0, 0};
     }
   }
 
   __device__ __forceinline__ void store(uint16_t* stage, int tid) const {
     uint16_t* ks = stage;
-    uint16_t* vt = stage + kTileKeys * L::KROW;
+    uint16_t* vs = stage + kTileKeys * L::KROW;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
+    for (int i = 0; i < N; ++i) {
       const int c = tid + i * NT;
       const int row = c / L::CPR;
-      const int col = c % L::CPR;
-      *reinterpret_cast<u32x4_t*>(ks + row * L::KROW + col * 8) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int b = tid + i * NT;
-      if (b >= NVB) continue;
-      const int kq = b / L::CPR;
-      const int dc = b % L::CPR;
-      const int g = kq >> 2;
-      const int qi = kq & 3;
-      // quads 0,1,2,3 of a 16-key group are stored at quad slots 0,2,1,3
-      const int pos = 16 * g + 4 * (((qi & 1) << 1) | (qi >> 1));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2_t w;
-        w[0] = half_of(vr[i][0], e) | (half_of(vr[i][1], e) << 16);
-        w[1] = half_of(vr[i][2], e) | (half_of(vr[i][3], e) << 16);
-        *reinterpret_cast<u32x2_t*>(vt + (8 * dc + e) * L::VROW + pos) = w;
-      }
+      const int col = (c % L::CPR) * 8;
+      *reinterpret_cast<u32x4_t*>(ks + row * L::KROW + col) = kr[i];
+      *reinterpret_cast<u32x4_t*>(vs + row * L::VROW + col) = vr[i];
     }
   }
 };
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposing LDS read of 4 bf16 (see the header comment for the lane layout).
+__device__ __forceinline__ s16x4_t ld_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<uint16_t*>(p)));
+}
 
 // Two waves per SIMD: caps VGPR + AGPR at 256 per lane so that two 4-wave
 // workgroups share a CU and one wave's softmax overlaps the other's MFMAs.
@@ -259,7 +222,11 @@ void attn_fwd_kernel(const AttnParams p) {
       stg.load(kh + off, vh + off, p.ks_n, len, tid);
     }
     const uint16_t* ks = smem + (t & 1) * L::STAGE;
-    const uint16_t* vt = ks + kTileKeys * L::KROW;
+    // this lane's source address for the transposing V reads: key row
+    // 4*(lane/32) + (lane%16)/4, column 16*((lane/16)%2) + 4*(lane%4)
+    const uint16_t* vtr = ks + kTileKeys * L::KROW +
+                          (4 * hg + ((lane & 15) >> 2)) * L::VROW +
+                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // S^T = K Q^T for two 32-key sub-tiles
     f32x16_t s[2];
@@ -319,10 +286,15 @@ void attn_fwd_kernel(const AttnParams p) {
           pf[e] = pe;
         }
         const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
-        const uint16_t* vp = vt + col * L::VROW + 16 * (2 * kt + u) + 8 * hg;
+        // A = V^T rows d = 32dt + (lane & 31), keys 32kt + 16u + {4hg..4hg+3,
+        // 8+4hg..8+4hg+3}: two transposing reads of 4 keys each.
+        const uint16_t* vp = vtr + (32 * kt + 16 * u) * L::VROW;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vp + 32 * dt * L::VROW);
+          const s16x4_t lo = ld_tr4(vp + 32 * dt);
+          const s16x4_t hi = ld_tr4(vp + 8 * L::VROW + 32 * dt);
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
         }
       }
