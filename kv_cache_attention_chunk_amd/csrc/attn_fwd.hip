@@ -56,14 +56,23 @@ struct TileStage {
 
   __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb,
                                        int64_t stride, int len, int tid) {
+    if (len == kTileKeys) {          // full tile: no per-row predicates
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int c = tid + i * NT;
+        const int64_t off = (c / L::CPR) * stride + (c % L::CPR) * 8;
+        kr[i] = ld16(kb + off);
+        vr[i] = ld16(vb + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + i * NT;
       const int row = c / L::CPR;
       const int64_t off = row * stride + (c % L::CPR) * 8;
-      const bool ok = len == kTileKeys || row < len;
-      kr[i] = ok ? ld16(kb + off) : u32x4_t{0, 0, 0, 0};
-      vr[i] = ok ? ld16(vb + off) : u32x4_t{0, 0, 0, 0};
+      kr[i] = row < len ? ld16(kb + off) : u32x4_t{0, 0, 0, 0};
+      vr[i] = row < len ? ld16(vb + off) : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -80,6 +89,20 @@ struct TileStage {
     }
   }
 };
+
+// max of x over lanes l and l ^ 32 (the two halves of one query column),
+// exchanged with v_permlane32_swap instead of an LDS permute.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                   false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                   false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -258,7 +281,7 @@ void attn_fwd_kernel(const AttnParams p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+    mx = half_max(mx) * p.scale_log2;
     // The exponent base m is the exact running row max, so the largest weight
     // of a row is exactly 1 and survives the bf16 rounding of P unchanged.
     // The O accumulator is rescaled only when some row of the wave found a
@@ -281,9 +304,8 @@ void attn_fwd_kernel(const AttnParams p) {
         f32x8_t pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + e], p.scale_log2, -m_use));
-          l += pe;
-          pf[e] = pe;
+          pf[e] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + e], p.scale_log2, -m_use));
+          l += pf[e];    // float32 weights: the LSE must not carry bf16 rounding
         }
         const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
         // A = V^T rows d = 32dt + (lane & 31), keys 32kt + 16u + {4hg..4hg+3,
@@ -305,7 +327,7 @@ void attn_fwd_kernel(const AttnParams p) {
   }
 
   // ---- epilogue --------------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
     const int64_t obase = b * p.os_b + (int64_t)qrow * p.os_n + h * p.os_h;
