@@ -2,15 +2,22 @@
 //
 // One workgroup owns NW*32 query rows of one (b, h) and streams that head's
 // key set in 64-token tiles:
-//   * K and V tiles go global -> registers -> LDS, double buffered; the next
-//     tile's global loads are in flight while the current tile is computed.
-//     Both are stored row-major [key][d] with 16-byte row writes; the row
-//     pads (16 B for K, 64 B for V) keep every LDS read pattern below free of
-//     bank conflicts.
+//   * K and V tiles go straight from global memory to LDS with buffer loads
+//     (buffer_load_dwordx4 ... lds, 1 KB per wave instruction): no staging
+//     registers, and the buffer range check returns zeros for rows past a
+//     partial tile.  K is triple- and V double-buffered; the loads for K(t+2)
+//     and V(t+1) are in flight during the whole of iteration t.
+//   * LDS rows are unpadded and XOR-swizzled by 16-byte chunk so that every
+//     read pattern below is free of bank conflicts: K chunk c of row r sits at
+//     c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64); V chunk c at
+//     c ^ 4(r & 3) (d = 128) or c ^ 4((r >> 1) & 1) (d = 64).
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K tile rows (keys), B =
 //     Q^T held in registers for the whole loop (lane = query column).  The
 //     accumulator layout puts one query per lane column, so the row max and
 //     row sum over keys are in-lane except for one exchange with lane^32.
+//   * software pipeline: iteration t issues the QK MFMAs of tile t+1 before
+//     the softmax of tile t, so the softmax VALU work overlaps matrix work of
+//     the same wave (two score register sets alternate).
 //   * online softmax in the log2 domain (scale*log2e folded into one FMA),
 //     P rounded to bf16, then O^T += V^T P^T with the same MFMA: B = P^T
 //     straight from the S^T accumulator registers (no shuffle), A = V^T read
@@ -31,67 +38,26 @@ namespace chunkattn {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
 template <int D>
 struct Layout {
-  static constexpr int KROW = D + 8;               // bf16 per K row in LDS (+16 B)
-  static constexpr int VROW = D + 32;              // bf16 per V row in LDS (+64 B)
-  static constexpr int STAGE = kTileKeys * (KROW + VROW);
-  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int ROWB = 2 * D;                    // bytes per K / V row
+  static constexpr int TILEB = kTileKeys * ROWB;        // bytes per K or V tile
+  static constexpr int KSTAGES = 3;
+  static constexpr int VSTAGES = 2;
+  static constexpr int LDSB = (KSTAGES + VSTAGES) * TILEB;
+  // physical 16-byte chunk of logical chunk c in row r
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Global -> register staging of one K/V tile and register -> LDS store.
-// Thread c of the workgroup moves 16-byte chunks c, c + NT, ... of each
-// 64 x D tile (row = chunk / (D/8)); rows past the tile length are zero.
-template <int D, int NT>
-struct TileStage {
-  using L = Layout<D>;
-  static constexpr int N = (kTileKeys * L::CPR) / NT;            // chunks / thread
-  u32x4_t kr[N];
-  u32x4_t vr[N];
-
-  __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb,
-                                       int64_t stride, int len, int tid) {
-    if (len == kTileKeys) {          // full tile: no per-row predicates
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int c = tid + i * NT;
-        const int64_t off = (c / L::CPR) * stride + (c % L::CPR) * 8;
-        kr[i] = ld16(kb + off);
-        vr[i] = ld16(vb + off);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / L::CPR;
-      const int64_t off = row * stride + (c % L::CPR) * 8;
-      kr[i] = row < len ? ld16(kb + off) : u32x4_t{0, 0, 0, 0};
-      vr[i] = row < len ? ld16(vb + off) : u32x4_t{0, 0, 0, 0};
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* stage, int tid) const {
-    uint16_t* ks = stage;
-    uint16_t* vs = stage + kTileKeys * L::KROW;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / L::CPR;
-      const int col = (c % L::CPR) * 8;
-      *reinterpret_cast<u32x4_t*>(ks + row * L::KROW + col) = kr[i];
-      *reinterpret_cast<u32x4_t*>(vs + row * L::VROW + col) = vr[i];
-    }
-  }
-};
-
-// max of x over lanes l and l ^ 32 (the two halves of one query column),
-// exchanged with v_permlane32_swap instead of an LDS permute.
+// max / sum of x over lanes l and l ^ 32 (the two halves of one query
+// column), exchanged with v_permlane32_swap instead of an LDS permute.
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                    false, false);
@@ -106,11 +72,76 @@ __device__ __forceinline__ float half_sum(float x) {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Transposing LDS read of 4 bf16 (see the header comment for the lane layout).
-__device__ __forceinline__ s16x4_t ld_tr4(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<uint16_t*>(p)));
+__device__ __forceinline__ s16x4_t ld_tr4(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p)));
 }
+
+// Per-lane byte offsets of the buffer->LDS loads of one 64 x D tile: wave w's
+// instruction j fills LDS bytes [(NI w + j) KB, +1 KB), lane i the 16 bytes at
+// +16 i, i.e. physical row r and chunk pc; it loads logical chunk
+// pc ^ swizzle(r) of row r.
+template <int D, int NW>
+struct TileLoader {
+  using L = Layout<D>;
+  static constexpr int NI = L::TILEB / (1024 * NW);
+  uint32_t koff[NI], voff[NI];
+  int wave;
+
+  __device__ __forceinline__ void init(int lane, int wave_, uint32_t stride_bytes) {
+    wave = wave_;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int pbyte = (NI * wave + j) * 1024 + 16 * lane;
+      const int r = pbyte / L::ROWB;
+      const int pc = (pbyte % L::ROWB) / 16;
+      koff[j] = r * stride_bytes + 16 * (pc ^ L::swz_k(r));
+      voff[j] = r * stride_bytes + 16 * (pc ^ L::swz_v(r));
+    }
+  }
+
+  // Loads rows [0, len) of the tile whose row 0 is at kb / vb; rows past len
+  // (and all rows when len == 0) are written as zeros by the range check.
+  __device__ __forceinline__ void issue(const uint16_t* kb, const uint16_t* vb, int len,
+                                        uint32_t stride_bytes, char* lk, char* lv) const {
+    const int nrec = len * (int)stride_bytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, nrec, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (NI * wave + j) * 1024), 16,
+                                               (int)koff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (NI * wave + j) * 1024), 16,
+                                               (int)voff[j], 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void issue_k(const uint16_t* kb, int len, uint32_t stride_bytes,
+                                          char* lk) const {
+    const int nrec = len * (int)stride_bytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, nrec, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (NI * wave + j) * 1024), 16,
+                                               (int)koff[j], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void issue_v(const uint16_t* vb, int len, uint32_t stride_bytes,
+                                          char* lv) const {
+    const int nrec = len * (int)stride_bytes;
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, nrec, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (NI * wave + j) * 1024), 16,
+                                               (int)voff[j], 0, 0, 0);
+  }
+};
 
 // Two waves per SIMD: caps VGPR + AGPR at 256 per lane so that two 4-wave
 // workgroups share a CU and one wave's softmax overlaps the other's MFMAs.
@@ -118,15 +149,16 @@ template <int D, int NW, int MODE, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const AttnParams p) {
   using L = Layout<D>;
-  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int NST = D / 16;     // MFMA k-steps over d for S
   constexpr int NDT = D / 32;     // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[L::LDSB];
+  char* const kst = smem;                                  // K stages
+  char* const vst = smem + L::KSTAGES * L::TILEB;          // V stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;      // query column (B/C operands) or A-operand row
   const int hg = lane >> 5;       // lane half: selects k sub-range / row quad
 
@@ -188,20 +220,25 @@ void attn_fwd_kernel(const AttnParams p) {
     vh = p.v + b * p.ks_b + h * p.ks_h;
   }
 
+  // tile t -> (element offset of its row 0, number of valid rows)
   auto tile_src = [&](int t, int64_t& off, int& len) {
     if (MODE == MODE_BLOCKS) {
       const int id = p.indices[list0 + t];
-      int s = 0, l = 0;
-      if (id >= 0 && id < p.nkb) block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s, l);
-      off = (int64_t)s * p.ks_n;
-      len = l;
+      int s0 = 0, l0 = 0;
+      if (id >= 0 && id < p.nkb) block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0);
+      off = (int64_t)s0 * p.ks_n;
+      len = l0;
     } else {
-      const int s = t * kTileKeys;
-      const int rest = kv_len - s;
-      off = (int64_t)(kv_lo + s) * p.ks_n;
+      const int s0 = t * kTileKeys;
+      const int rest = kv_len - s0;
+      off = (int64_t)(kv_lo + s0) * p.ks_n;
       len = rest < kTileKeys ? rest : kTileKeys;
     }
   };
+
+  const uint32_t stride_bytes = (uint32_t)(p.ks_n * 2);
+  TileLoader<D, NW> ldr;
+  ldr.init(lane, wave, stride_bytes);
 
   // ---- Q^T operand in registers ---------------------------------------------
   const int qr = wave * 32 + col;
@@ -217,70 +254,57 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   }
 
+  // Per-lane LDS read addresses.  Row base, stage offset and the swizzled
+  // chunk occupy disjoint address bits, so each read is (base | swizzle) ^
+  // (step * chunk), one v_xor per read.
+  //   K rows 32kt + col, chunk 2st + hg: byte 16((2st + hg) ^ kz)
+  //     = 32(st ^ (kz >> 1)) + 16(hg ^ (kz & 1)).
+  const int kz = L::swz_k(col);
+  const int kbx = col * L::ROWB + 16 * (hg ^ (kz & 1)) + 32 * (kz >> 1);
+  //   V source row 4hg + (lane & 15)/4 (+ 32kt + 16u + 8 half), chunk
+  //   4dt + vcol16: byte 16((4dt + vcol16) ^ vz) = 64(dt ^ vz/4) + 16 vcol16.
+  const int vz = D == 128 ? ((lane & 15) >> 2) : ((lane >> 3) & 1);
+  const int vcol16 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vbx = (4 * hg + ((lane & 15) >> 2)) * L::ROWB + 8 * (lane & 1) + 16 * vcol16 + 64 * vz;
+
   f32x16_t acc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = f32x16_t{};
   float m = -INFINITY;   // running max, log2 domain
   float l = 0.f;         // this lane's partial row sum
 
-  TileStage<D, NT> stg;
-  if (ntiles > 0) {
-    int64_t off;
-    int len;
-    tile_src(0, off, len);
-    stg.load(kh + off, vh + off, p.ks_n, len, tid);
-    stg.store(smem, tid);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    int64_t off_cur;
-    int len_cur;
-    tile_src(t, off_cur, len_cur);
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      int64_t off;
-      int len;
-      tile_src(t + 1, off, len);
-      stg.load(kh + off, vh + off, p.ks_n, len, tid);
-    }
-    const uint16_t* ks = smem + (t & 1) * L::STAGE;
-    // this lane's source address for the transposing V reads: key row
-    // 4*(lane/32) + (lane%16)/4, column 16*((lane/16)%2) + 4*(lane%4)
-    const uint16_t* vtr = ks + kTileKeys * L::KROW +
-                          (4 * hg + ((lane & 15) >> 2)) * L::VROW +
-                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    // S^T = K Q^T for two 32-key sub-tiles
-    f32x16_t s[2];
+  // S^T = K Q^T for the two 32-key halves of the tile in K stage ks
+  auto qk = [&](int ks, f32x16_t (&sc)[2]) {
+    const int kb = ks * L::TILEB + kbx;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16_t{};
-      const uint16_t* kp = ks + (32 * kt + col) * L::KROW + 8 * hg;
+      sc[kt] = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + 16 * st);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], s[kt], 0, 0, 0);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            kst + (kb ^ (32 * st)) + kt * 32 * L::ROWB);
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sc[kt], 0, 0, 0);
       }
     }
+  };
 
-    // online softmax in the log2 domain; key of s[kt][i] = 32kt + 8(i/4) + 4hg + i%4.
-    // Row max of the raw scores (scale > 0 keeps the order), one exchange
-    // with lane^32 (the other half of the same query column).
+  // online softmax of one tile's scores, then O^T += V^T P^T from V stage vs
+  auto softmax_pv = [&](f32x16_t (&sc)[2], int len_cur, int vs) {
+    // key of sc[kt][i] = 32kt + 8(i/4) + 4hg + i%4
     if (len_cur < kTileKeys) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
-          if (key >= len_cur) s[kt][i] = -INFINITY;
+          if (key >= len_cur) sc[kt][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
     mx = half_max(mx) * p.scale_log2;
     // The exponent base m is the exact running row max, so the largest weight
     // of a row is exactly 1 and survives the bf16 rounding of P unchanged.
@@ -296,7 +320,7 @@ void attn_fwd_kernel(const AttnParams p) {
       for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
     }
     const float m_use = m == -INFINITY ? 0.f : m;
-
+    const int vb = vs * L::TILEB + vbx;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -304,26 +328,71 @@ void attn_fwd_kernel(const AttnParams p) {
         f32x8_t pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pf[e] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + e], p.scale_log2, -m_use));
+          pf[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * u + e], p.scale_log2, -m_use));
           l += pf[e];    // float32 weights: the LSE must not carry bf16 rounding
         }
         const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
         // A = V^T rows d = 32dt + (lane & 31), keys 32kt + 16u + {4hg..4hg+3,
         // 8+4hg..8+4hg+3}: two transposing reads of 4 keys each.
-        const uint16_t* vp = vtr + (32 * kt + 16 * u) * L::VROW;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const s16x4_t lo = ld_tr4(vp + 32 * dt);
-          const s16x4_t hi = ld_tr4(vp + 8 * L::VROW + 32 * dt);
+          const char* vp = vst + (vb ^ (64 * dt)) + (32 * kt + 16 * u) * L::ROWB;
+          const s16x4_t lo = ld_tr4(vp);
+          const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
           const bf16x8_t a = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
         }
       }
     }
+  };
 
-    if (more) stg.store(smem + ((t + 1) & 1) * L::STAGE, tid);
+  auto issue_k = [&](int t) {
+    int64_t off;
+    int len;
+    tile_src(t, off, len);
+    ldr.issue_k(kh + off, len, stride_bytes, kst + (t % L::KSTAGES) * L::TILEB);
+  };
+  auto issue_v = [&](int t) {
+    int64_t off;
+    int len;
+    tile_src(t, off, len);
+    ldr.issue_v(vh + off, len, stride_bytes, vst + (t % L::VSTAGES) * L::TILEB);
+  };
+  auto tile_len = [&](int t) {
+    int64_t off;
+    int len;
+    tile_src(t, off, len);
+    return len;
+  };
+  auto sync_loads = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  // one pipeline step: loads for K(t+2), V(t+1); QK(t+1) -> nx; softmax +
+  // PV of tile t from cur
+  auto step = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
+    if (t + 2 < ntiles) issue_k(t + 2);
+    if (t + 1 < ntiles) {
+      issue_v(t + 1);
+      qk((t + 1) % L::KSTAGES, nx);
+    }
+    softmax_pv(cur, tile_len(t), t % L::VSTAGES);
+    sync_loads();
+  };
+
+  f32x16_t sa[2], sb[2];
+  if (ntiles > 0) {
+    issue_k(0);
+    issue_v(0);
+    if (ntiles > 1) issue_k(1);
+    sync_loads();
+    qk(0, sa);
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, sa, sb);
+      if (t + 1 < ntiles) step(t + 1, sb, sa);
+    }
   }
 
   // ---- epilogue --------------------------------------------------------------
