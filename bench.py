@@ -172,15 +172,17 @@ def main():
         for key in ("local_blocks", "history_blocks"))
     _, _, info = sparse()
     torch.cuda.synchronize()
-    ip = info["indptr"].cpu().numpy()
-    ix = info["indices"].cpu().numpy()[:ip[-1]]
+
     def block_len(j):           # frame-aligned tiling: 25 blocks per 1560-token frame
         r = j % 25
         return np.minimum(64, 1560 - 64 * r)
-    toks = np.array([block_len(ix[ip[r]:ip[r + 1]]).sum() for r in range(len(ip) - 1)])
     nqb = ca.num_blocks(Nq, 64, 1560)
+    sp, sx = info["shared_indptr"].cpu().numpy(), info["shared_indices"].cpu().numpy()
+    lp, lx = info["local_indptr"].cpu().numpy(), info["local_indices"].cpu().numpy()
+    shared_toks = np.array([block_len(sx[sp[r]:sp[r + 1]]).sum() for r in range(B * H)])
+    local_toks = np.array([block_len(lx[lp[r]:lp[r + 1]]).sum() for r in range(B * H * nqb)])
     qlen = np.tile(block_len(np.arange(nqb)), B * H)
-    f_sparse = 4.0 * d * float((toks * qlen).sum())
+    f_sparse = 4.0 * d * (float(shared_toks.sum()) * Nq + float((local_toks * qlen).sum()))
     f_step = f_dense + f_merge + f_sparse if args.only == "step" else f_dense
 
     stream = torch.cuda.current_stream()

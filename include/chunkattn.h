@@ -89,6 +89,14 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  *   kv_nnz       number of entries of kv_indices; row spans are clamped to it.
  *   kv_block     1..64; kv_seg >= 1; q_block >= 1; q_seg >= 1 (block mode)
  *   scale        softmax scale, finite and > 0 (1/sqrt(d) for the pages' models)
+ *   o_init,      NULL, NULL -> plain attention.  Else the float32 O [B, Nq, H, d]
+ *   lse_init     (strides o_init_strides) and LSE [B, H, Nq] of attention over
+ *                another, disjoint key set: the softmax state starts from it, so
+ *                the outputs are the LSE merge of that branch with this call's
+ *                key set (ISPA page, section 2 item 1: local and history
+ *                branches combined through the LSE), without a separate pass.
+ *                o may alias o_init (float32 output, same strides) and lse may
+ *                alias lse_init.
  *   o            [B, Nq, H, d] of o_dtype (CA_BF16 or CA_F32), strides o_strides
  *   lse          float32 [B, H, Nq]; an empty key set gives O = 0, LSE = -inf
  */
@@ -97,8 +105,9 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       const int64_t* q_strides, const int64_t* kv_strides,
                       const int64_t* o_strides,
                       const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
-                      int kv_block, int kv_seg, int q_block, int q_seg,
-                      float scale, void* o, int o_dtype, float* lse, void* stream);
+                      int kv_block, int kv_seg, int q_block, int q_seg, float scale,
+                      const float* o_init, const int64_t* o_init_strides, const float* lse_init,
+                      void* o, int o_dtype, float* lse, void* stream);
 
 /*
  * Chunk attention over ragged per-head caches (Pyramid Forcing page, section
@@ -161,11 +170,14 @@ int ca_lse_merge(const void* o1, const float* lse1, const void* o2, const float*
  * Block representatives (Sparse Forcing page, section 2 item 2: each block is
  * compressed to one representative token for coarse scoring): the mean of
  * each block's tokens, accumulated in float32.
- *   x    bf16 [B, N, H, d], strides x_strides (host); d a multiple of 8, <= 512
- *   out  float32 [B, H, NB, d] contiguous, NB = ca_num_blocks(N, block, seg)
+ *   x          bf16 [B, N, H, d], strides x_strides (host); d a multiple of 8, <= 512
+ *   out        float32 [B, H, NB, d] contiguous, NB = ca_num_blocks(N, block, seg)
+ *   out_total  optional (NULL allowed) float32 [B, H, 1, d]: the mean over all N
+ *              tokens (the chunk-mean query used to pick persistent blocks),
+ *              formed from the block means weighted by block length.
  */
 int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_strides,
-                  int block_size, int seg_len, float* out, void* stream);
+                  int block_size, int seg_len, float* out, float* out_total, void* stream);
 
 /*
  * Coarse block scores and top-K (Sparse Forcing page, section 2 items 1-2:

@@ -29,7 +29,8 @@ SIGNATURES = {
     "ca_last_error": (ctypes.c_char_p, []),
     "ca_num_blocks": (_i, [_i, _i, _i]),
     "ca_chunk_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
-                               _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p]),
+                               _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i64p, _p,
+                               _p, _i, _p, _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
                                       _i64p, _i64, _i64p, _f, _p, _i, _p, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
@@ -37,7 +38,7 @@ SIGNATURES = {
                                      _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _p]),
     "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
                           _i64p, _i64p, _i64p, _p]),
-    "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p]),
+    "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),
     "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "ca_build_kv_index": (_i, [_i, _i, _i, _i, _i, _i32p, _i, _i32p, _i, _i, _p, _p, _p]),
 }

@@ -92,10 +92,13 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                    kv_block: int = 64, kv_seg: Optional[int] = None,
                    q_block: int = 64, q_seg: Optional[int] = None,
                    scale: Optional[float] = None, out_dtype=None,
-                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   o_init: Optional[torch.Tensor] = None, lse_init: Optional[torch.Tensor] = None
                    ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk attention against a dense cache, or against per-query-block
     block lists (CSR kv_indptr / kv_indices) when given.  Returns (O, LSE).
+    With (o_init float32 [B,Nq,H,d], lse_init [B,H,Nq]) from attention over a
+    disjoint key set, the result is their LSE merge with this key set.
     The output dtype is out_dtype, else out's dtype, else bf16."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q), _bshd("k", k), _bshd("v", v)
@@ -111,11 +114,22 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nnz = 0 if kv_indices is None else kv_indices.numel()
+    if (o_init is None) != (lse_init is None):
+        raise ValueError("o_init and lse_init go together")
+    if o_init is not None:
+        _bshd("o_init", o_init, torch.float32)
+        if tuple(o_init.shape) != (B, Nq, H, d):
+            raise ValueError("o_init shape")
+        if lse_init.dtype != torch.float32 or tuple(lse_init.shape) != (B, H, Nq) or \
+                not lse_init.is_contiguous():
+            raise ValueError("lse_init must be contiguous float32 [B, H, Nq]")
     st = lib().ca_chunk_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d,
         _st(q), _st(k), _st(o),
         _ptr(kv_indptr), _ptr(kv_indices), nnz, kv_block, kv_seg or max(Nkv, 1),
-        q_block, q_seg or max(Nq, 1), sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+        q_block, q_seg or max(Nq, 1), sc, _ptr(o_init),
+        None if o_init is None else _st(o_init), _ptr(lse_init),
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
     check(st)
     return o, l
 
@@ -218,8 +232,10 @@ def lse_merge(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torc
 
 
 def block_mean(x: torch.Tensor, block_size: int = 64, seg_len: Optional[int] = None,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Block representatives: mean of each block's tokens -> float32 [B, H, NB, d]."""
+               out: Optional[torch.Tensor] = None, with_total: bool = False):
+    """Block representatives: mean of each block's tokens -> float32
+    [B, H, NB, d]; with_total also returns the mean over all N tokens
+    [B, H, 1, d] (the chunk-mean query)."""
     _bshd("x", x)
     B, N, H, d = x.shape
     seg = seg_len or max(N, 1)
@@ -228,10 +244,11 @@ def block_mean(x: torch.Tensor, block_size: int = 64, seg_len: Optional[int] = N
         out = torch.empty((B, H, nb, d), dtype=torch.float32, device=x.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, nb, d) or not out.is_contiguous():
         raise ValueError("out must be contiguous float32 [B, H, NB, d]")
+    tot = torch.empty((B, H, 1, d), dtype=torch.float32, device=x.device) if with_total else None
     st = lib().ca_block_mean(x.data_ptr(), B, N, H, d, _st(x), block_size, seg,
-                             out.data_ptr(), _stream())
+                             out.data_ptr(), _ptr(tot), _stream())
     check(st)
-    return out
+    return (out, tot) if with_total else out
 
 
 def block_score_topk(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *, cand_begin: int = 0,
@@ -277,22 +294,34 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
                      seg: Optional[int] = None, k_mean: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, out_dtype=torch.bfloat16):
     """The block-sparse path in the Sparse Forcing order: block means of Q and
-    K, persistent blocks = top-C history blocks against the chunk-mean query,
-    top-K local-window blocks per query block, PBSA block lists, attention.
+    K (and the chunk-mean query), persistent blocks = top-C history blocks
+    against the chunk-mean query, top-K local-window blocks per query block,
+    then PBSA attention: dense over the blocks every query block shares (sink
+    + persistent, one list per head, float32 branch output), continued per
+    query block over its top-K local blocks by resuming from that branch's
+    (O, LSE) state.  The sink, history and local id ranges must be disjoint.
     `k_mean` may carry precomputed key-block means (resident cache state).
-    Returns (O, LSE, info) with the selected ids and the CSR in `info`."""
+    Returns (O, LSE, info) with the selected ids and block lists in `info`."""
     B, Nq, H, d = q.shape
     seg = seg or Nq
-    qm = block_mean(q, block, seg)
+    ranges = sorted([(sink_begin, sink_count), (hist_begin, hist_count), (local_begin, local_count)])
+    if any(a[0] + a[1] > b[0] for a, b in zip(ranges, ranges[1:])):
+        raise ValueError("sink, history and local block ranges must be disjoint")
+    qm, cm = block_mean(q, block, seg, with_total=True)
     km = block_mean(k, block, seg) if k_mean is None else k_mean
-    cm = block_mean(q, Nq, Nq)
     pers = block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count) if C else None
     loc = block_score_topk(qm, km, K, cand_begin=local_begin, cand_count=local_count) if K else None
     nqb = qm.shape[2]
-    indptr, indices = build_kv_index(B, H, nqb, sink_begin, sink_count,
-                                     None if pers is None else pers[:, :, 0, :].contiguous(),
-                                     loc, 0, device=q.device)
-    o, l = chunk_attn_fwd(q, k, v, kv_indptr=indptr, kv_indices=indices, kv_block=block,
-                          kv_seg=seg, q_block=block, q_seg=seg, scale=scale, out_dtype=out_dtype)
+    sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
+                                    None if pers is None else pers[:, :, 0, :].contiguous(),
+                                    None, 0, device=q.device)
+    o1, l1 = chunk_attn_fwd(q, k, v, kv_indptr=sh_ptr, kv_indices=sh_idx, kv_block=block,
+                            kv_seg=seg, q_block=Nq, q_seg=Nq, scale=scale,
+                            out_dtype=torch.float32)
+    lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, loc, 0, device=q.device)
+    o, l = chunk_attn_fwd(q, k, v, kv_indptr=lo_ptr, kv_indices=lo_idx, kv_block=block,
+                          kv_seg=seg, q_block=block, q_seg=seg, scale=scale,
+                          out_dtype=out_dtype, o_init=o1, lse_init=l1)
     return o, l, {"q_mean": qm, "k_mean": km, "chunk_mean": cm, "persistent": pers,
-                  "local": loc, "indptr": indptr, "indices": indices}
+                  "local": loc, "shared_indptr": sh_ptr, "shared_indices": sh_idx,
+                  "local_indptr": lo_ptr, "local_indices": lo_idx}

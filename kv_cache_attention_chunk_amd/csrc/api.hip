@@ -152,6 +152,7 @@ void fill_blocks(AttnParams& p, int Nq, int Nkv, const int32_t* indptr, const in
   p.kv_block = kv_block;
   p.kv_seg = kv_seg;
   p.kv_bps = (kv_seg + kv_block - 1) / kv_block;
+  p.kv_bps_magic = (uint32_t)((((uint64_t)1) << 32) / (uint64_t)p.kv_bps);
   p.nkb = num_blocks(Nkv, kv_block, kv_seg);
   p.q_block = q_block;
   p.q_seg = q_seg;
@@ -195,14 +196,25 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
                       int d, const int64_t* q_strides, const int64_t* kv_strides,
                       const int64_t* o_strides, const int32_t* kv_indptr,
                       const int32_t* kv_indices, int kv_nnz, int kv_block, int kv_seg,
-                      int q_block, int q_seg, float scale, void* o, int o_dtype, float* lse,
-                      void* stream) {
+                      int q_block, int q_seg, float scale, const float* o_init,
+                      const int64_t* o_init_strides, const float* lse_init, void* o,
+                      int o_dtype, float* lse, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
+  if ((o_init == nullptr) != (lse_init == nullptr))
+    return fail(CA_EINVAL, "o_init and lse_init must be given together");
+  if (o_init) {
+    if (!aligned16(o_init) || !aligned16(lse_init)) return fail(CA_EINVAL, "o_init, lse_init must be 16-byte aligned");
+    if (int r = check_strides("o_init", o_init_strides, 4)) return r;
+    if (o == o_init && (o_dtype != CA_F32 || o_init_strides[0] != o_strides[0] ||
+                        o_init_strides[1] != o_strides[1] || o_init_strides[2] != o_strides[2]))
+      return fail(CA_EINVAL, "o aliases o_init with a different dtype or strides");
+  }
   if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
   if (Nkv > 0 && (!k || !v)) return fail(CA_EINVAL, "k and v must be non-NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
   if (int r = check_strides("kv", kv_strides, 8)) return r;
+  if (kv_strides[1] < d || kv_strides[1] > (1 << 23)) return fail(CA_ERANGE, "kv row stride outside [d, 2^23]");
   const bool blocks = kv_indptr || kv_indices;
   if (blocks) {
     if (int r = check_csr(kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
@@ -216,6 +228,11 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
   p.v = static_cast<const uint16_t*>(v);
   p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
   p.Nkv = Nkv;
+  if (o_init) {
+    p.o_init = o_init;
+    p.lse_init = lse_init;
+    p.is_b = o_init_strides[0]; p.is_n = o_init_strides[1]; p.is_h = o_init_strides[2];
+  }
   if (blocks) {
     fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
     return launch_heads(MODE_BLOCKS, c, p, {}, static_cast<hipStream_t>(stream));
@@ -234,7 +251,8 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
   if (total_kv > 0 && (!k_flat || !v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be non-NULL");
   if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
   if (total_kv < 0) return fail(CA_EINVAL, "total_kv < 0");
-  if (kv_row_stride < d || kv_row_stride % 8) return fail(CA_EINVAL, "kv_row_stride must be >= d and a multiple of 8");
+  if (kv_row_stride < d || kv_row_stride % 8 || kv_row_stride > (1 << 23))
+    return fail(CA_EINVAL, "kv_row_stride must be in [d, 2^23] and a multiple of 8");
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0) return fail(CA_EINVAL, "cu_seqlens[0] != 0");
     for (int i = 0; i < B * H; ++i)
@@ -284,6 +302,7 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
     if (!k || !v) return fail(CA_EINVAL, "k and v must be non-NULL");
     if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
     if (int r = check_strides("kv", kv_strides, 8)) return r;
+    if (kv_strides[1] < d || kv_strides[1] > (1 << 23)) return fail(CA_ERANGE, "kv row stride outside [d, 2^23]");
     if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
   }
   if (!hb.empty()) {
@@ -293,7 +312,8 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
     if (!k_flat || !v_flat || !cu_seqlens) return fail(CA_EINVAL, "k_flat, v_flat, cu_seqlens must be non-NULL");
     if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
     if (total_kv < 0) return fail(CA_EINVAL, "total_kv < 0");
-    if (kv_row_stride < d || kv_row_stride % 8) return fail(CA_EINVAL, "kv_row_stride must be >= d and a multiple of 8");
+    if (kv_row_stride < d || kv_row_stride % 8 || kv_row_stride > (1 << 23))
+    return fail(CA_EINVAL, "kv_row_stride must be in [d, 2^23] and a multiple of 8");
   }
   if (int r = check_device()) return r;
   if ((int64_t)B * H * Nq == 0) return ok();
@@ -359,7 +379,7 @@ int ca_lse_merge(const void* o1, const float* lse1, const void* o2, const float*
 }
 
 int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_strides,
-                  int block_size, int seg_len, float* out, void* stream) {
+                  int block_size, int seg_len, float* out, float* out_total, void* stream) {
   if (B < 0 || N < 0 || H < 0) return fail(CA_EINVAL, "negative size");
   if (d <= 0 || d % 8 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 8, <= 512)", d);
   if (block_size < 1 || seg_len < 1) return fail(CA_EINVAL, "block_size and seg_len must be >= 1");
@@ -371,7 +391,7 @@ int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_st
   if (int r = check_device()) return r;
   return launched(launch_block_mean(static_cast<const uint16_t*>(x), B, N, H, d, x_strides,
                                     block_size, seg_len, (seg_len + block_size - 1) / block_size,
-                                    nb, out, static_cast<hipStream_t>(stream)),
+                                    nb, out, out_total, static_cast<hipStream_t>(stream)),
                   "block_mean launch");
 }
 

@@ -102,24 +102,8 @@ struct TileLoader {
     }
   }
 
-  // Loads rows [0, len) of the tile whose row 0 is at kb / vb; rows past len
+  // Loads rows [0, len) of the tile whose row 0 is at kb (vb); rows past len
   // (and all rows when len == 0) are written as zeros by the range check.
-  __device__ __forceinline__ void issue(const uint16_t* kb, const uint16_t* vb, int len,
-                                        uint32_t stride_bytes, char* lk, char* lv) const {
-    const int nrec = len * (int)stride_bytes;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, nrec, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, nrec, kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (NI * wave + j) * 1024), 16,
-                                               (int)koff[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (NI * wave + j) * 1024), 16,
-                                               (int)voff[j], 0, 0, 0);
-    }
-  }
-
   __device__ __forceinline__ void issue_k(const uint16_t* kb, int len, uint32_t stride_bytes,
                                           char* lk) const {
     const int nrec = len * (int)stride_bytes;
@@ -225,7 +209,8 @@ void attn_fwd_kernel(const AttnParams p) {
     if (MODE == MODE_BLOCKS) {
       const int id = p.indices[list0 + t];
       int s0 = 0, l0 = 0;
-      if (id >= 0 && id < p.nkb) block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0);
+      if (id >= 0 && id < p.nkb)
+        block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0, p.kv_bps_magic);
       off = (int64_t)s0 * p.ks_n;
       len = l0;
     } else {
@@ -272,6 +257,22 @@ void attn_fwd_kernel(const AttnParams p) {
   for (int i = 0; i < NDT; ++i) acc[i] = f32x16_t{};
   float m = -INFINITY;   // running max, log2 domain
   float l = 0.f;         // this lane's partial row sum
+  if (p.o_init && qvalid) {
+    // Resume from a previous branch (O1, LSE1): the state (m, l, acc) =
+    // (LSE1 * log2 e, 1, O1) has acc / l = O1 and m + log2 l = LSE1 / ln 2,
+    // i.e. it is that branch's softmax state up to a common scale.
+    m = p.lse_init[(int64_t)bh * p.Nq + qrow] * 1.4426950408889634f;
+    l = hg == 0 ? 1.f : 0.f;            // the two lane halves' sums are added
+    const float* oi = p.o_init + b * p.is_b + (int64_t)qrow * p.is_n + h * p.is_h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(oi + 32 * dt + 8 * r + 4 * hg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[dt][4 * r + e] = x[e];
+      }
+  }
 
   // S^T = K Q^T for the two 32-key halves of the tile in K stage ks
   auto qk = [&](int ks, f32x16_t (&sc)[2]) {
@@ -347,46 +348,44 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   };
 
-  auto issue_k = [&](int t) {
-    int64_t off;
-    int len;
-    tile_src(t, off, len);
-    ldr.issue_k(kh + off, len, stride_bytes, kst + (t % L::KSTAGES) * L::TILEB);
-  };
-  auto issue_v = [&](int t) {
-    int64_t off;
-    int len;
-    tile_src(t, off, len);
-    ldr.issue_v(vh + off, len, stride_bytes, vst + (t % L::VSTAGES) * L::TILEB);
-  };
-  auto tile_len = [&](int t) {
-    int64_t off;
-    int len;
-    tile_src(t, off, len);
-    return len;
-  };
   auto sync_loads = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  // one pipeline step: loads for K(t+2), V(t+1); QK(t+1) -> nx; softmax +
-  // PV of tile t from cur
+  // Tile descriptors are computed once, when a tile's K load is issued, and
+  // carried for its V load (one iteration later) and its softmax mask (two
+  // iterations later).
+  int64_t off0 = 0, off1 = 0, off2 = 0;
+  int len0 = 0, len1 = 0, len2 = 0;
+
+  // one pipeline step for tile t: K(t+2) and V(t+1) loads, QK(t+1) -> nx,
+  // softmax + PV of tile t from cur.  On entry (off0,len0) describe tile t,
+  // (off1,len1) tile t+1; on exit they are shifted by one tile.
   auto step = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
-    if (t + 2 < ntiles) issue_k(t + 2);
+    if (t + 2 < ntiles) {
+      tile_src(t + 2, off2, len2);
+      ldr.issue_k(kh + off2, len2, stride_bytes, kst + ((t + 2) % L::KSTAGES) * L::TILEB);
+    }
     if (t + 1 < ntiles) {
-      issue_v(t + 1);
+      ldr.issue_v(vh + off1, len1, stride_bytes, vst + ((t + 1) % L::VSTAGES) * L::TILEB);
       qk((t + 1) % L::KSTAGES, nx);
     }
-    softmax_pv(cur, tile_len(t), t % L::VSTAGES);
+    softmax_pv(cur, len0, t % L::VSTAGES);
+    off0 = off1; len0 = len1;
+    off1 = off2; len1 = len2;
     sync_loads();
   };
 
   f32x16_t sa[2], sb[2];
   if (ntiles > 0) {
-    issue_k(0);
-    issue_v(0);
-    if (ntiles > 1) issue_k(1);
+    tile_src(0, off0, len0);
+    ldr.issue_k(kh + off0, len0, stride_bytes, kst);
+    ldr.issue_v(vh + off0, len0, stride_bytes, vst);
+    if (ntiles > 1) {
+      tile_src(1, off1, len1);
+      ldr.issue_k(kh + off1, len1, stride_bytes, kst + L::TILEB);
+    }
     sync_loads();
     qk(0, sa);
     for (int t = 0; t < ntiles; t += 2) {

@@ -31,6 +31,9 @@ struct AttnParams {
   int64_t qs_b, qs_n, qs_h;
   int64_t ks_b, ks_n, ks_h;   // varlen: ks_n = flat row stride, ks_b = ks_h = 0
   int64_t os_b, os_n, os_h;
+  const float* o_init;        // optional starting state (float32 O and LSE)
+  const float* lse_init;
+  int64_t is_b, is_n, is_h;
   int B, H, Nq, Nkv;
   float scale_log2;           // softmax scale * log2(e)
   // block-list mode
@@ -38,6 +41,7 @@ struct AttnParams {
   const int32_t* indices;
   int nnz;                    // entries of indices; row spans are clamped to it
   int kv_block, kv_seg, kv_bps, nkb;
+  uint32_t kv_bps_magic;      // floor(2^32 / kv_bps): id / kv_bps by multiply-high
   int q_block, q_seg, q_bps, nqb, q_sub;
   // ragged mode
   const int32_t* cu;
@@ -55,7 +59,7 @@ hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32,
                             const AttnParams& p, hipStream_t stream);
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
                              const int64_t* xs, int block, int seg, int bps, int nb,
-                             float* out, hipStream_t stream);
+                             float* out, float* out_total, hipStream_t stream);
 hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int NQB,
                              int NKB, int d, int cand_begin, int cand_count, int K,
                              int32_t* out_idx, float* out_score, hipStream_t stream);
@@ -80,11 +84,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return x * per + (x < rem ? x : rem) + j;
 }
 
+// id / div for 0 <= id < 2^31 with magic = floor(2^32 / div): the
+// multiply-high estimate is low by at most one, fixed by one correction.
+__host__ __device__ __forceinline__ int div_magic(int id, int div, uint32_t magic) {
+  int q = (int)(((uint64_t)(uint32_t)id * magic) >> 32);
+  if (id - q * div >= div) ++q;
+  return q;
+}
+
 // Start and length of block `id` of the frame-aligned tiling of n tokens
 // (segments of `seg` tokens, `bps` blocks of `block` tokens per segment).
 __host__ __device__ __forceinline__ void block_span(int id, int n, int block, int seg,
-                                                    int bps, int& start, int& len) {
-  const int s = id / bps;
+                                                    int bps, int& start, int& len,
+                                                    uint32_t magic = 0) {
+  const int s = magic ? div_magic(id, bps, magic) : id / bps;
   const int j = id - s * bps;
   const int seg_start = s * seg;
   int seg_len = n - seg_start;

@@ -53,6 +53,24 @@ __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
   }
 }
 
+// Mean over all N tokens of each (b, h) from its block means: sum over blocks
+// of len_j * mean_j (block order, float32) divided by N.  One workgroup per
+// (b, h), one thread per d-element.
+__global__ __launch_bounds__(kMeanThreads) void total_mean_kernel(
+    const float* __restrict__ means, int N, int block, int seg, int bps, int nb, int d,
+    float* __restrict__ out) {
+  const int bh = blockIdx.x;
+  for (int j = threadIdx.x; j < d; j += kMeanThreads) {
+    float s = 0.f;
+    for (int blk = 0; blk < nb; ++blk) {
+      int start, len;
+      block_span(blk, N, block, seg, bps, start, len);
+      s = fmaf((float)len, means[((int64_t)bh * nb + blk) * d + j], s);
+    }
+    out[(int64_t)bh * d + j] = N > 0 ? s / (float)N : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Coarse scores + top-K.  One workgroup per (b*H + h, query block): every
 // thread scores candidates with a float32 dot product over d (sequential
@@ -237,11 +255,15 @@ int next_pow2(int x) {
 }  // namespace
 
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d, const int64_t* xs,
-                             int block, int seg, int bps, int nb, float* out,
+                             int block, int seg, int bps, int nb, float* out, float* out_total,
                              hipStream_t stream) {
-  if (B * H == 0 || nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_mean_kernel, dim3(nb, B * H), dim3(kMeanThreads), 0, stream, x, N,
-                     H, d, xs[0], xs[1], xs[2], block, seg, bps, nb, out);
+  if (B * H == 0) return hipSuccess;
+  if (nb > 0)
+    hipLaunchKernelGGL(block_mean_kernel, dim3(nb, B * H), dim3(kMeanThreads), 0, stream, x, N,
+                       H, d, xs[0], xs[1], xs[2], block, seg, bps, nb, out);
+  if (out_total)
+    hipLaunchKernelGGL(total_mean_kernel, dim3(B * H), dim3(kMeanThreads), 0, stream, out, N,
+                       block, seg, bps, nb, d, out_total);
   return hipGetLastError();
 }
 

@@ -46,12 +46,12 @@ def test_num_blocks(L):
 def fwd(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=12, Nq=4680, Nkv=32760, d=128, qs=S, kvs=S, os=S,
              indptr=None, indices=None, nnz=0, kb=64, ks=1560, qb=64, qseg=1560, scale=0.088,
-             o=FAKE, odt=0, lse=FAKE, stream=None)
+             oi=None, ois=None, li=None, o=FAKE, odt=0, lse=FAKE, stream=None)
     a.update(kw)
     return L.ca_chunk_attn_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["Nq"], a["Nkv"], a["d"],
                                a["qs"], a["kvs"], a["os"], a["indptr"], a["indices"], a["nnz"],
-                               a["kb"], a["ks"], a["qb"], a["qseg"], a["scale"], a["o"], a["odt"],
-                               a["lse"], a["stream"])
+                               a["kb"], a["ks"], a["qb"], a["qseg"], a["scale"], a["oi"], a["ois"],
+                               a["li"], a["o"], a["odt"], a["lse"], a["stream"])
 
 
 def test_attention_argument_errors(L):
@@ -65,6 +65,10 @@ def test_attention_argument_errors(L):
     assert fwd(L, indptr=FAKE, indices=FAKE, kb=65) == CA_ERANGE
     assert fwd(L, indptr=FAKE, indices=FAKE, nnz=-1) == CA_EINVAL
     assert fwd(L, scale=float("nan")) == CA_EINVAL
+    assert fwd(L, scale=-0.1) == CA_EINVAL
+    assert fwd(L, oi=FAKE, ois=S) == CA_EINVAL                 # lse_init missing
+    assert fwd(L, oi=FAKE, ois=S, li=FAKE, o=FAKE, odt=0) == CA_EINVAL   # aliases o_init as bf16
+    assert fwd(L, kvs=strides3((0, 64, 8))) == CA_ERANGE        # row stride below d
     fwd(L, d=96)
     assert b"head dim 96" in L.ca_last_error()
 
@@ -116,8 +120,8 @@ def test_merge_mean_topk_index_checks(L):
     assert m(o1=None) == CA_EINVAL
     assert m(o=FAKE + 4096) == CA_EINVAL                      # aliases o2
     assert m(o=FAKE, odt=0) == CA_EINVAL                      # aliases o1 with another dtype
-    assert L.ca_block_mean(FAKE, 1, 100, 2, 12, s, 64, 100, FAKE, None) == CA_EUNSUPPORTED
-    assert L.ca_block_mean(FAKE, 1, 100, 2, 64, s, 0, 100, FAKE, None) == CA_EINVAL
+    assert L.ca_block_mean(FAKE, 1, 100, 2, 12, s, 64, 100, FAKE, None, None) == CA_EUNSUPPORTED
+    assert L.ca_block_mean(FAKE, 1, 100, 2, 64, s, 0, 100, FAKE, None, None) == CA_EINVAL
     t = lambda **kw: L.ca_block_score_topk(FAKE, FAKE, 1, 2, 75, 525, 128, kw.get("cb", 450),
                                            kw.get("cc", 75), kw.get("K", 10), FAKE, None, None)
     assert t(K=0) == CA_ERANGE

@@ -358,6 +358,20 @@ def test_wan_local_history_merge_full_size(wan, wan_dev):
     assert_lse(lm[:, :, WAN_ROWS], Lr, "wan merge")
 
 
+def _union_csr(info, H, nqb):
+    """Per (h, qb) row: the head's shared list followed by the row's local list."""
+    sp, sx = info["shared_indptr"].cpu().numpy(), info["shared_indices"].cpu().numpy()
+    lp, lx = info["local_indptr"].cpu().numpy(), info["local_indices"].cpu().numpy()
+    rows = []
+    for h in range(H):
+        for qb in range(nqb):
+            r = h * nqb + qb
+            rows.append(np.concatenate([sx[sp[h]:sp[h + 1]], lx[lp[r]:lp[r + 1]]]))
+    ip = np.zeros(len(rows) + 1, np.int32)
+    ip[1:] = np.cumsum([len(x) for x in rows])
+    return ip, np.concatenate(rows).astype(np.int32)
+
+
 @pytest.mark.parametrize("ratio", [0.25, 0.125, 0.0625])
 def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
     say(f"wan block-sparse ratio={ratio}")
@@ -372,19 +386,64 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
     sel = orc.sparse_selection(wan.q.f32, wan.k.f32, 64, 1560, 64, 1560, lay)
     np.testing.assert_allclose(info["q_mean"].cpu().numpy(), sel["q_mean"], rtol=0, atol=5e-6)
     np.testing.assert_allclose(info["k_mean"].cpu().numpy(), sel["k_mean"], rtol=0, atol=5e-6)
+    np.testing.assert_allclose(info["chunk_mean"].cpu().numpy(), sel["chunk_mean"], rtol=0, atol=5e-6)
     ties = compare_topk(info["persistent"], sel["persistent"]) + compare_topk(info["local"], sel["local"])
     say(f"top-K rows differing at near-ties: {ties}")
-    ip = info["indptr"].cpu().numpy()
-    ix = info["indices"].cpu().numpy()[:ip[-1]]
+    ip, ix = _union_csr(info, wan.H, 75)
     if ties == 0:
-        np.testing.assert_array_equal(ip, sel["indptr"])
-        np.testing.assert_array_equal(ix, sel["indices"])
+        # the shared + local lists together are exactly the PBSA block list
+        for r in range(len(ip) - 1):
+            np.testing.assert_array_equal(np.sort(ix[ip[r]:ip[r + 1]]),
+                                          sel["indices"][sel["indptr"][r]:sel["indptr"][r + 1]])
     # attention over the selected lists (as built on the GPU, checked above)
     rows = np.r_[0:64, 1536:1560, 4616:4680]
     Or, Lr = orc.chunk_attn_blocks(wan.q.f32, wan.k.f32, wan.v.f32, ip, ix, 64, 1560, 64, 1560,
                                    wan.scale, rows=rows)
     assert_o(o[:, rows], Or, True, "wan sparse")
     assert_lse(l[:, :, rows], Lr, "wan sparse")
+
+
+@pytest.mark.parametrize("q_block,alias", [(64, False), (256, False), (256, True)])
+def test_resume_from_branch_equals_union(q_block, alias):
+    say(f"resume q_block={q_block} alias={alias}")
+    w = wl.tiny_dense(seed=4)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    nqb = w.Nq // q_block
+    rows = w.B * w.H * nqb
+    loc, hist = w.meta["local_blocks"], w.meta["history_blocks"]
+    ip1 = np.arange(w.B * w.H + 1, dtype=np.int32) * len(hist)
+    o1, l1 = ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(ip1), kv_indices=i32(np.tile(hist, w.B * w.H)),
+                               kv_block=64, kv_seg=w.Nkv, q_block=w.Nq, q_seg=w.Nq,
+                               out_dtype=torch.float32)
+    ip2 = np.arange(rows + 1, dtype=np.int32) * len(loc)
+    kw = dict(out=o1, lse=l1) if alias else dict(out_dtype=torch.bfloat16)
+    o, l = ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(ip2), kv_indices=i32(np.tile(loc, rows)),
+                             kv_block=64, kv_seg=w.Nkv, q_block=q_block, q_seg=w.Nq,
+                             o_init=o1, lse_init=l1, **kw)
+    torch.cuda.synchronize()
+    Od, Ld = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale)
+    assert_o(o, Od, not alias, "resumed vs dense")
+    assert_lse(l, Ld, "resumed vs dense")
+
+
+def test_resume_from_empty_branch_and_into_empty_set():
+    say("resume edge cases")
+    B, H, Nq, Nkv, d = 1, 2, 100, 130, 128
+    Q, K, V = _gen(60, B, Nq, H, d), _gen(61, B, Nkv, H, d), _gen(62, B, Nkv, H, d)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    zero_o = torch.zeros((B, Nq, H, d), dtype=torch.float32, device="cuda")
+    ninf = torch.full((B, H, Nq), float("-inf"), device="cuda")
+    o, l = ca.chunk_attn_fwd(q, k, v, o_init=zero_o, lse_init=ninf, out_dtype=torch.float32)
+    Od, Ld = orc.chunk_attn_dense(Q.f32, K.f32, V.f32, 1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert_o(o, Od, False, "resume from empty")
+    assert_lse(l, Ld, "resume from empty")
+    # an empty key set after a branch passes the branch through
+    ip = torch.zeros(B * H * 2 + 1, dtype=torch.int32, device="cuda")
+    o2, l2 = ca.chunk_attn_fwd(q, k, v, kv_indptr=ip, kv_indices=ip, q_block=64, q_seg=Nq,
+                               o_init=o, lse_init=l, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.allclose(o2, o, atol=1e-6, rtol=0) and torch.allclose(l2, l, atol=1e-6, rtol=0)
 
 
 def test_ragged_full_size():
