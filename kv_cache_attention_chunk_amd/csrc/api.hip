@@ -110,14 +110,15 @@ int launch_heads(int mode, const Common& c, AttnParams& p, const std::vector<int
                  hipStream_t stream) {
   const bool all = heads.empty();
   const int nh = all ? c.B * c.H : (int)heads.size();
-  int nwaves = kDenseWaves;
+  int nwaves;
   if (mode == MODE_BLOCKS) {
-    // one workgroup per query block (or 128-row slice of one)
+    // one workgroup per query block (or row slice of one)
     int maxq = std::min(std::min(p.q_block, p.q_seg), std::max(c.Nq, 1));
     nwaves = maxq <= 64 ? 2 : 4;
     p.q_sub = (maxq + nwaves * 32 - 1) / (nwaves * 32);
   } else {
-    p.n_qtiles = (c.Nq + kDenseWaves * 32 - 1) / (kDenseWaves * 32);
+    nwaves = kDenseWaves;
+    p.n_qtiles = (c.Nq + nwaves * 32 - 1) / (nwaves * 32);
   }
   for (int h0 = 0; h0 < nh; h0 += kMaxHeadsPerLaunch) {
     const int n = std::min(kMaxHeadsPerLaunch, nh - h0);

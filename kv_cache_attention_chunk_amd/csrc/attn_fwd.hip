@@ -5,8 +5,8 @@
 //   * K and V tiles go straight from global memory to LDS with buffer loads
 //     (buffer_load_dwordx4 ... lds, 1 KB per wave instruction): no staging
 //     registers, and the buffer range check returns zeros for rows past a
-//     partial tile.  K is triple- and V double-buffered; the loads for K(t+2)
-//     and V(t+1) are in flight during the whole of iteration t.
+//     partial tile.  K is triple- and V double-buffered: K(t+3) is loaded two
+//     iterations ahead of its use and V(t+1) one.
 //   * LDS rows are unpadded and XOR-swizzled by 16-byte chunk so that every
 //     read pattern below is free of bank conflicts: K chunk c of row r sits at
 //     c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64); V chunk c at
@@ -40,7 +40,9 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
-template <int D>
+// LDS ring of K and V tile stages: K x3 and V x2 (80 KB at d = 128, so two
+// 4-wave workgroups share a CU).
+template <int D, int NW>
 struct Layout {
   static constexpr int ROWB = 2 * D;                    // bytes per K / V row
   static constexpr int TILEB = kTileKeys * ROWB;        // bytes per K or V tile
@@ -73,6 +75,35 @@ __device__ __forceinline__ float half_sum(float x) {
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+
+// Destination of a buffer->LDS load as a bare wave-uniform LDS address.  The
+// kernel orders these loads against its LDS reads itself (s_waitcnt vmcnt +
+// barrier at the end of each iteration).  A destination the compiler cannot
+// tie to an LDS object keeps it from also placing a vmcnt(0) wait, i.e. a
+// wait for every load in flight, in front of the transposing LDS reads.
+__device__ __forceinline__ lds_void_t* dma_dst(char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_char_t*)p;
+  return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(a);
+}
+
+// Workgroup barrier for the load pipeline.  The caller has already waited
+// (s_waitcnt) for its own buffer->LDS loads and LDS reads; the empty asm
+// statements keep the compiler from moving memory accesses across the
+// barrier.  (__syncthreads' release fence would add a vmcnt(0) wait here,
+// draining the loads meant to stay in flight.)
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Read-only kernel input read through the scalar cache (s_load): the block
+// lists do not change while a launch runs.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int i) {
+  return ((const_i32_t*)p)[i];
+}
 
 // Transposing LDS read of 4 bf16 (see the header comment for the lane layout).
 __device__ __forceinline__ s16x4_t ld_tr4(const char* p) {
@@ -85,7 +116,7 @@ __device__ __forceinline__ s16x4_t ld_tr4(const char* p) {
 // pc ^ swizzle(r) of row r.
 template <int D, int NW>
 struct TileLoader {
-  using L = Layout<D>;
+  using L = Layout<D, NW>;
   static constexpr int NI = L::TILEB / (1024 * NW);
   uint32_t koff[NI], voff[NI];
   int wave;
@@ -111,7 +142,7 @@ struct TileLoader {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, nrec, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (NI * wave + j) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dma_dst(lk + (NI * wave + j) * 1024), 16,
                                                (int)koff[j], 0, 0, 0);
   }
 
@@ -122,23 +153,24 @@ struct TileLoader {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, nrec, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (NI * wave + j) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dma_dst(lv + (NI * wave + j) * 1024), 16,
                                                (int)voff[j], 0, 0, 0);
   }
 };
 
 // Two waves per SIMD: caps VGPR + AGPR at 256 per lane so that two 4-wave
-// workgroups share a CU and one wave's softmax overlaps the other's MFMAs.
+// workgroups share a CU.
 template <int D, int NW, int MODE, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const AttnParams p) {
-  using L = Layout<D>;
+  using L = Layout<D, NW>;
   constexpr int BM = NW * 32;
   constexpr int NST = D / 16;     // MFMA k-steps over d for S
   constexpr int NDT = D / 32;     // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(1024))) char smem[L::LDSB];
-  char* const kst = smem;                                  // K stages
-  char* const vst = smem + L::KSTAGES * L::TILEB;          // V stages
+  // K and V stages as two LDS objects, so that the reads of each carry the
+  // object they come from.
+  __shared__ __attribute__((aligned(1024))) char kst[L::KSTAGES * L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vst[L::VSTAGES * L::TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -204,10 +236,14 @@ void attn_fwd_kernel(const AttnParams p) {
     vh = p.v + b * p.ks_b + h * p.ks_h;
   }
 
-  // tile t -> (element offset of its row 0, number of valid rows)
+  // tile t -> (element offset of its row 0, number of valid rows).  Called
+  // for t = 0, 1, 2, ... in order; in block mode each call also fetches the
+  // next tile's block id, so that its latency overlaps one iteration.
+  int id_next = (MODE == MODE_BLOCKS && ntiles > 0) ? ld_uniform(p.indices, list0) : 0;
   auto tile_src = [&](int t, int64_t& off, int& len) {
     if (MODE == MODE_BLOCKS) {
-      const int id = p.indices[list0 + t];
+      const int id = id_next;
+      if (t + 1 < ntiles) id_next = ld_uniform(p.indices, list0 + t + 1);
       int s0 = 0, l0 = 0;
       if (id >= 0 && id < p.nkb)
         block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0, p.kv_bps_magic);
@@ -225,7 +261,7 @@ void attn_fwd_kernel(const AttnParams p) {
   TileLoader<D, NW> ldr;
   ldr.init(lane, wave, stride_bytes);
 
-  // ---- Q^T operand in registers ---------------------------------------------
+  // ---- Q^T operands in registers (query row row0 + 32 wave + col) ----------
   const int qr = wave * 32 + col;
   const bool qvalid = qr < nrows;
   const int qrow = row0 + qr;
@@ -255,14 +291,14 @@ void attn_fwd_kernel(const AttnParams p) {
   f32x16_t acc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = f32x16_t{};
-  float m = -INFINITY;   // running max, log2 domain
-  float l = 0.f;         // this lane's partial row sum
+  float m = -INFINITY;   // running max of this lane's query row (log2 domain)
+  float l = 0.f;         // this lane's partial row sum (lane halves added at the end)
   if (p.o_init && qvalid) {
     // Resume from a previous branch (O1, LSE1): the state (m, l, acc) =
     // (LSE1 * log2 e, 1, O1) has acc / l = O1 and m + log2 l = LSE1 / ln 2,
     // i.e. it is that branch's softmax state up to a common scale.
     m = p.lse_init[(int64_t)bh * p.Nq + qrow] * 1.4426950408889634f;
-    l = hg == 0 ? 1.f : 0.f;            // the two lane halves' sums are added
+    l = hg == 0 ? 1.f : 0.f;
     const float* oi = p.o_init + b * p.is_b + (int64_t)qrow * p.is_n + h * p.is_h;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -274,7 +310,7 @@ void attn_fwd_kernel(const AttnParams p) {
       }
   }
 
-  // S^T = K Q^T for the two 32-key halves of the tile in K stage ks
+  // S^T = K Q^T for the two 32-key halves of the tile in K stage ks.
   auto qk = [&](int ks, f32x16_t (&sc)[2]) {
     const int kb = ks * L::TILEB + kbx;
 #pragma unroll
@@ -289,9 +325,10 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   };
 
-  // online softmax of one tile's scores, then O^T += V^T P^T from V stage vs
-  auto softmax_pv = [&](f32x16_t (&sc)[2], int len_cur, int vs) {
-    // key of sc[kt][i] = 32kt + 8(i/4) + 4hg + i%4
+  // Row max of one tile's scores (masking keys past len_cur) and the
+  // accumulator rescale when a row's max grew.  Key of sc[kt][i] =
+  // 32kt + 8(i/4) + 4hg + i%4.
+  auto prep = [&](f32x16_t (&sc)[2], int len_cur) {
     if (len_cur < kTileKeys) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -307,10 +344,10 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
     mx = half_max(mx) * p.scale_log2;
-    // The exponent base m is the exact running row max, so the largest weight
-    // of a row is exactly 1 and survives the bf16 rounding of P unchanged.
-    // The O accumulator is rescaled only when some row of the wave found a
-    // new max in this tile (a minority of tiles once a few have been seen).
+    // The exponent base m is the exact running row max, so the largest
+    // weight of a row is exactly 1 and survives the bf16 rounding of P
+    // unchanged.  The O accumulator is rescaled only when some row of the
+    // wave found a new max in this tile.
     const bool grow = mx > m;
     if (__any(grow)) {
       const float m_new = grow ? mx : m;
@@ -320,74 +357,146 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
     }
+  };
+
+  // The fused body of one iteration, straight-line and explicitly ordered:
+  // P of tile t (exp2, row sum, bf16 pack) for the four 8-key groups, the QK
+  // MFMAs of tile t+1 (K stage ksn -> nx) and the PV MFMAs of tile t (V stage
+  // vs) are interleaved segment by segment, so the softmax VALU work issues
+  // while the matrix cores run.  Each segment's MFMA operands are read from
+  // LDS one segment ahead.  Group g's PV MFMAs run in group g+1's segments.
+  auto fused = [&](f32x16_t (&sc)[2], int vs, int ksn, f32x16_t (&nx)[2]) {
+    constexpr int QPG = NST / 2;                      // K fragments per group
+    constexpr int SEG = QPG > NDT ? QPG : NDT;        // segments per group
+    constexpr int NSEG = 4 * SEG + NDT;               // + tail: PV of group 3
+    constexpr int EPS = 8 / SEG;                      // exp2 per segment
     const float m_use = m == -INFINITY ? 0.f : m;
     const int vb = vs * L::TILEB + vbx;
+    const int kb = ksn * L::TILEB + kbx;
+    auto kfrag = [&](int g, int i) {
+      const int st = (g & 1) * QPG + i;
+      return *reinterpret_cast<const bf16x8_t*>(kst + (kb ^ (32 * st)) + (g >> 1) * 32 * L::ROWB);
+    };
+    auto vfrag = [&](int g, int dt) {
+      const char* vp = vst + (vb ^ (64 * dt)) + (32 * (g >> 1) + 16 * (g & 1)) * L::ROWB;
+      const s16x4_t lo = ld_tr4(vp);
+      const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // segment s: K fragment (g, i) if g < 4 and i < QPG; V fragment of group
+    // g - 1, d tile i, if 1 <= g and i < NDT (the tail segments have g = 4)
+    auto has_qk = [](int s_) { return s_ < 4 * SEG && (s_ % SEG) < QPG; };
+    auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
+    nx[0] = f32x16_t{};
+    nx[1] = f32x16_t{};
+    bf16x8_t ka = has_qk(0) ? kfrag(0, 0) : bf16x8_t{};
+    bf16x8_t va = {};
+    bf16x8_t pb = {};
+    f32x8_t pf;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int s_ = 0; s_ < NSEG; ++s_) {
+      const int g = s_ / SEG, i = s_ % SEG;
+      // operands of the next segment
+      bf16x8_t ka_n = {}, va_n = {};
+      if (s_ + 1 < NSEG) {
+        const int g1 = (s_ + 1) / SEG, i1 = (s_ + 1) % SEG;
+        if (has_qk(s_ + 1)) ka_n = kfrag(g1, i1);
+        if (has_pv(s_ + 1)) va_n = vfrag(g1 - 1, i1);
+      }
+      // softmax VALU work of group g
+      if (g < 4) {
+        const int kt = g >> 1, u = g & 1;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x8_t pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = i * EPS; e < (i + 1) * EPS; ++e) {
           pf[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * u + e], p.scale_log2, -m_use));
-          l += pf[e];    // float32 weights: the LSE must not carry bf16 rounding
-        }
-        const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
-        // A = V^T rows d = 32dt + (lane & 31), keys 32kt + 16u + {4hg..4hg+3,
-        // 8+4hg..8+4hg+3}: two transposing reads of 4 keys each.
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const char* vp = vst + (vb ^ (64 * dt)) + (32 * kt + 16 * u) * L::ROWB;
-          const s16x4_t lo = ld_tr4(vp);
-          const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
+          l += pf[e];   // float32 weights: the LSE must not carry bf16 rounding
         }
       }
+      if (has_pv(s_)) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[i], 0, 0, 0);
+      if (has_qk(s_))
+        nx[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[(g & 1) * QPG + i],
+                                                            nx[g >> 1], 0, 0, 0);
+      if (g < 4 && i == SEG - 1) pb = __builtin_convertvector(pf, bf16x8_t);
+      ka = ka_n;
+      va = va_n;
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  auto sync_loads = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Load pipeline.  K(t) is last read by the QK MFMAs of iteration t-1, so
+  // K(t + KSTAGES) goes out at the start of iteration t; V(t) is read in
+  // iteration t, so V(t + VSTAGES - 1) goes out at the start of iteration t.
+  // Each iteration issues its V load before its K load.  The end-of-iteration
+  // wait needs V(t+1) and K(t+2) and leaves every load issued after V(t+1)
+  // in flight: vmcnt counts this wave's loads in issue order.
+  constexpr int NIK = TileLoader<D, NW>::NI;     // load instructions per wave per tile
+  constexpr int KA = L::KSTAGES, VA = L::VSTAGES - 1;   // K / V load lead in tiles
+  static_assert(VA <= 2 && KA <= VA + 2, "wait counts below assume these leads");
+  auto wait_vm = [&](int groups_after) {
+    // s_waitcnt vmcnt(n): vmcnt[3:0] | expcnt 7 << 4 | lgkmcnt 0 << 8 | vmcnt[5:4] << 14
+#define CA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+    switch (groups_after) {
+      case 0: CA_WAIT_VM(0); break;
+      case 1: CA_WAIT_VM(NIK); break;
+      case 2: CA_WAIT_VM(2 * NIK); break;
+      default: CA_WAIT_VM(3 * NIK); break;
+    }
+#undef CA_WAIT_VM
+    block_sync();
   };
 
-  // Tile descriptors are computed once, when a tile's K load is issued, and
-  // carried for its V load (one iteration later) and its softmax mask (two
-  // iterations later).
-  int64_t off0 = 0, off1 = 0, off2 = 0;
-  int len0 = 0, len1 = 0, len2 = 0;
+  // Tile descriptor ring: (doff[j], dlen[j]) describe tile t + j, j = 0..KA;
+  // each is computed once, when the tile's K load is issued.
+  int64_t doff[KA + 1];
+  int dlen[KA + 1];
+#pragma unroll
+  for (int j = 0; j <= KA; ++j) {
+    doff[j] = 0;
+    dlen[j] = 0;
+  }
 
-  // one pipeline step for tile t: K(t+2) and V(t+1) loads, QK(t+1) -> nx,
-  // softmax + PV of tile t from cur.  On entry (off0,len0) describe tile t,
-  // (off1,len1) tile t+1; on exit they are shifted by one tile.
   auto step = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
-    if (t + 2 < ntiles) {
-      tile_src(t + 2, off2, len2);
-      ldr.issue_k(kh + off2, len2, stride_bytes, kst + ((t + 2) % L::KSTAGES) * L::TILEB);
+    if (t + VA < ntiles)
+      ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((t + VA) % L::VSTAGES) * L::TILEB);
+    if (t + KA < ntiles) {
+      tile_src(t + KA, doff[KA], dlen[KA]);
+      ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((t + KA) % L::KSTAGES) * L::TILEB);
     }
-    if (t + 1 < ntiles) {
-      ldr.issue_v(vh + off1, len1, stride_bytes, vst + ((t + 1) % L::VSTAGES) * L::TILEB);
-      qk((t + 1) % L::KSTAGES, nx);
+    prep(cur, dlen[0]);
+    fused(cur, t % L::VSTAGES, (t + 1) % L::KSTAGES, nx);
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+      doff[j] = doff[j + 1];
+      dlen[j] = dlen[j + 1];
     }
-    softmax_pv(cur, len0, t % L::VSTAGES);
-    off0 = off1; len0 = len1;
-    off1 = off2; len1 = len2;
-    sync_loads();
+    // Tile groups issued after V(t+1), which may stay in flight.  V(t+1) went
+    // out in iteration t + 1 - VA (or, for t + 1 < VA, in the prologue, which
+    // ended with a full wait).
+    int after = 0;
+    for (int it = t + 1 - VA; it <= t; ++it) {
+      if (it < 0) continue;
+      if (it != t + 1 - VA && it + VA < ntiles) ++after;   // V(it + VA)
+      if (it + KA < ntiles) ++after;                        // K(it + KA)
+    }
+    wait_vm(after);
   };
 
   f32x16_t sa[2], sb[2];
   if (ntiles > 0) {
-    tile_src(0, off0, len0);
-    ldr.issue_k(kh + off0, len0, stride_bytes, kst);
-    ldr.issue_v(vh + off0, len0, stride_bytes, vst);
-    if (ntiles > 1) {
-      tile_src(1, off1, len1);
-      ldr.issue_k(kh + off1, len1, stride_bytes, kst + L::TILEB);
-    }
-    sync_loads();
+#pragma unroll
+    for (int j = 0; j < KA; ++j)
+      if (j < ntiles) {
+        tile_src(j, doff[j], dlen[j]);
+        ldr.issue_k(kh + doff[j], dlen[j], stride_bytes, kst + j * L::TILEB);
+      }
+#pragma unroll
+    for (int j = 0; j < VA; ++j)
+      if (j < ntiles) ldr.issue_v(vh + doff[j], dlen[j], stride_bytes, vst + j * L::TILEB);
+    wait_vm(0);
     qk(0, sa);
+    // iteration 0 refills K stage 0, which every wave has just read
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    block_sync();
     for (int t = 0; t < ntiles; t += 2) {
       step(t, sa, sb);
       if (t + 1 < ntiles) step(t + 1, sb, sa);
@@ -416,10 +525,8 @@ void attn_fwd_kernel(const AttnParams p) {
         }
       }
     }
-    if (hg == 0) {
-      p.lse[(int64_t)bh * p.Nq + qrow] =
-          lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-    }
+    if (hg == 0)
+      p.lse[(int64_t)bh * p.Nq + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -442,16 +549,19 @@ hipError_t launch_mode(int mode, bool of32, const AttnParams& p, hipStream_t str
   }
 }
 
+template <int D>
+hipError_t launch_d(int mode, int nwaves, bool of32, const AttnParams& p, hipStream_t stream) {
+  return nwaves == 2 ? launch_mode<D, 2>(mode, of32, p, stream)
+                     : launch_mode<D, 4>(mode, of32, p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32, const AttnParams& p,
                             hipStream_t stream) {
   if (p.n_items <= 0) return hipSuccess;
-  if (d == 64)
-    return nwaves == 2 ? launch_mode<64, 2>(mode, out_f32, p, stream)
-                       : launch_mode<64, 4>(mode, out_f32, p, stream);
-  return nwaves == 2 ? launch_mode<128, 2>(mode, out_f32, p, stream)
-                     : launch_mode<128, 4>(mode, out_f32, p, stream);
+  return d == 64 ? launch_d<64>(mode, nwaves, out_f32, p, stream)
+                 : launch_d<128>(mode, nwaves, out_f32, p, stream);
 }
 
 }  // namespace chunkattn
