@@ -300,17 +300,40 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
     + persistent, one list per head, float32 branch output), continued per
     query block over its top-K local blocks by resuming from that branch's
     (O, LSE) state.  The sink, history and local id ranges must be disjoint.
-    `k_mean` may carry precomputed key-block means (resident cache state).
-    Returns (O, LSE, info) with the selected ids and block lists in `info`."""
+
+    `k_mean` carries key-block means of the cache kept from earlier steps
+    (resident state, [B, H, NB, d] float32); only the history entries are read
+    from it.  The local window holds the current chunk, so its block means are
+    recomputed here from k (over just that window when it starts on a segment
+    boundary).  Without `k_mean` the means of every cache block are computed.
+    Returns (O, LSE, info) with the selected ids and block lists in `info`;
+    info["local"] holds local-window ids relative to info["local_base"]."""
     B, Nq, H, d = q.shape
+    Nkv = k.shape[1]
     seg = seg or Nq
+    kv_seg = seg
     ranges = sorted([(sink_begin, sink_count), (hist_begin, hist_count), (local_begin, local_count)])
     if any(a[0] + a[1] > b[0] for a, b in zip(ranges, ranges[1:])):
         raise ValueError("sink, history and local block ranges must be disjoint")
     qm, cm = block_mean(q, block, seg, with_total=True)
-    km = block_mean(k, block, seg) if k_mean is None else k_mean
+    bps = -(-kv_seg // block)
+    km_loc, loc_base = None, local_begin
+    if k_mean is None:
+        km = block_mean(k, block, kv_seg)
+        km_loc = km
+    else:
+        km = k_mean
+        if K and local_begin % bps == 0:
+            last = local_begin + local_count - 1
+            t0 = (local_begin // bps) * kv_seg
+            t1 = min(Nkv, (last // bps) * kv_seg + min(kv_seg, (last % bps + 1) * block))
+            km_loc = block_mean(k[:, t0:t1], block, kv_seg)
+            loc_base = 0
+        elif K:
+            km_loc = block_mean(k, block, kv_seg)
     pers = block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count) if C else None
-    loc = block_score_topk(qm, km, K, cand_begin=local_begin, cand_count=local_count) if K else None
+    loc = (block_score_topk(qm, km_loc, K, cand_begin=loc_base, cand_count=local_count)
+           if K else None)
     nqb = qm.shape[2]
     sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
                                     None if pers is None else pers[:, :, 0, :].contiguous(),
@@ -318,10 +341,12 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
     o1, l1 = chunk_attn_fwd(q, k, v, kv_indptr=sh_ptr, kv_indices=sh_idx, kv_block=block,
                             kv_seg=seg, q_block=Nq, q_seg=Nq, scale=scale,
                             out_dtype=torch.float32)
-    lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, loc, 0, device=q.device)
+    lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, loc, local_begin - loc_base,
+                                    device=q.device)
     o, l = chunk_attn_fwd(q, k, v, kv_indptr=lo_ptr, kv_indices=lo_idx, kv_block=block,
                           kv_seg=seg, q_block=block, q_seg=seg, scale=scale,
                           out_dtype=out_dtype, o_init=o1, lse_init=l1)
-    return o, l, {"q_mean": qm, "k_mean": km, "chunk_mean": cm, "persistent": pers,
-                  "local": loc, "shared_indptr": sh_ptr, "shared_indices": sh_idx,
+    return o, l, {"q_mean": qm, "k_mean": km, "k_mean_local": km_loc, "chunk_mean": cm,
+                  "persistent": pers, "local": loc, "local_base": local_begin - loc_base,
+                  "shared_indptr": sh_ptr, "shared_indices": sh_idx,
                   "local_indptr": lo_ptr, "local_indices": lo_idx}

@@ -54,129 +54,198 @@ __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
 }
 
 // Mean over all N tokens of each (b, h) from its block means: sum over blocks
-// of len_j * mean_j (block order, float32) divided by N.  One workgroup per
-// (b, h), one thread per d-element.
+// of len_j * mean_j divided by N.  One workgroup per (b, h).  With G =
+// 256 / d thread groups (at least 1), group g sums blocks g, g + G, ... in
+// float32 (independent loads, so many are in flight), then the G partial
+// sums of each column are added in group order.
 __global__ __launch_bounds__(kMeanThreads) void total_mean_kernel(
     const float* __restrict__ means, int N, int block, int seg, int bps, int nb, int d,
     float* __restrict__ out) {
+  __shared__ float red[512];
   const int bh = blockIdx.x;
-  for (int j = threadIdx.x; j < d; j += kMeanThreads) {
+  const int G = d <= kMeanThreads ? kMeanThreads / d : 1;
+  const float* m = means + (int64_t)bh * nb * d;
+  for (int slot = threadIdx.x; slot < G * d; slot += kMeanThreads) {
+    const int g = slot / d, j = slot - (slot / d) * d;
     float s = 0.f;
-    for (int blk = 0; blk < nb; ++blk) {
+#pragma unroll 8
+    for (int blk = g; blk < nb; blk += G) {
       int start, len;
       block_span(blk, N, block, seg, bps, start, len);
-      s = fmaf((float)len, means[((int64_t)bh * nb + blk) * d + j], s);
+      s = fmaf((float)len, m[(int64_t)blk * d + j], s);
     }
-    out[(int64_t)bh * d + j] = N > 0 ? s / (float)N : 0.f;
+    red[slot] = s;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += kMeanThreads) {
+    float t = 0.f;
+    for (int g = 0; g < G; ++g) t += red[g * d + j];
+    out[(int64_t)bh * d + j] = N > 0 ? t / (float)N : 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Coarse scores + top-K.  One workgroup per (b*H + h, query block): every
-// thread scores candidates with a float32 dot product over d (sequential
-// fused multiply-adds in index order), then a bitonic sort in LDS orders the
-// padded list by (score descending, block id ascending) and a second bitonic
-// sort puts the first K ids in ascending order.
+// Coarse scores + top-K.  One workgroup per (b*H + h, query block).
+//   * scores: float32 dot products.  For d/4 a power of two up to 64, d/4
+//     lanes share one candidate (a 16-byte slice each, then a butterfly sum)
+//     and the loads of a batch of candidates are all issued before any is
+//     used; otherwise each thread scores whole candidates sequentially.
+//     A NaN score ranks as -inf.
+//   * selection by rank: rank(i) = #{j : s_j > s_i} + #{j < i : s_j = s_i},
+//     the position in (score descending, block id ascending) order.  F
+//     threads share one candidate, each counting a slice of j four scores at
+//     a time; the second term is counted only when s_i has a tie.  The
+//     candidates with rank < K are written in index order, i.e. ascending
+//     block id.
+// Scores live in dynamic LDS, padded with -inf to a multiple of 4.
 // ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 256;
 constexpr int kTopkMaxCand = 4096;
+constexpr int kTopkBatch = 16;
 
-__device__ __forceinline__ bool before(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
+__host__ __device__ constexpr int topk_lds_bytes(int n, int threads) {
+  return 4 * (4 * ((n + 3) / 4)) + 4 * n + 4 * (threads / 64);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int NQB, int NKB, int d,
-    int cand_begin, int cand_count, int K, int npad, int kpad, int32_t* __restrict__ out_idx,
-    float* __restrict__ out_score) {
-  __shared__ float qs[512];
-  __shared__ float ss[kTopkMaxCand];
-  __shared__ int is[kTopkMaxCand];
+    int cand_begin, int n, int K, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  extern __shared__ __attribute__((aligned(16))) float topk_lds[];
+  const int n4 = (n + 3) >> 2;
+  float* ss = topk_lds;                                          // [4 n4] scores
+  int* rk = reinterpret_cast<int*>(ss + 4 * n4);                 // [n] ranks
+  int* wcount = rk + n;                                          // [THREADS / 64]
   const int qb = blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const float* q = qm + ((int64_t)bh * NQB + qb) * d;
-  for (int j = tid; j < d; j += kTopkThreads) qs[j] = q[j];
-  __syncthreads();
-  for (int j = tid; j < npad; j += kTopkThreads) {
-    if (j < cand_count) {
-      const float* kr = km + ((int64_t)bh * NKB + cand_begin + j) * d;
-      float acc = 0.f;
-      for (int c = 0; c < d; c += 4) {
-        const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + c);
-        acc = fmaf(qs[c], kv[0], acc);
-        acc = fmaf(qs[c + 1], kv[1], acc);
-        acc = fmaf(qs[c + 2], kv[2], acc);
-        acc = fmaf(qs[c + 3], kv[3], acc);
+  const float* kbase = km + ((int64_t)bh * NKB + cand_begin) * d;
+  auto key = [](float x) { return x != x ? -INFINITY : x; };
+  const int lpc = d / 4;                       // lanes per candidate
+  if ((lpc & (lpc - 1)) == 0 && lpc <= 64) {
+    const int sub = tid & (lpc - 1);
+    const int slot = tid / lpc;
+    const int per_pass = THREADS / lpc;
+    const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(q + 4 * sub);
+    for (int c0 = 0; c0 < 4 * n4; c0 += kTopkBatch * per_pass) {
+      f32x4_t kv[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int c = c0 + u * per_pass + slot;
+        kv[u] = c < n ? *reinterpret_cast<const f32x4_t*>(kbase + (int64_t)c * d + 4 * sub)
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float part[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u)
+        part[u] = fmaf(qv[3], kv[u][3], fmaf(qv[2], kv[u][2], fmaf(qv[1], kv[u][1], qv[0] * kv[u][0])));
+      // butterfly over the lpc lanes of each candidate, the batch's exchanges
+      // issued together
+      for (int o = lpc >> 1; o > 0; o >>= 1) {
+#pragma unroll
+        for (int u = 0; u < kTopkBatch; ++u) part[u] += __shfl_xor(part[u], o);
+      }
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int c = c0 + u * per_pass + slot;
+        if (sub == 0 && c < 4 * n4) ss[c] = c < n ? key(part[u]) : -INFINITY;
+      }
+    }
+  } else {
+    for (int j = tid; j < 4 * n4; j += THREADS) {
+      float acc = -INFINITY;
+      if (j < n) {
+        const float* kr = kbase + (int64_t)j * d;
+        acc = 0.f;
+        for (int c = 0; c < d; ++c) acc = fmaf(q[c], kr[c], acc);
+        acc = key(acc);
       }
       ss[j] = acc;
-      is[j] = cand_begin + j;
-    } else {
-      ss[j] = -INFINITY;
-      is[j] = 0x7FFFFFFF;
     }
   }
   __syncthreads();
-  // bitonic sort of npad entries: (score desc, id asc)
-  for (int size = 2; size <= npad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < npad; i += kTopkThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;   // this run ascends in "before" order
-          const float si = ss[i], sj = ss[j];
-          const int ii = is[i], ij = is[j];
-          const bool swap = up ? before(sj, ij, si, ii) : before(si, ii, sj, ij);
-          if (swap) {
-            ss[i] = sj; ss[j] = si;
-            is[i] = ij; is[j] = ii;
-          }
-        }
+
+  // ranks (padding entries sit above every index, compare as -inf and so
+  // never count)
+  int F = 1;
+  while (F < 64 && n * (2 * F) <= THREADS) F *= 2;
+  const int chunk4 = (n4 + F - 1) / F;
+  const f32x4_t* ss4 = reinterpret_cast<const f32x4_t*>(ss);
+  for (int base = 0; base < n; base += THREADS / F) {
+    const int i = base + tid / F;
+    const int part = tid & (F - 1);
+    int gt = 0, eq = 0;
+    float si = 0.f;
+    if (i < n) {
+      si = ss[i];
+      const int b0 = part * chunk4;
+      const int b1 = b0 + chunk4 < n4 ? b0 + chunk4 : n4;
+#pragma unroll 4
+      for (int b = b0; b < b1; ++b) {
+        const f32x4_t v = ss4[b];
+        gt += (int)(v[0] > si) + (int)(v[1] > si) + (int)(v[2] > si) + (int)(v[3] > si);
+        eq += (int)(v[0] == si) + (int)(v[1] == si) + (int)(v[2] == si) + (int)(v[3] == si);
       }
-      __syncthreads();
     }
-  }
-  // keep the first K, pad to kpad, sort by id ascending
-  for (int i = tid; i < kpad; i += kTopkThreads) {
-    if (i >= K) {
-      ss[i] = 0.f;
-      is[i] = 0x7FFFFFFF;
+    for (int o = F >> 1; o > 0; o >>= 1) {
+      gt += __shfl_xor(gt, o);
+      eq += __shfl_xor(eq, o);
+    }
+    if (i < n && part == 0) {
+      if (eq > 1)                              // s_i is tied: lower ids rank first
+        for (int j = 0; j < i; ++j) gt += ss[j] == si;
+      rk[i] = gt;
     }
   }
   __syncthreads();
-  for (int size = 2; size <= kpad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < kpad; i += kTopkThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const int ii = is[i], ij = is[j];
-          const bool swap = up ? (ij < ii) : (ii < ij);
-          if (swap) {
-            const float t = ss[i];
-            ss[i] = ss[j]; ss[j] = t;
-            is[i] = ij; is[j] = ii;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+
+  // the K candidates of rank < K, compacted in index order
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t o = ((int64_t)bh * NQB + qb) * K;
-  for (int i = tid; i < K; i += kTopkThreads) {
-    out_idx[o + i] = is[i];
-    if (out_score) out_score[o + i] = ss[i];
+  int carry = 0;
+  for (int c0 = 0; c0 < n; c0 += THREADS) {
+    const int i = c0 + tid;
+    const bool sel = i < n && rk[i] < K;
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int wpre = 0, tot = 0;
+    for (int w = 0; w < THREADS / 64; ++w) {
+      const int c = wcount[w];
+      wpre += w < wave ? c : 0;
+      tot += c;
+    }
+    if (sel) {
+      const int pos = carry + wpre + __popcll(m & ((1ull << lane) - 1));
+      if (pos < K) {
+        out_idx[o + pos] = cand_begin + i;
+        if (out_score) out_score[o + pos] = ss[i];
+      }
+    }
+    carry += tot;
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// PBSA block lists.  One workgroup of 1024 threads; each thread owns a
-// contiguous range of CSR rows.  Row = sorted merge, duplicates dropped, of
-// the sink id range, the head's persistent ids and the query block's top-K
-// ids (+ offset); all three inputs ascending.  Pass 1 counts, a workgroup
-// exclusive scan gives row offsets, pass 2 writes.
+// PBSA block lists.  One workgroup of 1024 threads.  Row r (head h = r / NQB)
+// = sorted union, duplicates dropped, of the sink range S = [s_lo, s_hi),
+// the head's persistent ids P_h and the row's top-K ids T_r (+ offset); P and
+// T are ascending.
+//
+// The inputs are staged in LDS when they fit.  With many rows, one thread
+// merges whole rows (count pass, workgroup scan, write pass).  With few rows
+// (each long), every output element is placed independently:
+// an id is kept if no earlier list (S, then P, then T) and no earlier index
+// of its own list holds it, and its position in the row is the number of
+// distinct ids below it,
+//   |S below v| + kept P ids below v + kept T ids below v,
+// the last two read from per-list prefix counts of kept flags at the list's
+// lower bound of v.  Inputs too large for LDS are merged row by row straight
+// from global memory.
 // ---------------------------------------------------------------------------
 constexpr int kIndexThreads = 1024;
+constexpr int kIndexLds = 32768;       // int32 words of LDS (128 KB)
 
 struct Merge3 {
   int s_lo, s_hi;            // sink range [s_lo, s_hi)
@@ -206,50 +275,168 @@ struct Merge3 {
   }
 };
 
-__global__ __launch_bounds__(kIndexThreads) void build_index_kernel(
-    int rows, int sink_begin, int sink_count, const int32_t* __restrict__ pers, int C, int NQB,
-    const int32_t* __restrict__ topk, int K, int toff, int32_t* __restrict__ indptr,
-    int32_t* __restrict__ indices) {
-  __shared__ int scan[kIndexThreads];
+// first index in a[0, n) whose value is >= v (a ascending)
+__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int v) {
+  int lo = 0;
+  while (n > 0) {
+    const int half = n >> 1;
+    if (a[lo + half] < v) {
+      lo += half + 1;
+      n -= half + 1;
+    } else {
+      n = half;
+    }
+  }
+  return lo;
+}
+
+// Workgroup exclusive scan of per-thread counts; returns this thread's offset
+// and writes the total to *total.
+__device__ int block_exclusive_scan(int cnt, int* scan, int* total) {
   const int tid = threadIdx.x;
-  const int per = (rows + kIndexThreads - 1) / kIndexThreads;
-  const int r0 = tid * per;
-  const int r1 = r0 + per < rows ? r0 + per : rows;
-  auto make = [&](int r) {
-    Merge3 m;
-    m.s_lo = sink_begin;
-    m.s_hi = sink_begin + sink_count;
-    const int bh = r / NQB;
-    m.pp = pers ? pers + (int64_t)bh * C : nullptr;
-    m.pc = pers ? C : 0;
-    m.tp = topk ? topk + (int64_t)r * K : nullptr;
-    m.tc = topk ? K : 0;
-    m.toff = toff;
-    return m;
-  };
-  int cnt = 0;
-  for (int r = r0; r < r1; ++r) cnt += make(r).template run<false>(nullptr);
   scan[tid] = cnt;
   __syncthreads();
-  // Hillis-Steele inclusive scan
-  for (int off = 1; off < kIndexThreads; off <<= 1) {
+  for (int off = 1; off < kIndexThreads; off <<= 1) {   // Hillis-Steele inclusive scan
     const int v = tid >= off ? scan[tid - off] : 0;
     __syncthreads();
     scan[tid] += v;
     __syncthreads();
   }
-  int pos = scan[tid] - cnt;
-  for (int r = r0; r < r1; ++r) {
-    indptr[r] = pos;
-    pos += make(r).template run<true>(indices + pos);
-  }
-  if (tid == kIndexThreads - 1) indptr[rows] = scan[tid];
+  *total = scan[kIndexThreads - 1];
+  const int r = scan[tid] - cnt;
+  __syncthreads();
+  return r;
 }
 
-int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+__global__ __launch_bounds__(kIndexThreads) void build_index_kernel(
+    int rows, int sink_begin, int sink_count, const int32_t* __restrict__ pers, int C, int NQB,
+    const int32_t* __restrict__ topk, int K, int toff, int32_t* __restrict__ indptr,
+    int32_t* __restrict__ indices) {
+  __shared__ int scan[kIndexThreads];
+  __shared__ int32_t lds[kIndexLds];
+  const int tid = threadIdx.x;
+  const int per = (rows + kIndexThreads - 1) / kIndexThreads;
+  const int r0 = tid * per;
+  const int r1 = r0 + per < rows ? r0 + per : rows;
+  const int BH = NQB > 0 ? rows / NQB : 0;
+  const int nc = pers ? C : 0;
+  const int nk = topk ? K : 0;
+  const int s_lo = sink_begin, s_hi = sink_begin + sink_count;
+
+  // one thread merges whole rows: count pass, workgroup scan, write pass
+  auto merge_rows = [&](const int32_t* P, const int32_t* T, int t_off) {
+    auto make = [&](int r) {
+      Merge3 m;
+      m.s_lo = s_lo;
+      m.s_hi = s_hi;
+      m.pp = nc ? P + (r / NQB) * nc : nullptr;
+      m.pc = nc;
+      m.tp = nk ? T + r * nk : nullptr;
+      m.tc = nk;
+      m.toff = t_off;
+      return m;
+    };
+    int cnt = 0, total;
+    for (int r = r0; r < r1; ++r) cnt += make(r).template run<false>(nullptr);
+    int pos = block_exclusive_scan(cnt, scan, &total);
+    for (int r = r0; r < r1; ++r) {
+      indptr[r] = pos;
+      pos += make(r).template run<true>(indices + pos);
+    }
+    if (tid == 0) indptr[rows] = total;
+  };
+
+  const int64_t need = (int64_t)BH * (2 * nc + 1) + (int64_t)rows * (2 * nk + 2);
+  if (need > kIndexLds) {
+    merge_rows(pers, topk, toff);
+    return;
+  }
+
+  // LDS layout: P [BH][nc], prefP [BH][nc + 1], T [rows][nk] (offset added),
+  // prefT [rows][nk + 1], row offsets [rows]
+  int32_t* P = lds;
+  int* prefP = P + BH * nc;
+  int32_t* T = prefP + BH * (nc + 1);
+  int* prefT = T + rows * nk;
+  int* rowoff = prefT + rows * (nk + 1);
+  for (int i = tid; i < BH * nc; i += kIndexThreads) P[i] = pers[i];
+  for (int i = tid; i < rows * nk; i += kIndexThreads) T[i] = topk[i] + toff;
+  __syncthreads();
+  if (rows >= kIndexThreads / 4) {
+    // many rows: a thread per row already fills the workgroup
+    merge_rows(P, T, 0);
+    return;
+  }
+
+  // few (long) rows: every output id is placed by its own thread
+  auto in_s = [&](int v) { return v >= s_lo && v < s_hi; };
+  for (int hh = tid; hh < BH; hh += kIndexThreads) {
+    const int32_t* p = P + hh * nc;
+    int* pp = prefP + hh * (nc + 1);
+    int c = 0;
+    pp[0] = 0;
+    for (int i = 0; i < nc; ++i) {
+      const int v = p[i];
+      c += !in_s(v) && (i == 0 || p[i - 1] != v);
+      pp[i + 1] = c;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kIndexThreads) {
+    const int32_t* t = T + r * nk;
+    const int32_t* p = P + (r / NQB) * nc;
+    int* pt = prefT + r * (nk + 1);
+    int c = 0;
+    pt[0] = 0;
+    for (int j = 0; j < nk; ++j) {
+      const int v = t[j];
+      const int lb = lower_bound(p, nc, v);
+      c += !in_s(v) && (j == 0 || t[j - 1] != v) && !(lb < nc && p[lb] == v);
+      pt[j + 1] = c;
+    }
+  }
+  __syncthreads();
+  auto row_count = [&](int r) {
+    return sink_count + prefP[(r / NQB) * (nc + 1) + nc] + prefT[r * (nk + 1) + nk];
+  };
+  int cnt = 0, total;
+  for (int r = r0; r < r1; ++r) cnt += row_count(r);
+  int pos = block_exclusive_scan(cnt, scan, &total);
+  for (int r = r0; r < r1; ++r) {
+    indptr[r] = pos;
+    rowoff[r] = pos;
+    pos += row_count(r);
+  }
+  if (tid == 0) indptr[rows] = total;
+  __syncthreads();
+  const int width = sink_count + nc + nk;          // rows * width < 2^31 (checked by the caller)
+  for (int e = tid; e < rows * width; e += kIndexThreads) {
+    const int r = e / width;
+    const int slot = e - r * width;
+    const int hh = r / NQB;
+    const int32_t* p = P + hh * nc;
+    const int* pp = prefP + hh * (nc + 1);
+    const int32_t* t = T + r * nk;
+    const int* pt = prefT + r * (nk + 1);
+    int v;
+    bool keep;
+    if (slot < sink_count) {
+      v = s_lo + slot;
+      keep = true;
+    } else if (slot < sink_count + nc) {
+      const int i = slot - sink_count;
+      v = p[i];
+      keep = pp[i + 1] > pp[i];
+    } else {
+      const int j = slot - sink_count - nc;
+      v = t[j];
+      keep = pt[j + 1] > pt[j];
+    }
+    if (!keep) continue;
+    const int below_s = v <= s_lo ? 0 : (v >= s_hi ? sink_count : v - s_lo);
+    const int at = below_s + pp[lower_bound(p, nc, v)] + pt[lower_bound(t, nk, v)];
+    if (at < row_count(r)) indices[rowoff[r] + at] = v;   // always, for ascending inputs
+  }
 }
 
 }  // namespace
@@ -271,11 +458,14 @@ hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int
                              int d, int cand_begin, int cand_count, int K, int32_t* out_idx,
                              float* out_score, hipStream_t stream) {
   if (B * H == 0 || NQB == 0) return hipSuccess;
-  const int npad = next_pow2(cand_count);
-  const int kpad = next_pow2(K);
-  hipLaunchKernelGGL(score_topk_kernel, dim3(NQB, B * H), dim3(kTopkThreads), 0, stream, qm,
-                     km, NQB, NKB, d, cand_begin, cand_count, K, npad, kpad, out_idx,
-                     out_score);
+  // small candidate sets: 256-thread workgroups, several resident per CU
+  const dim3 grid(NQB, B * H);
+  if (cand_count <= 256)
+    hipLaunchKernelGGL(score_topk_kernel<256>, grid, dim3(256), topk_lds_bytes(cand_count, 256),
+                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score);
+  else
+    hipLaunchKernelGGL(score_topk_kernel<1024>, grid, dim3(1024), topk_lds_bytes(cand_count, 1024),
+                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score);
   return hipGetLastError();
 }
 

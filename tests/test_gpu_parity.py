@@ -313,6 +313,66 @@ def test_build_kv_index_dedup_and_offset():
     np.testing.assert_array_equal(ix.cpu().numpy()[:len(ixr)], ixr)
 
 
+@pytest.mark.parametrize("d", [24, 64, 128, 512])
+def test_block_mean_with_chunk_mean(d):
+    """Block means and the mean over all tokens (the chunk-mean query), for
+    head dims below, at and above one thread per column of the reduction."""
+    say(f"block_mean + chunk mean d={d}")
+    X = _gen(51, 1, 1560 * 2 + 100, 3, d, 2.0)
+    m, tot = ca.block_mean(to_dev(X), 64, 1560, with_total=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(m.cpu().numpy(), orc.block_mean(X.f32, 64, 1560), rtol=0, atol=2e-6)
+    np.testing.assert_allclose(tot.cpu().numpy(), orc.chunk_mean_query(X.f32), rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("d", [4, 12, 64, 96, 256, 512])
+def test_topk_head_dims(d):
+    """Cooperative (d/4 a power of two up to 64) and per-thread scoring paths."""
+    say(f"topk d={d}")
+    rng = np.random.default_rng(d)
+    qm = rng.standard_normal((1, 3, 7, d)).astype(np.float32)
+    km = rng.standard_normal((1, 3, 300, d)).astype(np.float32)
+    qt, kt = torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda()
+    for K, cb, cc in [(10, 20, 75), (32, 0, 300), (1, 299, 1)]:
+        idx, sc = ca.block_score_topk(qt, kt, K, cand_begin=cb, cand_count=cc, return_scores=True)
+        torch.cuda.synchronize()
+        ref = orc.block_score_topk(qm, km, cb, cc, K)
+        compare_topk(idx, ref)
+        same = np.all(idx.cpu().numpy() == ref["idx"], axis=-1)
+        np.testing.assert_allclose(sc.cpu().numpy()[same], ref["score"][same], rtol=1e-5, atol=1e-5 * d)
+
+
+@pytest.mark.parametrize("NQB", [3, 200])
+def test_build_kv_index_overlapping_lists(NQB):
+    """Sink, persistent and top-K lists that overlap and repeat ids, on few
+    long rows (one thread per output id) and many rows (one thread per row)."""
+    say(f"build_kv_index overlaps NQB={NQB}")
+    rng = np.random.default_rng(NQB)
+    B, H, C, K = 1, 2, 12, 9
+    pers = np.sort(rng.choice(40, size=(B, H, C), replace=True), axis=-1).astype(np.int32)
+    topk = np.sort(rng.choice(30, size=(B, H, NQB, K), replace=True), axis=-1).astype(np.int32)
+    ip, ix = ca.build_kv_index(B, H, NQB, 4, 10, i32(pers), i32(topk), 7)
+    torch.cuda.synchronize()
+    ipr, ixr = orc.build_kv_index(B, H, NQB, 4, 10, pers, topk, 7)
+    np.testing.assert_array_equal(ip.cpu().numpy(), ipr)
+    np.testing.assert_array_equal(ix.cpu().numpy()[:len(ixr)], ixr)
+
+
+def test_build_kv_index_unstaged_large():
+    """More persistent + top-K ids than the LDS staging holds: the merges read
+    global memory directly."""
+    say("build_kv_index large")
+    rng = np.random.default_rng(7)
+    B, H, NQB, C, K = 1, 8, 300, 16, 8
+    pers = np.sort(rng.choice(200, size=(B, H, C), replace=True), axis=-1).astype(np.int32)
+    topk = np.sort(rng.choice(60, size=(B, H, NQB, K), replace=True), axis=-1).astype(np.int32)
+    ip, ix = ca.build_kv_index(B, H, NQB, 5, 20, i32(pers), i32(topk), 150)
+    torch.cuda.synchronize()
+    ipr, ixr = orc.build_kv_index(B, H, NQB, 5, 20, pers, topk, 150)
+    np.testing.assert_array_equal(ip.cpu().numpy(), ipr)
+    np.testing.assert_array_equal(ix.cpu().numpy()[:len(ixr)], ixr)
+
+
 # ---------------------------------------------------------------------------
 # workload-sized cases, exactly as the benchmark runs them, on sampled rows
 # ---------------------------------------------------------------------------
@@ -387,7 +447,8 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
     np.testing.assert_allclose(info["q_mean"].cpu().numpy(), sel["q_mean"], rtol=0, atol=5e-6)
     np.testing.assert_allclose(info["k_mean"].cpu().numpy(), sel["k_mean"], rtol=0, atol=5e-6)
     np.testing.assert_allclose(info["chunk_mean"].cpu().numpy(), sel["chunk_mean"], rtol=0, atol=5e-6)
-    ties = compare_topk(info["persistent"], sel["persistent"]) + compare_topk(info["local"], sel["local"])
+    ties = (compare_topk(info["persistent"], sel["persistent"])
+            + compare_topk(info["local"] + info["local_base"], sel["local"]))
     say(f"top-K rows differing at near-ties: {ties}")
     ip, ix = _union_csr(info, wan.H, 75)
     if ties == 0:
@@ -401,6 +462,26 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
                                    wan.scale, rows=rows)
     assert_o(o[:, rows], Or, True, "wan sparse")
     assert_lse(l[:, :, rows], Lr, "wan sparse")
+
+
+def test_wan_block_sparse_resident_key_means(wan, wan_dev):
+    """With the history key-block means passed in as resident state, only the
+    local window's means are recomputed (over that window alone); the
+    selection and the output are identical to computing every mean."""
+    say("wan block-sparse with resident key means")
+    q, k, v = wan_dev
+    lay = wl.sparse_layout(wan, 0.125)
+    args = dict(sink_begin=0, sink_count=lay["sink_count"], hist_begin=lay["hist_begin"],
+                hist_count=lay["hist_count"], C=lay["C"], local_begin=lay["local_begin"],
+                local_count=lay["local_count"], K=lay["K"], block=64, seg=1560, scale=wan.scale)
+    o0, l0, i0 = ca.block_sparse_fwd(q, k, v, **args)
+    o1, l1, i1 = ca.block_sparse_fwd(q, k, v, k_mean=i0["k_mean"].clone(), **args)
+    torch.cuda.synchronize()
+    assert i1["local_base"] == lay["local_begin"] and i1["k_mean_local"].shape[2] == lay["local_count"]
+    assert torch.equal(i1["k_mean_local"], i0["k_mean"][:, :, lay["local_begin"]:])
+    assert torch.equal(i1["local"] + i1["local_base"], i0["local"])
+    assert torch.equal(i1["local_indices"], i0["local_indices"])
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
 
 
 @pytest.mark.parametrize("q_block,alias", [(64, False), (256, False), (256, True)])
