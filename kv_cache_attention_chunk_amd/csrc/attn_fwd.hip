@@ -389,20 +389,23 @@ void attn_fwd_kernel(const AttnParams p) {
     auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
     nx[0] = f32x16_t{};
     nx[1] = f32x16_t{};
-    bf16x8_t ka = has_qk(0) ? kfrag(0, 0) : bf16x8_t{};
-    bf16x8_t va = {};
+    // MFMA operands of segment s are read PD segments ahead into ring slot
+    // s % (PD + 1), so each LDS read has PD segments of work to land in.
+    constexpr int PD = 2;
+    bf16x8_t kr[PD + 1], vr[PD + 1];
+    auto fetch = [&](int s1) {
+      const int g1 = s1 / SEG, i1 = s1 % SEG;
+      if (has_qk(s1)) kr[s1 % (PD + 1)] = kfrag(g1, i1);
+      if (has_pv(s1)) vr[s1 % (PD + 1)] = vfrag(g1 - 1, i1);
+    };
+#pragma unroll
+    for (int s1 = 0; s1 < PD; ++s1) fetch(s1);
     bf16x8_t pb = {};
     f32x8_t pf;
 #pragma unroll
     for (int s_ = 0; s_ < NSEG; ++s_) {
       const int g = s_ / SEG, i = s_ % SEG;
-      // operands of the next segment
-      bf16x8_t ka_n = {}, va_n = {};
-      if (s_ + 1 < NSEG) {
-        const int g1 = (s_ + 1) / SEG, i1 = (s_ + 1) % SEG;
-        if (has_qk(s_ + 1)) ka_n = kfrag(g1, i1);
-        if (has_pv(s_ + 1)) va_n = vfrag(g1 - 1, i1);
-      }
+      if (s_ + PD < NSEG) fetch(s_ + PD);
       // softmax VALU work of group g
       if (g < 4) {
         const int kt = g >> 1, u = g & 1;
@@ -412,13 +415,13 @@ void attn_fwd_kernel(const AttnParams p) {
           l += pf[e];   // float32 weights: the LSE must not carry bf16 rounding
         }
       }
-      if (has_pv(s_)) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[i], 0, 0, 0);
+      const int slot = s_ % (PD + 1);
+      if (has_pv(s_))
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[slot], pb, acc[i], 0, 0, 0);
       if (has_qk(s_))
-        nx[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[(g & 1) * QPG + i],
+        nx[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[slot], qreg[(g & 1) * QPG + i],
                                                             nx[g >> 1], 0, 0, 0);
       if (g < 4 && i == SEG - 1) pb = __builtin_convertvector(pf, bf16x8_t);
-      ka = ka_n;
-      va = va_n;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
