@@ -325,24 +325,23 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   };
 
-  // Row max of one tile's scores (masking keys past len_cur) and the
-  // accumulator rescale when a row's max grew.  Key of sc[kt][i] =
-  // 32kt + 8(i/4) + 4hg + i%4.
-  auto prep = [&](f32x16_t (&sc)[2], int len_cur) {
+  // Row max of one tile and the accumulator rescale when a row's max grew.
+  // The raw (unscaled) per-lane max of a full tile arrives precomputed in
+  // `rawmax`; a partial tile first masks keys past len_cur and takes its max
+  // here.  Key of sc[kt][i] = 32kt + 8(i/4) + 4hg + i%4.
+  auto prep = [&](f32x16_t (&sc)[2], int len_cur, float rawmax) {
+    float mx = rawmax;
     if (len_cur < kTileKeys) {
+      mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
           if (key >= len_cur) sc[kt][i] = -INFINITY;
+          mx = fmaxf(mx, sc[kt][i]);
         }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
     mx = half_max(mx) * p.scale_log2;
     // The exponent base m is the exact running row max, so the largest
     // weight of a row is exactly 1 and survives the bf16 rounding of P
@@ -359,53 +358,58 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   };
 
+  // Segments of the fused iteration body.  Group g (0..3) is the g-th 8-key
+  // slice of tile t's P; segment s of group g = s / SEG holds the QK MFMA of
+  // K fragment (g, s % SEG) for tile t+1 (if s % SEG < QPG; groups 0-1 build
+  // scores 0-31, groups 2-3 scores 32-63) and the PV MFMA of d tile s % SEG
+  // for group g - 1 (if g >= 1 and s % SEG < NDT); NDT tail segments finish
+  // group 3's PV.
+  constexpr int QPG = NST / 2;                      // K fragments per group
+  constexpr int SEG = QPG > NDT ? QPG : NDT;        // segments per group
+  constexpr int NSEG = 4 * SEG + NDT;
+  constexpr int EPS = 8 / SEG;                      // exp2 per segment
+  constexpr int PD = 2;                             // operand read-ahead, segments
+  auto has_qk = [](int s_) { return s_ < 4 * SEG && (s_ % SEG) < QPG; };
+  auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
+  auto kfrag = [&](int kb, int g, int i) {
+    const int st = (g & 1) * QPG + i;
+    return *reinterpret_cast<const bf16x8_t*>(kst + (kb ^ (32 * st)) + (g >> 1) * 32 * L::ROWB);
+  };
+  auto vfrag = [&](int vb, int g, int dt) {
+    const char* vp = vst + (vb ^ (64 * dt)) + (32 * (g >> 1) + 16 * (g & 1)) * L::ROWB;
+    const s16x4_t lo = ld_tr4(vp);
+    const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // MFMA operands of segment s are read PD segments ahead into ring slot
+  // s % (PD + 1), so each LDS read has PD segments of work to land in.
+  bf16x8_t kr[PD + 1], vr[PD + 1];
+  auto fetch = [&](int s1, int kb, int vb) {
+    const int g1 = s1 / SEG, i1 = s1 % SEG;
+    if (has_qk(s1)) kr[s1 % (PD + 1)] = kfrag(kb, g1, i1);
+    if (has_pv(s1)) vr[s1 % (PD + 1)] = vfrag(vb, g1 - 1, i1);
+  };
+
   // The fused body of one iteration, straight-line and explicitly ordered:
-  // P of tile t (exp2, row sum, bf16 pack) for the four 8-key groups, the QK
-  // MFMAs of tile t+1 (K stage ksn -> nx) and the PV MFMAs of tile t (V stage
-  // vs) are interleaved segment by segment, so the softmax VALU work issues
-  // while the matrix cores run.  Each segment's MFMA operands are read from
-  // LDS one segment ahead.  Group g's PV MFMAs run in group g+1's segments.
-  auto fused = [&](f32x16_t (&sc)[2], int vs, int ksn, f32x16_t (&nx)[2]) {
-    constexpr int QPG = NST / 2;                      // K fragments per group
-    constexpr int SEG = QPG > NDT ? QPG : NDT;        // segments per group
-    constexpr int NSEG = 4 * SEG + NDT;               // + tail: PV of group 3
-    constexpr int EPS = 8 / SEG;                      // exp2 per segment
+  // P of tile t (exp2, row sum, bf16 pack), the QK MFMAs of tile t+1 (-> nx)
+  // and the PV MFMAs of tile t are interleaved segment by segment, so the
+  // softmax VALU work issues while the matrix cores run.  The raw row max of
+  // nx is taken here too, each half a few segments after its last QK MFMA.
+  // The operands of segments 0 .. PD-1 have been fetched by the caller.
+  auto fused = [&](f32x16_t (&sc)[2], int kb, int vb, f32x16_t (&nx)[2], float& nmax) {
     const float m_use = m == -INFINITY ? 0.f : m;
-    const int vb = vs * L::TILEB + vbx;
-    const int kb = ksn * L::TILEB + kbx;
-    auto kfrag = [&](int g, int i) {
-      const int st = (g & 1) * QPG + i;
-      return *reinterpret_cast<const bf16x8_t*>(kst + (kb ^ (32 * st)) + (g >> 1) * 32 * L::ROWB);
-    };
-    auto vfrag = [&](int g, int dt) {
-      const char* vp = vst + (vb ^ (64 * dt)) + (32 * (g >> 1) + 16 * (g & 1)) * L::ROWB;
-      const s16x4_t lo = ld_tr4(vp);
-      const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // segment s: K fragment (g, i) if g < 4 and i < QPG; V fragment of group
-    // g - 1, d tile i, if 1 <= g and i < NDT (the tail segments have g = 4)
-    auto has_qk = [](int s_) { return s_ < 4 * SEG && (s_ % SEG) < QPG; };
-    auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
     nx[0] = f32x16_t{};
     nx[1] = f32x16_t{};
-    // MFMA operands of segment s are read PD segments ahead into ring slot
-    // s % (PD + 1), so each LDS read has PD segments of work to land in.
-    constexpr int PD = 2;
-    bf16x8_t kr[PD + 1], vr[PD + 1];
-    auto fetch = [&](int s1) {
-      const int g1 = s1 / SEG, i1 = s1 % SEG;
-      if (has_qk(s1)) kr[s1 % (PD + 1)] = kfrag(g1, i1);
-      if (has_pv(s1)) vr[s1 % (PD + 1)] = vfrag(g1 - 1, i1);
-    };
-#pragma unroll
-    for (int s1 = 0; s1 < PD; ++s1) fetch(s1);
+    float nm0 = -INFINITY, nm1 = -INFINITY;
+    constexpr int M0 = 2 * SEG + 1;                 // segments taking nx[0]'s max
+    constexpr int M1 = 4 * SEG;                     // segments taking nx[1]'s max
+    constexpr int V1 = 16 / NDT;                    // nx[1] values per tail segment
     bf16x8_t pb = {};
     f32x8_t pf;
 #pragma unroll
     for (int s_ = 0; s_ < NSEG; ++s_) {
       const int g = s_ / SEG, i = s_ % SEG;
-      if (s_ + PD < NSEG) fetch(s_ + PD);
+      if (s_ + PD < NSEG) fetch(s_ + PD, kb, vb);
       // softmax VALU work of group g
       if (g < 4) {
         const int kt = g >> 1, u = g & 1;
@@ -415,6 +419,12 @@ void attn_fwd_kernel(const AttnParams p) {
           l += pf[e];   // float32 weights: the LSE must not carry bf16 rounding
         }
       }
+      if (s_ >= M0 && s_ < M0 + 4)
+#pragma unroll
+        for (int e = 4 * (s_ - M0); e < 4 * (s_ - M0 + 1); ++e) nm0 = fmaxf(nm0, nx[0][e]);
+      if (s_ >= M1)
+#pragma unroll
+        for (int e = V1 * (s_ - M1); e < V1 * (s_ - M1 + 1); ++e) nm1 = fmaxf(nm1, nx[1][e]);
       const int slot = s_ % (PD + 1);
       if (has_pv(s_))
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[slot], pb, acc[i], 0, 0, 0);
@@ -424,7 +434,9 @@ void attn_fwd_kernel(const AttnParams p) {
       if (g < 4 && i == SEG - 1) pb = __builtin_convertvector(pf, bf16x8_t);
       __builtin_amdgcn_sched_barrier(0);
     }
+    nmax = fmaxf(nm0, nm1);
   };
+  static_assert(2 * SEG + 1 + 4 <= NSEG && 16 % NDT == 0, "max segments must fit the body");
 
   // Load pipeline.  K(t) is last read by the QK MFMAs of iteration t-1, so
   // K(t + KSTAGES) goes out at the start of iteration t; V(t) is read in
@@ -458,15 +470,22 @@ void attn_fwd_kernel(const AttnParams p) {
     dlen[j] = 0;
   }
 
+  // One iteration: the first operand reads of the fused body go out right
+  // after the barrier, ahead of the load issue and the rescale.
+  float rawmax = -INFINITY;     // raw row max of the tile in `cur`
   auto step = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
+    const int kb = ((t + 1) % L::KSTAGES) * L::TILEB + kbx;
+    const int vb = (t % L::VSTAGES) * L::TILEB + vbx;
+#pragma unroll
+    for (int s1 = 0; s1 < PD; ++s1) fetch(s1, kb, vb);
     if (t + VA < ntiles)
       ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((t + VA) % L::VSTAGES) * L::TILEB);
     if (t + KA < ntiles) {
       tile_src(t + KA, doff[KA], dlen[KA]);
       ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((t + KA) % L::KSTAGES) * L::TILEB);
     }
-    prep(cur, dlen[0]);
-    fused(cur, t % L::VSTAGES, (t + 1) % L::KSTAGES, nx);
+    prep(cur, dlen[0], rawmax);
+    fused(cur, kb, vb, nx, rawmax);
 #pragma unroll
     for (int j = 0; j < KA; ++j) {
       doff[j] = doff[j + 1];
@@ -497,6 +516,10 @@ void attn_fwd_kernel(const AttnParams p) {
       if (j < ntiles) ldr.issue_v(vh + doff[j], dlen[j], stride_bytes, vst + j * L::TILEB);
     wait_vm(0);
     qk(0, sa);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, sa[kt][i]);
     // iteration 0 refills K stage 0, which every wave has just read
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     block_sync();
