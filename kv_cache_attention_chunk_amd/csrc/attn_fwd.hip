@@ -5,8 +5,8 @@
 //   * K and V tiles go straight from global memory to LDS with buffer loads
 //     (buffer_load_dwordx4 ... lds, 1 KB per wave instruction): no staging
 //     registers, and the buffer range check returns zeros for rows past a
-//     partial tile.  K is triple- and V double-buffered: K(t+3) is loaded two
-//     iterations ahead of its use and V(t+1) one.
+//     partial tile.  K and V are double-buffered: K(t+2) and V(t+1) are
+//     loaded during iteration t.
 //   * LDS rows are unpadded and XOR-swizzled by 16-byte chunk so that every
 //     read pattern below is free of bank conflicts: K chunk c of row r sits at
 //     c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64); V chunk c at
@@ -33,6 +33,8 @@
 // head's span of a flat ragged buffer (Pyramid Forcing page, section 3).
 #include "common.h"
 
+#include <type_traits>
+
 namespace chunkattn {
 
 namespace {
@@ -40,13 +42,14 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
-// LDS ring of K and V tile stages: K x3 and V x2 (80 KB at d = 128, so two
-// 4-wave workgroups share a CU).
+// LDS ring of K and V tile stages: K x2 and V x2 (64 KB at d = 128, so two
+// 4-wave workgroups share a CU).  With two stages each, the stage of every
+// read is a compile-time constant in the two-iteration unrolled loop.
 template <int D, int NW>
 struct Layout {
   static constexpr int ROWB = 2 * D;                    // bytes per K / V row
   static constexpr int TILEB = kTileKeys * ROWB;        // bytes per K or V tile
-  static constexpr int KSTAGES = 3;
+  static constexpr int KSTAGES = 2;
   static constexpr int VSTAGES = 2;
   static constexpr int LDSB = (KSTAGES + VSTAGES) * TILEB;
   // physical 16-byte chunk of logical chunk c in row r
@@ -282,11 +285,17 @@ void attn_fwd_kernel(const AttnParams p) {
   //     = 32(st ^ (kz >> 1)) + 16(hg ^ (kz & 1)).
   const int kz = L::swz_k(col);
   const int kbx = col * L::ROWB + 16 * (hg ^ (kz & 1)) + 32 * (kz >> 1);
+  int kx[NST];                    // per-k-step K read offsets within a stage
+#pragma unroll
+  for (int st = 0; st < NST; ++st) kx[st] = kbx ^ (32 * st);
   //   V source row 4hg + (lane & 15)/4 (+ 32kt + 16u + 8 half), chunk
   //   4dt + vcol16: byte 16((4dt + vcol16) ^ vz) = 64(dt ^ vz/4) + 16 vcol16.
   const int vz = D == 128 ? ((lane & 15) >> 2) : ((lane >> 3) & 1);
   const int vcol16 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vbx = (4 * hg + ((lane & 15) >> 2)) * L::ROWB + 8 * (lane & 1) + 16 * vcol16 + 64 * vz;
+  int vx[NDT];                    // per-d-tile V read offsets within a stage
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) vx[dt] = vbx ^ (64 * dt);
 
   f32x16_t acc[NDT];
 #pragma unroll
@@ -312,14 +321,13 @@ void attn_fwd_kernel(const AttnParams p) {
 
   // S^T = K Q^T for the two 32-key halves of the tile in K stage ks.
   auto qk = [&](int ks, f32x16_t (&sc)[2]) {
-    const int kb = ks * L::TILEB + kbx;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sc[kt] = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            kst + (kb ^ (32 * st)) + kt * 32 * L::ROWB);
+            kst + ks * L::TILEB + kx[st] + kt * 32 * L::ROWB);
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sc[kt], 0, 0, 0);
       }
     }
@@ -371,12 +379,12 @@ void attn_fwd_kernel(const AttnParams p) {
   constexpr int PD = 2;                             // operand read-ahead, segments
   auto has_qk = [](int s_) { return s_ < 4 * SEG && (s_ % SEG) < QPG; };
   auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
-  auto kfrag = [&](int kb, int g, int i) {
+  auto kfrag = [&](int ks, int g, int i) {
     const int st = (g & 1) * QPG + i;
-    return *reinterpret_cast<const bf16x8_t*>(kst + (kb ^ (32 * st)) + (g >> 1) * 32 * L::ROWB);
+    return *reinterpret_cast<const bf16x8_t*>(kst + ks * L::TILEB + kx[st] + (g >> 1) * 32 * L::ROWB);
   };
-  auto vfrag = [&](int vb, int g, int dt) {
-    const char* vp = vst + (vb ^ (64 * dt)) + (32 * (g >> 1) + 16 * (g & 1)) * L::ROWB;
+  auto vfrag = [&](int vs, int g, int dt) {
+    const char* vp = vst + vs * L::TILEB + vx[dt] + (32 * (g >> 1) + 16 * (g & 1)) * L::ROWB;
     const s16x4_t lo = ld_tr4(vp);
     const s16x4_t hi = ld_tr4(vp + 8 * L::ROWB);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -384,10 +392,10 @@ void attn_fwd_kernel(const AttnParams p) {
   // MFMA operands of segment s are read PD segments ahead into ring slot
   // s % (PD + 1), so each LDS read has PD segments of work to land in.
   bf16x8_t kr[PD + 1], vr[PD + 1];
-  auto fetch = [&](int s1, int kb, int vb) {
+  auto fetch = [&](int s1, int ks, int vs) {
     const int g1 = s1 / SEG, i1 = s1 % SEG;
-    if (has_qk(s1)) kr[s1 % (PD + 1)] = kfrag(kb, g1, i1);
-    if (has_pv(s1)) vr[s1 % (PD + 1)] = vfrag(vb, g1 - 1, i1);
+    if (has_qk(s1)) kr[s1 % (PD + 1)] = kfrag(ks, g1, i1);
+    if (has_pv(s1)) vr[s1 % (PD + 1)] = vfrag(vs, g1 - 1, i1);
   };
 
   // The fused body of one iteration, straight-line and explicitly ordered:
@@ -396,7 +404,7 @@ void attn_fwd_kernel(const AttnParams p) {
   // softmax VALU work issues while the matrix cores run.  The raw row max of
   // nx is taken here too, each half a few segments after its last QK MFMA.
   // The operands of segments 0 .. PD-1 have been fetched by the caller.
-  auto fused = [&](f32x16_t (&sc)[2], int kb, int vb, f32x16_t (&nx)[2], float& nmax) {
+  auto fused = [&](f32x16_t (&sc)[2], int ks, int vs, f32x16_t (&nx)[2], float& nmax) {
     const float m_use = m == -INFINITY ? 0.f : m;
     nx[0] = f32x16_t{};
     nx[1] = f32x16_t{};
@@ -409,7 +417,7 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
     for (int s_ = 0; s_ < NSEG; ++s_) {
       const int g = s_ / SEG, i = s_ % SEG;
-      if (s_ + PD < NSEG) fetch(s_ + PD, kb, vb);
+      if (s_ + PD < NSEG) fetch(s_ + PD, ks, vs);
       // softmax VALU work of group g
       if (g < 4) {
         const int kt = g >> 1, u = g & 1;
@@ -446,7 +454,7 @@ void attn_fwd_kernel(const AttnParams p) {
   // in flight: vmcnt counts this wave's loads in issue order.
   constexpr int NIK = TileLoader<D, NW>::NI;     // load instructions per wave per tile
   constexpr int KA = L::KSTAGES, VA = L::VSTAGES - 1;   // K / V load lead in tiles
-  static_assert(VA <= 2 && KA <= VA + 2, "wait counts below assume these leads");
+  static_assert(KA >= 2 && VA >= 1, "K(t+2) and V(t+1) must already be on their way");
   auto wait_vm = [&](int groups_after) {
     // s_waitcnt vmcnt(n): vmcnt[3:0] | expcnt 7 << 4 | lgkmcnt 0 << 8 | vmcnt[5:4] << 14
 #define CA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
@@ -473,32 +481,38 @@ void attn_fwd_kernel(const AttnParams p) {
   // One iteration: the first operand reads of the fused body go out right
   // after the barrier, ahead of the load issue and the rescale.
   float rawmax = -INFINITY;     // raw row max of the tile in `cur`
-  auto step = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
-    const int kb = ((t + 1) % L::KSTAGES) * L::TILEB + kbx;
-    const int vb = (t % L::VSTAGES) * L::TILEB + vbx;
+  // `par` = t % 2 as a compile-time constant (the loop below is unrolled by
+  // two), which makes every stage index a constant offset.
+  static_assert(L::KSTAGES == 2 && L::VSTAGES == 2, "stage indices below assume two stages");
+  auto step = [&](int t, auto par, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
+    constexpr int P = decltype(par)::value;
+    constexpr int ks = (P + 1) % 2, vs = P;
 #pragma unroll
-    for (int s1 = 0; s1 < PD; ++s1) fetch(s1, kb, vb);
+    for (int s1 = 0; s1 < PD; ++s1) fetch(s1, ks, vs);
     if (t + VA < ntiles)
-      ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((t + VA) % L::VSTAGES) * L::TILEB);
+      ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((P + VA) % 2) * L::TILEB);
     if (t + KA < ntiles) {
       tile_src(t + KA, doff[KA], dlen[KA]);
-      ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((t + KA) % L::KSTAGES) * L::TILEB);
+      ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((P + KA) % 2) * L::TILEB);
     }
     prep(cur, dlen[0], rawmax);
-    fused(cur, kb, vb, nx, rawmax);
+    fused(cur, ks, vs, nx, rawmax);
 #pragma unroll
     for (int j = 0; j < KA; ++j) {
       doff[j] = doff[j + 1];
       dlen[j] = dlen[j + 1];
     }
-    // Tile groups issued after V(t+1), which may stay in flight.  V(t+1) went
-    // out in iteration t + 1 - VA (or, for t + 1 < VA, in the prologue, which
-    // ended with a full wait).
+    // Tile loads issued after the later of V(t+1) and K(t+2), which may stay
+    // in flight.  V(t+1) went out in iteration t + 1 - VA and K(t+2) in
+    // iteration t + 2 - KA (a negative iteration is the prologue, which ended
+    // with a full wait); within an iteration V goes out before K.
+    const int it_k = t + 2 - KA, it_v = t + 1 - VA;
+    const int last_it = it_k > it_v ? it_k : it_v;
+    const int last_slot = it_k >= it_v ? 1 : 0;
     int after = 0;
-    for (int it = t + 1 - VA; it <= t; ++it) {
-      if (it < 0) continue;
-      if (it != t + 1 - VA && it + VA < ntiles) ++after;   // V(it + VA)
-      if (it + KA < ntiles) ++after;                        // K(it + KA)
+    for (int it = last_it > 0 ? last_it : 0; it <= t; ++it) {
+      if ((it > last_it || last_slot < 0) && it + VA < ntiles) ++after;   // V(it + VA)
+      if ((it > last_it || last_slot < 1) && it + KA < ntiles) ++after;   // K(it + KA)
     }
     wait_vm(after);
   };
@@ -524,8 +538,8 @@ void attn_fwd_kernel(const AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     block_sync();
     for (int t = 0; t < ntiles; t += 2) {
-      step(t, sa, sb);
-      if (t + 1 < ntiles) step(t + 1, sb, sa);
+      step(t, std::integral_constant<int, 0>{}, sa, sb);
+      if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{}, sb, sa);
     }
   }
 
