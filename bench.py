@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -91,16 +93,185 @@ def cpu_baseline(w):
                       f"float64 numpy oracle, {dt:.1f} s"}
 
 
+def _time_ms(torch, fn, reps=10, warmup_s=0.2):
+    """Average HIP-event time of fn() on the current stream, in ms, after
+    about warmup_s seconds of untimed calls (clocks settle under load)."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warmup_s:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _block_len(ids, block=64, seg=1560):
+    """Tokens of frame-aligned block ids (25 blocks per 1560-token frame)."""
+    bps = -(-seg // block)
+    return np.minimum(block, seg - block * (np.asarray(ids) % bps))
+
+
+def _rec(ms, flops, kv_bytes, **extra):
+    r = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+         "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+         "kv_GBs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+         "kv_frac_hbm": round(kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+         "gflop": round(flops / 1e9, 2), "kv_MB": round(kv_bytes / 1e6, 2)}
+    r.update(extra)
+    return r
+
+
+def per_config(reps=10, wan=None):
+    """Time every configured workload once on the GPU (inputs resident):
+    tiny dense + merge, Wan dense + merge, block-sparse at three top-K ratios,
+    ragged 12-head, mixed 40-head.  FLOPs are algorithmic (4 d per score of
+    every key set attended); kv bytes are the distinct K/V bytes the call
+    must read."""
+    import torch
+    import kv_cache_attention_chunk_amd as ca
+    from kv_cache_attention_chunk_amd import workloads as wl
+    dev = lambda t: torch.from_numpy(t.bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    out = {}
+
+    def merged_fn(q, k, v, w, seg):
+        br = []
+        for key in ("local_blocks", "history_blocks"):
+            blocks = np.array(w.meta[key], np.int32)
+            BH = w.B * w.H
+            br.append((i32(np.arange(BH + 1) * len(blocks)), i32(np.tile(blocks, BH)),
+                       torch.empty((w.B, w.Nq, w.H, w.d), dtype=torch.float32, device="cuda"),
+                       torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")))
+        om = torch.empty_like(q)
+        lm = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+        def fn():
+            for ip, ix, ob, lb in br:
+                ca.chunk_attn_fwd(q, k, v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=seg,
+                                  q_block=w.Nq, q_seg=w.Nq, scale=w.scale,
+                                  out_dtype=torch.float32, out=ob, lse=lb)
+            ca.lse_merge(br[0][2], br[0][3], br[1][2], br[1][3], out=om, out_lse=lm)
+        return fn
+
+    # tiny dense chunk (launch-latency scale; no roofline claim)
+    w = wl.tiny_dense(seed=0)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
+    kvb = 2.0 * w.Nkv * w.H * w.d * 2
+    ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps)
+    ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv), reps)
+    out["tiny_dense"] = {"dense_us": round(ms_d * 1e3, 1), "local_history_merge_us": round(ms_m * 1e3, 1),
+                         "gflop": round(f / 1e9, 3)}
+    # Wan-1.3B layer: dense and local/history merge
+    w = wan or wl.wan_dense(seed=0)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
+    kvb = 2.0 * w.Nkv * w.H * w.d * 2
+    out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps), f, kvb)
+    out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
+    # block-sparse path at the three top-K ratios (selection included)
+    km = ca.block_mean(k, 64, 1560)
+    nqb = ca.num_blocks(w.Nq, 64, 1560)
+    qlen = np.tile(_block_len(np.arange(nqb)), w.B * w.H)
+    for ratio in (0.25, 0.125, 0.0625):
+        lay = wl.sparse_layout(w, ratio)
+        fn = lambda: ca.block_sparse_fwd(
+            q, k, v, sink_begin=0, sink_count=lay["sink_count"], hist_begin=lay["hist_begin"],
+            hist_count=lay["hist_count"], C=lay["C"], local_begin=lay["local_begin"],
+            local_count=lay["local_count"], K=lay["K"], block=64, seg=1560, k_mean=km,
+            scale=w.scale)
+        _, _, info = fn()
+        torch.cuda.synchronize()
+        sp, sx = info["shared_indptr"].cpu().numpy(), info["shared_indices"].cpu().numpy()
+        lp, lx = info["local_indptr"].cpu().numpy(), info["local_indices"].cpu().numpy()
+        sh = np.array([_block_len(sx[sp[r]:sp[r + 1]]).sum() for r in range(w.B * w.H)])
+        lo = np.array([_block_len(lx[lp[r]:lp[r + 1]]).sum() for r in range(w.B * w.H * nqb)])
+        f = 4.0 * w.d * (float(sh.sum()) * w.Nq + float((lo * qlen).sum()))
+        uniq = sum(_block_len(np.union1d(sx[sp[h]:sp[h + 1]], lx[lp[h * nqb]:lp[(h + 1) * nqb]])).sum()
+                   for h in range(w.B * w.H))
+        kvb = 2.0 * float(uniq) * w.d * 2
+        ms = _time_ms(torch, fn, reps)
+        # dense-equivalent rate: the dense layer's FLOPs over the sparse path's time
+        f_dense = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
+        out[f"sparse_K{lay['K']}"] = _rec(ms, f, kvb, ratio=ratio,
+                                          dense_equiv_tflops=round(f_dense / (ms * 1e-3) / 1e12, 1))
+    del q, k, v, km
+    # ragged per-head caches
+    w = wl.ragged(seed=0)
+    q, kf, vf, cu = dev(w.q), dev(w.k_flat), dev(w.v_flat), i32(w.cu_seqlens)
+    tot = int(w.cu_seqlens[-1])
+    f = 4.0 * w.d * w.Nq * tot
+    kvb = 2.0 * tot * w.d * 2
+    out["ragged"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_varlen_fwd(
+        q, kf, vf, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
+        sum_len=tot, lengths_frames=w.meta["n_frames"])
+    del q, kf, vf
+    # mixed 40-head layer (dense / block lists / ragged per head)
+    w = wl.mixed(seed=0)
+    lay = w.meta["sparse"]
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    hs = [h for h in range(w.H) if w.head_mode[h] == 1]
+    hsel = torch.tensor(hs, device="cuda")
+    qs, ks = q.index_select(2, hsel).contiguous(), k.index_select(2, hsel).contiguous()
+    qm, kms, cm = ca.block_mean(qs, 64, 1560), ca.block_mean(ks, 64, 1560), ca.block_mean(qs, w.Nq, w.Nq)
+    pers = ca.block_score_topk(cm, kms, lay["C"], cand_begin=lay["hist_begin"], cand_count=lay["hist_count"])
+    loc = ca.block_score_topk(qm, kms, lay["K"], cand_begin=lay["local_begin"], cand_count=lay["local_count"])
+    ip_s, ix_s = ca.build_kv_index(1, len(hs), nqb, 0, lay["sink_count"], pers[:, :, 0, :].contiguous(), loc, 0)
+    ip_s, ix_s = ip_s.cpu().numpy(), ix_s.cpu().numpy()
+    del qs, ks
+    lists, f, kvb = [], 0.0, 0.0
+    for h in range(w.H):
+        for qb in range(nqb):
+            if w.head_mode[h] == 1:
+                r = hs.index(h) * nqb + qb
+                lists.append(ix_s[ip_s[r]:ip_s[r + 1]])
+            else:
+                lists.append(np.zeros(0, np.int32))
+        if w.head_mode[h] == 0:
+            f += 4.0 * w.d * w.Nq * w.Nkv
+            kvb += 2.0 * w.Nkv * w.d * 2
+        elif w.head_mode[h] == 1:
+            rl = lists[h * nqb:(h + 1) * nqb]
+            f += 4.0 * w.d * float(sum(_block_len(x).sum() * ql for x, ql in zip(rl, qlen[:nqb])))
+            kvb += 2.0 * float(_block_len(np.unique(np.concatenate(rl))).sum()) * w.d * 2
+        else:
+            L = int(w.cu_seqlens[h + 1] - w.cu_seqlens[h])
+            f += 4.0 * w.d * w.Nq * L
+            kvb += 2.0 * L * w.d * 2
+    ip = np.zeros(len(lists) + 1, np.int32)
+    ip[1:] = np.cumsum([len(x) for x in lists])
+    ix = i32(np.concatenate(lists))
+    ip = i32(ip)
+    kf, vf, cu = dev(w.k_flat), dev(w.v_flat), i32(w.cu_seqlens)
+    out["mixed_40h"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_mixed_fwd(
+        q, w.head_mode, k=k, v=v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
+        q_block=64, q_seg=1560, k_flat=kf, v_flat=vf, cu_seqlens=cu,
+        cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
+        heads_dense_sparse_ragged=[int((w.head_mode == m).sum()) for m in range(3)])
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--topk-ratio", type=float, default=0.125)
-    ap.add_argument("--only", choices=["step", "dense", "copy"], default="step",
+    ap.add_argument("--only", choices=["step", "dense", "copy", "configs"], default="step",
                     help="'dense' times the dense kernel alone (for counter runs); 'copy' "
                          "runs a plain 1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload timings (tiny, Wan dense/merge, sparse at three "
+                         "top-K ratios, ragged, mixed 40-head)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -133,6 +304,9 @@ def main():
         ms = e0.elapsed_time(e1) / args.steps
         print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes,
                           "ms": ms, "GBps_read+write": 2 * n_bytes / (ms * 1e-3) / 1e9}))
+        return
+    if args.only == "configs":
+        print(json.dumps(per_config()), flush=True)
         return
     t0 = time.perf_counter()
     w = wl.wan_dense(seed=0)
@@ -261,6 +435,10 @@ def main():
     if args.only == "step":
         out["phase_tflops"]["merge_variant"] = round(f_merge / (res["merge_variant_ms"] * 1e-3) / 1e12, 1)
         out["phase_tflops"]["sparse_path"] = round(f_sparse / (res["sparse_path_ms"] * 1e-3) / 1e12, 1)
+    if args.only == "step" and not args.no_configs:
+        t0 = time.perf_counter()
+        out["configs"] = per_config(wan=w)
+        log(f"per-workload timings in {time.perf_counter() - t0:.1f} s")
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         out["cpu_baseline"] = cpu_baseline(w)

@@ -5,7 +5,8 @@
  * Plain C ABI.  Every tensor argument is a DEVICE pointer owned by the caller
  * unless marked "host".  Every call is asynchronous on `stream` (a hipStream_t;
  * NULL = the null stream), never synchronises, never allocates device memory
- * and keeps no state between calls besides the thread-local error text.
+ * and keeps no state between calls besides the thread-local error text and a
+ * per-device count of resident workgroups, queried once.
  *
  * Element types: CA_BF16 = bfloat16 (round-to-nearest-even on output),
  * CA_F32 = IEEE float32.  LSE is always float32, natural log.
@@ -29,13 +30,14 @@
 #ifndef CHUNKATTN_H
 #define CHUNKATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define CA_ABI_VERSION 1
+#define CA_ABI_VERSION 2
 
 enum ca_status {
   CA_OK = 0,
@@ -65,6 +67,28 @@ const char* ca_last_error(void);
  * blocks of 64 plus one block of 24.  Host-only; returns -1 on bad sizes.
  */
 int ca_num_blocks(int n_tokens, int block_size, int seg_len);
+
+/*
+ * Size in bytes of the optional workspace of the chunk-attention calls for
+ * head dim d (64 or 128) on the current device; 0 for another d or no device.
+ *
+ * With a workspace (caller-owned device memory, 16-byte aligned, at least this
+ * size) a dense or ragged launch may take the balanced schedule: its grid is
+ * the number of workgroups the device holds at once, and each workgroup takes
+ * an equal share of the (query tile, 64-key tile) pairs of all heads, in head
+ * order.  A query tile whose key range is split between workgroups is
+ * finished by an LSE merge of the float32 partial results (O/l, LSE) that
+ * the workgroups leave in the workspace: attention over consecutive key
+ * ranges recombined through the LSE state (ISPA page, section 2 item 1).
+ * The result is the same attention up to float32 rounding.  The schedule is
+ * taken only when it shortens the launch (heads of unequal length, or more
+ * query tiles than the device holds at once, not a whole multiple of it);
+ * it needs every head's key count on the host (always for the dense cache;
+ * for ragged heads only with cu_seqlens_host).  Calls sharing one workspace
+ * must be ordered on one stream.  NULL = no workspace: one workgroup per
+ * (head, query tile).
+ */
+size_t ca_attn_workspace_bytes(int d);
 
 /*
  * Chunk attention, dense or block-list cache.  For each (b, h) and query row i
@@ -99,6 +123,10 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  *                alias lse_init.
  *   o            [B, Nq, H, d] of o_dtype (CA_BF16 or CA_F32), strides o_strides
  *   lse          float32 [B, H, Nq]; an empty key set gives O = 0, LSE = -inf
+ *   workspace,   optional (NULL, 0 allowed), see ca_attn_workspace_bytes; used
+ *   workspace_bytes  by the dense cache only (block lists and o_init ignore
+ *                it).  A workspace smaller than the schedule needs is
+ *                CA_EINVAL.
  */
 int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       int B, int H, int Nq, int Nkv, int d,
@@ -107,7 +135,8 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
                       int kv_block, int kv_seg, int q_block, int q_seg, float scale,
                       const float* o_init, const int64_t* o_init_strides, const float* lse_init,
-                      void* o, int o_dtype, float* lse, void* stream);
+                      void* o, int o_dtype, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunk attention over ragged per-head caches (Pyramid Forcing page, section
@@ -118,8 +147,9 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
  *                   may be NULL when total_kv = 0
  *   cu_seqlens      int32 [B*H + 1], device, nondecreasing, cu[0] = 0,
  *                   cu[B*H] <= total_kv
- *   cu_seqlens_host optional host copy (NULL allowed): when given, heads are
- *                   scheduled longest first.
+ *   cu_seqlens_host optional host copy (NULL allowed), equal to cu_seqlens:
+ *                   when given, the launch can take the balanced schedule
+ *                   (with a workspace), else heads are scheduled longest first.
  * Other arguments as in ca_chunk_attn_fwd.
  */
 int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_flat,
@@ -127,7 +157,8 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
                              int total_kv, int B, int H, int Nq, int d,
                              const int64_t* q_strides, int64_t kv_row_stride,
                              const int64_t* o_strides, float scale,
-                             void* o, int o_dtype, float* lse, void* stream);
+                             void* o, int o_dtype, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Mixed per-head cache modes in one call (Pyramid Forcing page, section 3:
@@ -136,7 +167,9 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
  * CA_MODE_BLOCKS (k, v + the CSR, as in ca_chunk_attn_fwd; rows of other heads
  * are ignored) or CA_MODE_VARLEN (k_flat, v_flat + cu_seqlens, as in
  * ca_chunk_attn_varlen_fwd; other heads' spans are ignored).  Pointers of a
- * mode no head uses may be NULL.
+ * mode no head uses may be NULL.  Dense and ragged heads share one launch
+ * (balanced across them when a workspace is given and the ragged lengths are
+ * known on the host); block-list heads follow in a second launch.
  */
 int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v,
                             int B, int H, int Nq, int Nkv, int d,
@@ -147,7 +180,8 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v,
                             const void* k_flat, const void* v_flat,
                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                             int total_kv, int64_t kv_row_stride, float scale,
-                            void* o, int o_dtype, float* lse, void* stream);
+                            void* o, int o_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * LSE merge of two attention results over disjoint key sets (ISPA page,

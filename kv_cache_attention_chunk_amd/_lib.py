@@ -12,6 +12,7 @@ import re
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libchunkattn.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "chunkattn.h")
 
+ABI_VERSION = 2
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
 CA_BF16, CA_F32 = 0, 1
 CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
@@ -22,20 +23,22 @@ _f = ctypes.c_float
 _i64 = ctypes.c_int64
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i32p = ctypes.c_void_p   # device or host int32 pointers are passed as addresses
+_sz = ctypes.c_size_t
 
 SIGNATURES = {
     "ca_abi_version": (_i, []),
     "ca_status_str": (ctypes.c_char_p, [_i]),
     "ca_last_error": (ctypes.c_char_p, []),
     "ca_num_blocks": (_i, [_i, _i, _i]),
+    "ca_attn_workspace_bytes": (_sz, [_i]),
     "ca_chunk_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
                                _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i64p, _p,
-                               _p, _i, _p, _p]),
+                               _p, _i, _p, _p, _sz, _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
-                                      _i64p, _i64, _i64p, _f, _p, _i, _p, _p]),
+                                      _i64p, _i64, _i64p, _f, _p, _i, _p, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
                                      _i32p, _i32p, _i32p, _i, _i, _i, _i, _i, _p, _p,
-                                     _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _p]),
+                                     _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _p, _sz, _p]),
     "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
                           _i64p, _i64p, _i64p, _p]),
     "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),
@@ -65,7 +68,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.ca_abi_version() != 1:
+        if L.ca_abi_version() != ABI_VERSION:
             raise RuntimeError("libchunkattn ABI version mismatch")
         _LIB = L
     return _LIB

@@ -79,6 +79,36 @@ def _check_indptr(indptr, BH, Nq, q_block, q_seg):
         raise ValueError(f"kv_indptr must have B*H*NQB + 1 = {rows + 1} entries")
 
 
+_WS_BYTES = {}
+
+
+def workspace_bytes(d: int) -> int:
+    """Bytes of the balanced schedule's workspace for head dim d on the current
+    device (0 when it does not apply)."""
+    key = (torch.cuda.current_device(), d)
+    if key not in _WS_BYTES:
+        _WS_BYTES[key] = int(lib().ca_attn_workspace_bytes(d))
+    return _WS_BYTES[key]
+
+
+def _workspace(d: int, device, given: Optional[torch.Tensor] = None
+               ) -> Tuple[Optional[torch.Tensor], int]:
+    """Scratch for the balanced schedule of the dense / ragged launches: the
+    caller's uint8 tensor, else one from torch's caching allocator
+    (stream-ordered like every other tensor)."""
+    if given is not None:
+        if given.dtype != torch.uint8 or not given.is_cuda or not given.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        return given, given.numel()
+    key = (torch.cuda.current_device(), d)
+    if key not in _WS_BYTES:
+        _WS_BYTES[key] = int(lib().ca_attn_workspace_bytes(d))
+    n = _WS_BYTES[key]
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
 def num_blocks(n_tokens: int, block_size: int, seg_len: int) -> int:
     r = lib().ca_num_blocks(n_tokens, block_size, seg_len)
     if r < 0:
@@ -93,13 +123,16 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                    q_block: int = 64, q_seg: Optional[int] = None,
                    scale: Optional[float] = None, out_dtype=None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   o_init: Optional[torch.Tensor] = None, lse_init: Optional[torch.Tensor] = None
+                   o_init: Optional[torch.Tensor] = None, lse_init: Optional[torch.Tensor] = None,
+                   balanced: bool = True, workspace: Optional[torch.Tensor] = None
                    ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk attention against a dense cache, or against per-query-block
     block lists (CSR kv_indptr / kv_indices) when given.  Returns (O, LSE).
     With (o_init float32 [B,Nq,H,d], lse_init [B,H,Nq]) from attention over a
     disjoint key set, the result is their LSE merge with this key set.
-    The output dtype is out_dtype, else out's dtype, else bf16."""
+    The output dtype is out_dtype, else out's dtype, else bf16.  `balanced`
+    lets a dense launch split key ranges evenly over the device's resident
+    workgroups (a workspace is allocated for it)."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q), _bshd("k", k), _bshd("v", v)
     B, Nq, H, d = q.shape
@@ -123,13 +156,16 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
         if lse_init.dtype != torch.float32 or tuple(lse_init.shape) != (B, H, Nq) or \
                 not lse_init.is_contiguous():
             raise ValueError("lse_init must be contiguous float32 [B, H, Nq]")
+    ws, wsb = (None, 0)
+    if balanced and kv_indptr is None and o_init is None:
+        ws, wsb = _workspace(d, q.device, workspace)
     st = lib().ca_chunk_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d,
         _st(q), _st(k), _st(o),
         _ptr(kv_indptr), _ptr(kv_indices), nnz, kv_block, kv_seg or max(Nkv, 1),
         q_block, q_seg or max(Nq, 1), sc, _ptr(o_init),
         None if o_init is None else _st(o_init), _ptr(lse_init),
-        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
     check(st)
     return o, l
 
@@ -137,10 +173,13 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
 def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.Tensor,
                           cu_seqlens: torch.Tensor, *, cu_seqlens_host: Optional[np.ndarray] = None,
                           scale: Optional[float] = None, out_dtype=None,
-                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          balanced: bool = True, workspace: Optional[torch.Tensor] = None
                           ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk attention against ragged per-head caches flattened into
-    k_flat / v_flat [total, d] with cu_seqlens [B*H + 1] boundaries."""
+    k_flat / v_flat [total, d] with cu_seqlens [B*H + 1] boundaries.  With
+    cu_seqlens_host (a host copy equal to cu_seqlens) and `balanced`, key
+    ranges are split evenly over the device's resident workgroups."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q)
     B, Nq, H, d = q.shape
@@ -159,11 +198,12 @@ def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.T
     o = _out(B, Nq, H, d, out_dtype, q.device, out)
     l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws, wsb = _workspace(d, q.device, workspace) if (balanced and host is not None) else (None, 0)
     st = lib().ca_chunk_attn_varlen_fwd(
         q.data_ptr(), k_flat.data_ptr(), v_flat.data_ptr(), cu_seqlens.data_ptr(),
         None if host is None else host.ctypes.data, k_flat.shape[0], B, H, Nq, d,
         _st(q), k_flat.stride(0) if k_flat.numel() else d, _st(o), sc,
-        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
     check(st)
     return o, l
 
@@ -172,8 +212,10 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
                          kv_indices=None, kv_block: int = 64, kv_seg: Optional[int] = None,
                          q_block: int = 64, q_seg: Optional[int] = None, k_flat=None, v_flat=None,
                          cu_seqlens=None, cu_seqlens_host=None, scale: Optional[float] = None,
-                         out_dtype=None, out=None, lse=None):
-    """Per-head cache modes (0 dense, 1 block lists, 2 ragged) in one call."""
+                         out_dtype=None, out=None, lse=None, balanced: bool = True,
+                         workspace: Optional[torch.Tensor] = None):
+    """Per-head cache modes (0 dense, 1 block lists, 2 ragged) in one call;
+    dense and ragged heads share one (balanced) launch."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q)
     B, Nq, H, d = q.shape
@@ -195,6 +237,7 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
     l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kvs = _st(k) if k is not None else strides3((0, 0, 0))
+    ws, wsb = _workspace(d, q.device, workspace) if balanced else (None, 0)
     st = lib().ca_chunk_attn_mixed_fwd(
         q.data_ptr(), _ptr(k), _ptr(v), B, H, Nq, Nkv, d, _st(q), kvs,
         _st(o), mode.ctypes.data, _ptr(kv_indptr), _ptr(kv_indices),
@@ -202,7 +245,7 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
         q_block, q_seg or max(Nq, 1), _ptr(k_flat), _ptr(v_flat), _ptr(cu_seqlens),
         None if host is None else host.ctypes.data,
         0 if k_flat is None else k_flat.shape[0], d if k_flat is None else k_flat.stride(0),
-        sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _stream())
+        sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
     check(st)
     return o, l
 

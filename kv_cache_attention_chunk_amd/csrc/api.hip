@@ -102,38 +102,102 @@ void fill_common(AttnParams& p, const Common& c) {
   p.scale_log2 = c.scale * 1.4426950408889634f;
 }
 
-constexpr int kDenseWaves = 4;            // 128 query rows per workgroup
+constexpr int kDenseWaves = 4;            // 128 query rows per workgroup (range mode)
+constexpr int kMinUnitsPerWg = 8;         // balanced schedule: key tiles per workgroup, at least
 
-// Launch over a list of heads (or all heads when `heads` is empty), splitting
-// the list into launches of at most kMaxHeadsPerLaunch heads.
-int launch_heads(int mode, const Common& c, AttnParams& p, const std::vector<int>& heads,
-                 hipStream_t stream) {
+// Block mode: one workgroup per query block (or row slice of one), over a
+// list of heads (all heads when `heads` is empty), in launches of at most
+// kMaxHeadsPerLaunch heads.
+int launch_blocks(const Common& c, AttnParams& p, const std::vector<int>& heads,
+                  hipStream_t stream) {
   const bool all = heads.empty();
   const int nh = all ? c.B * c.H : (int)heads.size();
-  int nwaves;
-  if (mode == MODE_BLOCKS) {
-    // one workgroup per query block (or row slice of one)
-    int maxq = std::min(std::min(p.q_block, p.q_seg), std::max(c.Nq, 1));
-    nwaves = maxq <= 64 ? 2 : 4;
-    p.q_sub = (maxq + nwaves * 32 - 1) / (nwaves * 32);
-  } else {
-    nwaves = kDenseWaves;
-    p.n_qtiles = (c.Nq + nwaves * 32 - 1) / (nwaves * 32);
-  }
+  const int maxq = std::min(std::min(p.q_block, p.q_seg), std::max(c.Nq, 1));
+  const int nwaves = maxq <= 64 ? 2 : 4;
+  p.q_sub = (maxq + nwaves * 32 - 1) / (nwaves * 32);
   for (int h0 = 0; h0 < nh; h0 += kMaxHeadsPerLaunch) {
     const int n = std::min(kMaxHeadsPerLaunch, nh - h0);
     p.n_heads = n;
     p.use_list = (all && h0 == 0) ? 0 : 1;
     if (p.use_list)
-      for (int i = 0; i < n; ++i) p.heads[i] = (int16_t)(all ? h0 + i : heads[h0 + i]);
-    const int64_t per = mode == MODE_BLOCKS ? (int64_t)p.nqb * p.q_sub : p.n_qtiles;
-    const int64_t items = per * n;
+      for (int i = 0; i < n; ++i) p.heads[i] = (uint16_t)(all ? h0 + i : heads[h0 + i]);
+    const int64_t items = (int64_t)p.nqb * p.q_sub * n;
     if (items > 0x7FFFFFFF) return fail(CA_ERANGE, "too many work items");
     p.n_items = (int)items;
-    const hipError_t e = launch_attention(mode, c.d, nwaves, c.o_dtype == CA_F32, p, stream);
+    const hipError_t e = launch_attention(MODE_BLOCKS, c.d, nwaves, c.o_dtype == CA_F32, p, stream);
     if (e != hipSuccess) return launched(e, "chunk attention launch");
   }
   return ok();
+}
+
+// Bytes of the balanced schedule's partials for `slots` workgroups.
+size_t workspace_bytes(int slots, int d) {
+  return (size_t)2 * slots * kRangeRows * (d + 1) * sizeof(float);
+}
+
+// Range mode over a list of head words (b*H + h, | kFlatHead for heads that
+// read the flat buffers).  tiles[i] (host) is head i's key-tile count when
+// known (empty vector: unknown).  With a workspace and known tile counts a
+// launch takes the balanced schedule when that shortens it: the plain grid
+// runs one workgroup per (head, query tile), so its length is set by the
+// longest head and by how many rounds of workgroups the device needs; the
+// balanced grid gives every resident workgroup the same number of key tiles.
+int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& words,
+                 const std::vector<int>& tiles, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int nh = (int)words.size();
+  p.n_qtiles = (c.Nq + kRangeRows - 1) / kRangeRows;
+  const int slots = ws ? attention_slots(c.d) : 0;
+  for (int h0 = 0; h0 < nh;) {
+    int n = std::min(kMaxHeadsPerLaunch, nh - h0);
+    p.sched = 0;
+    if (slots > 0 && !tiles.empty() && !p.o_init) {
+      const int ns = std::min(n, kMaxSchedHeads);
+      int64_t tsum = 0;
+      int max_nt = 0;
+      for (int i = 0; i < ns; ++i) {
+        tsum += std::max(1, tiles[h0 + i]);
+        max_nt = std::max(max_nt, tiles[h0 + i]);
+      }
+      const int64_t units = tsum * p.n_qtiles;
+      const int64_t items = (int64_t)ns * p.n_qtiles;
+      const int64_t g = std::min<int64_t>(slots, units / kMinUnitsPerWg);
+      const int64_t est_plain = (items + slots - 1) / slots * (int64_t)max_nt;
+      const int64_t est_bal = g > 0 ? (units + g - 1) / g + 2 : INT64_MAX;
+      // (the merge grid has 16 workgroups per query tile; keep it in range)
+      if (units <= 0x7FFFFFFF && items * 16 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 &&
+          est_bal * 20 < est_plain * 19) {
+        if (ws_bytes < workspace_bytes((int)g, c.d))
+          return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                      ws_bytes, workspace_bytes((int)g, c.d));
+        n = ns;
+        p.sched = 1;
+        p.n_units = (int)units;
+        p.n_wgs = (int)g;
+        p.ws = static_cast<float*>(ws);
+        p.tprefix[0] = 0;
+        for (int i = 0; i < ns; ++i) p.tprefix[i + 1] = p.tprefix[i] + std::max(1, tiles[h0 + i]);
+      }
+    }
+    if ((int64_t)n * p.n_qtiles > 0x7FFFFFFF) return fail(CA_ERANGE, "too many work items");
+    p.n_heads = n;
+    p.use_list = 1;
+    for (int i = 0; i < n; ++i) p.heads[i] = words[h0 + i];
+    p.n_items = n * p.n_qtiles;
+    hipError_t e = launch_attention(MODE_RANGE, c.d, kDenseWaves, c.o_dtype == CA_F32, p, stream);
+    if (e != hipSuccess) return launched(e, "chunk attention launch");
+    if (p.sched) {
+      e = launch_split_merge(c.d, c.o_dtype == CA_F32, p, stream);
+      if (e != hipSuccess) return launched(e, "split merge launch");
+    }
+    h0 += n;
+  }
+  return ok();
+}
+
+int check_workspace(const void* ws, size_t ws_bytes) {
+  if (ws && !aligned16(ws)) return fail(CA_EINVAL, "workspace must be 16-byte aligned");
+  if (!ws && ws_bytes) return fail(CA_EINVAL, "workspace_bytes given without a workspace");
+  return CA_OK;
 }
 
 int check_csr(const int32_t* indptr, const int32_t* indices, int nnz, int kv_block, int kv_seg,
@@ -193,15 +257,23 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len) {
   return num_blocks(n_tokens, block_size, seg_len);
 }
 
+size_t ca_attn_workspace_bytes(int d) {
+  if (d != 64 && d != 128) return 0;
+  if (check_device() != CA_OK) return 0;
+  return workspace_bytes(attention_slots(d), d);
+}
+
 int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv,
                       int d, const int64_t* q_strides, const int64_t* kv_strides,
                       const int64_t* o_strides, const int32_t* kv_indptr,
                       const int32_t* kv_indices, int kv_nnz, int kv_block, int kv_seg,
                       int q_block, int q_seg, float scale, const float* o_init,
                       const int64_t* o_init_strides, const float* lse_init, void* o,
-                      int o_dtype, float* lse, void* stream) {
+                      int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
+  if (int r = check_workspace(workspace, workspace_bytes)) return r;
   if ((o_init == nullptr) != (lse_init == nullptr))
     return fail(CA_EINVAL, "o_init and lse_init must be given together");
   if (o_init) {
@@ -236,18 +308,24 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
   }
   if (blocks) {
     fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
-    return launch_heads(MODE_BLOCKS, c, p, {}, static_cast<hipStream_t>(stream));
+    return launch_blocks(c, p, {}, static_cast<hipStream_t>(stream));
   }
-  return launch_heads(MODE_DENSE, c, p, {}, static_cast<hipStream_t>(stream));
+  std::vector<uint16_t> words(B * H);
+  std::iota(words.begin(), words.end(), 0);
+  const std::vector<int> tiles(Nkv > 0 ? B * H : 0, (Nkv + kTileKeys - 1) / kTileKeys);
+  return launch_range(c, p, words, tiles, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
 }
 
 int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_flat,
                              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                              int total_kv, int B, int H, int Nq, int d, const int64_t* q_strides,
                              int64_t kv_row_stride, const int64_t* o_strides, float scale,
-                             void* o, int o_dtype, float* lse, void* stream) {
+                             void* o, int o_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
+  if (int r = check_workspace(workspace, workspace_bytes)) return r;
   if (!cu_seqlens) return fail(CA_EINVAL, "cu_seqlens must be non-NULL");
   if (total_kv > 0 && (!k_flat || !v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be non-NULL");
   if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
@@ -265,18 +343,26 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
   static thread_local AttnParams p;
   p = AttnParams{};
   fill_common(p, c);
-  p.k = static_cast<const uint16_t*>(k_flat);
-  p.v = static_cast<const uint16_t*>(v_flat);
-  p.ks_b = 0; p.ks_n = kv_row_stride; p.ks_h = 0;
+  p.kf = static_cast<const uint16_t*>(k_flat);
+  p.vf = static_cast<const uint16_t*>(v_flat);
+  p.kfs_n = kv_row_stride;
   p.cu = cu_seqlens;
   p.total_kv = total_kv;
-  std::vector<int> heads;
+  std::vector<int> all(B * H);
+  std::iota(all.begin(), all.end(), 0);
+  std::vector<uint16_t> words;
+  std::vector<int> tiles;
   if (cu_seqlens_host) {
-    std::vector<int> all(B * H);
-    std::iota(all.begin(), all.end(), 0);
-    heads = longest_first(cu_seqlens_host, all);
+    // longest heads first, so that the plain grid starts the long ones first
+    for (int bh : longest_first(cu_seqlens_host, all)) {
+      words.push_back((uint16_t)(bh | kFlatHead));
+      tiles.push_back((cu_seqlens_host[bh + 1] - cu_seqlens_host[bh] + kTileKeys - 1) / kTileKeys);
+    }
+  } else {
+    for (int bh : all) words.push_back((uint16_t)(bh | kFlatHead));
   }
-  return launch_heads(MODE_VARLEN, c, p, heads, static_cast<hipStream_t>(stream));
+  return launch_range(c, p, words, tiles, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
 }
 
 int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq,
@@ -286,9 +372,11 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
                             int kv_block, int kv_seg, int q_block, int q_seg,
                             const void* k_flat, const void* v_flat, const int32_t* cu_seqlens,
                             const int32_t* cu_seqlens_host, int total_kv, int64_t kv_row_stride,
-                            float scale, void* o, int o_dtype, float* lse, void* stream) {
+                            float scale, void* o, int o_dtype, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
+  if (int r = check_workspace(workspace, workspace_bytes)) return r;
   if (!head_mode) return fail(CA_EINVAL, "head_mode is NULL");
   std::vector<int> hd, hb, hv;
   for (int i = 0; i < B * H; ++i) {
@@ -320,25 +408,36 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
   if ((int64_t)B * H * Nq == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   static thread_local AttnParams p;
-  if (!hv.empty()) {
-    p = AttnParams{};
-    fill_common(p, c);
-    p.k = static_cast<const uint16_t*>(k_flat);
-    p.v = static_cast<const uint16_t*>(v_flat);
-    p.ks_n = kv_row_stride;
-    p.cu = cu_seqlens;
-    p.total_kv = total_kv;
-    if (cu_seqlens_host) hv = longest_first(cu_seqlens_host, hv);
-    if (int r = launch_heads(MODE_VARLEN, c, p, hv, s)) return r;
-  }
-  if (!hd.empty()) {
+  if (!hd.empty() || !hv.empty()) {
+    // dense and ragged heads both attend to one contiguous token range: one
+    // range-mode launch covers them, each head reading its own source
     p = AttnParams{};
     fill_common(p, c);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
-    p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+    if (!hd.empty()) {
+      p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+    }
     p.Nkv = Nkv;
-    if (int r = launch_heads(MODE_DENSE, c, p, hd, s)) return r;
+    p.kf = static_cast<const uint16_t*>(k_flat);
+    p.vf = static_cast<const uint16_t*>(v_flat);
+    p.kfs_n = kv_row_stride;
+    p.cu = cu_seqlens;
+    p.total_kv = total_kv;
+    std::vector<uint16_t> words;
+    std::vector<int> tiles;
+    const bool known = hv.empty() || cu_seqlens_host;
+    for (int bh : hd) {
+      words.push_back((uint16_t)bh);
+      if (known) tiles.push_back((Nkv + kTileKeys - 1) / kTileKeys);
+    }
+    if (cu_seqlens_host) hv = longest_first(cu_seqlens_host, hv);
+    for (int bh : hv) {
+      words.push_back((uint16_t)(bh | kFlatHead));
+      if (known)
+        tiles.push_back((cu_seqlens_host[bh + 1] - cu_seqlens_host[bh] + kTileKeys - 1) / kTileKeys);
+    }
+    if (int r = launch_range(c, p, words, tiles, workspace, workspace_bytes, s)) return r;
   }
   if (!hb.empty()) {
     p = AttnParams{};
@@ -348,7 +447,7 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
     p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
     p.Nkv = Nkv;
     fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
-    if (int r = launch_heads(MODE_BLOCKS, c, p, hb, s)) return r;
+    if (int r = launch_blocks(c, p, hb, s)) return r;
   }
   return ok();
 }

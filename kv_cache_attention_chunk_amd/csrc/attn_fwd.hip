@@ -181,11 +181,47 @@ void attn_fwd_kernel(const AttnParams p) {
   const int col = lane & 31;      // query column (B/C operands) or A-operand row
   const int hg = lane >> 5;       // lane half: selects k sub-range / row quad
 
-  // ---- work item ---------------------------------------------------------
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  if (item >= p.n_items) return;
-  int sel, row0, nrows, csr_row = 0;
+  // ---- work decomposition ----------------------------------------------------
+  // Each pass of the loop below runs one segment: query rows [row0, row0 +
+  // nrows) of launch-local head `sel` against key tiles [kt0, kt1) of its key
+  // set (range mode; kt1 < 0 = every tile) or its CSR row (block mode).
+  // slot < 0 writes the final O and LSE; slot >= 0 the float32 partial state
+  // into workspace slot `slot`.  Block mode and the plain grid run one
+  // segment per workgroup; the balanced schedule runs the workgroup's unit
+  // range as consecutive segments.
+  //
+  // Segment order under the balanced schedule: every segment of a range
+  // starts at key tile 0 except possibly the first, which continues a query
+  // tile begun by the previous workgroup.  That one runs last, so that each
+  // workgroup walks its head's keys in ascending order: the workgroups
+  // sharing a head then read the same few key tiles at any moment (shared
+  // through L2) instead of tiles spread over the whole cache.
+  int u_cur = 0, u_end = 0, u_first = 0, first_end = 0, head_i = 0, head_first = 0, g_self = 0;
+  int deferred = 0;     // 1: the first segment is still to run, at the end
+  if (MODE == MODE_RANGE && p.sched) {
+    g_self = xcd_remap(blockIdx.x, gridDim.x);
+    u_first = unit_begin(g_self, p.n_units, p.n_wgs);
+    u_end = unit_begin(g_self + 1, p.n_units, p.n_wgs);
+    // head holding u_first (binary search over the prefix)
+    int lo = 0, hi = p.n_heads - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.n_qtiles * p.tprefix[mid + 1] <= u_first) lo = mid + 1; else hi = mid;
+    }
+    const int nt = p.tprefix[lo + 1] - p.tprefix[lo];
+    const int rel = u_first - p.n_qtiles * p.tprefix[lo];
+    const int k0 = rel % nt;
+    first_end = u_first + (nt - k0 < u_end - u_first ? nt - k0 : u_end - u_first);
+    // a first segment that starts mid-tile and is not the whole range runs last
+    deferred = k0 != 0 && first_end < u_end;
+    u_cur = deferred ? first_end : u_first;
+    head_i = head_first = lo;
+  }
+  for (;;) {
+  int sel, row0, nrows, csr_row = 0, kt0 = 0, kt1 = -1, slot = -1;
   if (MODE == MODE_BLOCKS) {
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= p.n_items) return;
     const int per_head = p.nqb * p.q_sub;
     sel = item / per_head;
     const int rem = item - sel * per_head;
@@ -197,38 +233,67 @@ void attn_fwd_kernel(const AttnParams p) {
     nrows = ql - st * BM;
     if (nrows <= 0) return;
     if (nrows > BM) nrows = BM;
-    const int bh_ = p.use_list ? p.heads[sel] : sel;
+    const int bh_ = (p.use_list ? p.heads[sel] : sel) & 0x7FFF;
     csr_row = bh_ * p.nqb + qb;
-  } else {
+  } else if (!p.sched) {
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= p.n_items) return;
     sel = item / p.n_qtiles;
     const int qt = item - sel * p.n_qtiles;
     row0 = qt * BM;
     nrows = p.Nq - row0;
     if (nrows > BM) nrows = BM;
+  } else {
+    if (u_cur >= u_end) {
+      if (!deferred) return;
+      deferred = 0;
+      u_cur = u_first;
+      u_end = first_end;
+      head_i = head_first;
+    }
+    while (p.n_qtiles * p.tprefix[head_i + 1] <= u_cur) ++head_i;
+    sel = head_i;
+    const int nt = p.tprefix[head_i + 1] - p.tprefix[head_i];
+    const int rel = u_cur - p.n_qtiles * p.tprefix[head_i];
+    const int qt = rel / nt;
+    kt0 = rel - qt * nt;
+    kt1 = nt - kt0 < u_end - u_cur ? nt : kt0 + (u_end - u_cur);
+    u_cur += kt1 - kt0;
+    if (kt0 != 0 || kt1 != nt) slot = u_cur - (kt1 - kt0) == u_first ? 2 * g_self : 2 * g_self + 1;
+    row0 = qt * BM;
+    nrows = p.Nq - row0;
+    if (nrows > BM) nrows = BM;
   }
-  const int bh = p.use_list ? p.heads[sel] : sel;
+  const int hword = p.use_list ? p.heads[sel] : sel;
+  const int bh = hword & 0x7FFF;
+  const bool flat = p.use_list ? (hword & kFlatHead) != 0 : p.all_flat != 0;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
 
   // ---- key set -------------------------------------------------------------
   int ntiles;
   int kv_lo = 0, kv_len = 0, list0 = 0;
+  int64_t kstride;
   const uint16_t* kh;
   const uint16_t* vh;
-  if (MODE == MODE_DENSE) {
-    kv_len = p.Nkv;
-    ntiles = (kv_len + kTileKeys - 1) / kTileKeys;
-    kh = p.k + b * p.ks_b + h * p.ks_h;
-    vh = p.v + b * p.ks_b + h * p.ks_h;
-  } else if (MODE == MODE_VARLEN) {
-    int lo = p.cu[bh], hi = p.cu[bh + 1];
-    lo = lo < 0 ? 0 : (lo > p.total_kv ? p.total_kv : lo);
-    hi = hi < lo ? lo : (hi > p.total_kv ? p.total_kv : hi);
-    kv_lo = lo;
-    kv_len = hi - lo;
-    ntiles = (kv_len + kTileKeys - 1) / kTileKeys;
-    kh = p.k;
-    vh = p.v;
+  if (MODE == MODE_RANGE) {
+    if (flat) {
+      int lo = p.cu[bh], hi = p.cu[bh + 1];
+      lo = lo < 0 ? 0 : (lo > p.total_kv ? p.total_kv : lo);
+      hi = hi < lo ? lo : (hi > p.total_kv ? p.total_kv : hi);
+      kv_lo = lo;
+      kv_len = hi - lo;
+      kh = p.kf;
+      vh = p.vf;
+      kstride = p.kfs_n;
+    } else {
+      kv_len = p.Nkv;
+      kh = p.k + b * p.ks_b + h * p.ks_h;
+      vh = p.v + b * p.ks_b + h * p.ks_h;
+      kstride = p.ks_n;
+    }
+    if (kt1 < 0) kt1 = (kv_len + kTileKeys - 1) / kTileKeys;
+    ntiles = kt1 - kt0;
   } else {
     int lo = p.indptr[csr_row], hi = p.indptr[csr_row + 1];
     lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
@@ -237,11 +302,15 @@ void attn_fwd_kernel(const AttnParams p) {
     ntiles = hi - lo;
     kh = p.k + b * p.ks_b + h * p.ks_h;
     vh = p.v + b * p.ks_b + h * p.ks_h;
+    kstride = p.ks_n;
   }
 
   // tile t -> (element offset of its row 0, number of valid rows).  Called
   // for t = 0, 1, 2, ... in order; in block mode each call also fetches the
-  // next tile's block id, so that its latency overlaps one iteration.
+  // next tile's block id, so that its latency overlaps one iteration.  In
+  // range mode tile t covers keys [(kt0 + t) 64, +64) of the key set; a tile
+  // past its end (possible only when the schedule's tile count exceeds the
+  // device-side span) has no valid rows.
   int id_next = (MODE == MODE_BLOCKS && ntiles > 0) ? ld_uniform(p.indices, list0) : 0;
   auto tile_src = [&](int t, int64_t& off, int& len) {
     if (MODE == MODE_BLOCKS) {
@@ -250,17 +319,18 @@ void attn_fwd_kernel(const AttnParams p) {
       int s0 = 0, l0 = 0;
       if (id >= 0 && id < p.nkb)
         block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0, p.kv_bps_magic);
-      off = (int64_t)s0 * p.ks_n;
+      off = (int64_t)s0 * kstride;
       len = l0;
     } else {
-      const int s0 = t * kTileKeys;
+      int s0 = (kt0 + t) * kTileKeys;
+      s0 = s0 < kv_len ? s0 : kv_len;
       const int rest = kv_len - s0;
-      off = (int64_t)(kv_lo + s0) * p.ks_n;
+      off = (int64_t)(kv_lo + s0) * kstride;
       len = rest < kTileKeys ? rest : kTileKeys;
     }
   };
 
-  const uint32_t stride_bytes = (uint32_t)(p.ks_n * 2);
+  const uint32_t stride_bytes = (uint32_t)(kstride * 2);
   TileLoader<D, NW> ldr;
   ldr.init(lane, wave, stride_bytes);
 
@@ -546,7 +616,23 @@ void attn_fwd_kernel(const AttnParams p) {
   // ---- epilogue --------------------------------------------------------------
   const float lt = half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qvalid) {
+  const float lse_row = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  if (qvalid && slot >= 0) {
+    // partial state of a split query tile: O / l and LSE, float32
+    float* part = p.ws + (int64_t)slot * BM * (D + 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * dt + 8 * r + 4 * hg;
+        f32x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
+        *reinterpret_cast<f32x4_t*>(part + qr * D + d0) = v4;
+      }
+    }
+    if (hg == 0) part[BM * D + qr] = lse_row;
+  } else if (qvalid) {
     const int64_t obase = b * p.os_b + (int64_t)qrow * p.os_n + h * p.os_h;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -565,14 +651,102 @@ void attn_fwd_kernel(const AttnParams p) {
         }
       }
     }
-    if (hg == 0)
-      p.lse[(int64_t)bh * p.Nq + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    if (hg == 0) p.lse[(int64_t)bh * p.Nq + qrow] = lse_row;
   }
+  if (MODE == MODE_BLOCKS || !p.sched) return;
+  }   // segment loop
+}
+
+// Final O and LSE of the query tiles that the balanced schedule split across
+// workgroups: the LSE merge of their partial states (the decomposition of
+// the ISPA page, section 2 item 1, over consecutive key ranges):
+// M = max_s LSE_s, w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s,
+// LSE = M + ln sum_s w_s; every part empty -> O = 0, LSE = -inf.
+// One workgroup per (query tile, group of 1024/D rows), one thread per
+// 4-float chunk of a row; tiles written whole by one workgroup exit at once.
+// The parts' LSE values and O chunks are all loaded before they are used
+// (up to kMergeFast parts; more parts take a second, looped pass).
+constexpr int kMergeFast = 4;
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p) {
+  constexpr int BM = kRangeRows;
+  constexpr int C4 = D / 4;                  // float4 chunks per row
+  constexpr int RPW = 256 / C4;              // rows per workgroup
+  constexpr int GPT = BM / RPW;              // row groups per query tile
+  const int item = blockIdx.x / GPT;         // launch-local head * n_qtiles + query tile
+  const int rg = blockIdx.x - item * GPT;
+  const int sel = item / p.n_qtiles;
+  const int qt = item - sel * p.n_qtiles;
+  const int nt = p.tprefix[sel + 1] - p.tprefix[sel];
+  const int u0 = p.n_qtiles * p.tprefix[sel] + qt * nt;
+  const int g0 = g_of_unit(u0, p.n_units, p.n_wgs);
+  const int g1 = g_of_unit(u0 + nt - 1, p.n_units, p.n_wgs);
+  if (g0 == g1) return;
+  const int row0 = qt * BM;
+  const int r = rg * RPW + (int)threadIdx.x / C4;
+  const int c = (int)threadIdx.x % C4;
+  if (row0 + r >= p.Nq) return;
+  const int hword = p.use_list ? p.heads[sel] : sel;
+  const int bh = hword & 0x7FFF;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  // the tile is the last segment of g0 when g0's range starts before it,
+  // else g0's first; it is the first segment of every later workgroup
+  const int slot0 = unit_begin(g0, p.n_units, p.n_wgs) < u0 ? 2 * g0 + 1 : 2 * g0;
+  const int np = g1 - g0 + 1;
+  auto part = [&](int j) {
+    return p.ws + (int64_t)(j == 0 ? slot0 : 2 * (g0 + j)) * BM * (D + 1);
+  };
+  float ls[kMergeFast];
+  f32x4_t xs[kMergeFast];
+#pragma unroll
+  for (int j = 0; j < kMergeFast; ++j) {
+    if (j < np) {
+      const float* pp = part(j);
+      ls[j] = pp[BM * D + r];
+      xs[j] = *reinterpret_cast<const f32x4_t*>(pp + r * D + 4 * c);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMergeFast; ++j)
+    if (j < np) M = fmaxf(M, ls[j]);
+  for (int j = kMergeFast; j < np; ++j) M = fmaxf(M, part(j)[BM * D + r]);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kMergeFast; ++j) {
+      if (j < np) {
+        const float w = expf(ls[j] - M);
+        wsum += w;
+        acc += w * xs[j];
+      }
+    }
+    for (int j = kMergeFast; j < np; ++j) {
+      const float* pp = part(j);
+      const float w = expf(pp[BM * D + r] - M);
+      wsum += w;
+      acc += w * *reinterpret_cast<const f32x4_t*>(pp + r * D + 4 * c);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  acc *= inv;
+  const int64_t obase = b * p.os_b + (int64_t)(row0 + r) * p.os_n + h * p.os_h + 4 * c;
+  if (OF32) {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.o) + obase) = acc;
+  } else {
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+    *reinterpret_cast<bf16x4_t*>(reinterpret_cast<uint16_t*>(p.o) + obase) =
+        __builtin_convertvector(acc, bf16x4_t);
+  }
+  if (c == 0) p.lse[(int64_t)bh * p.Nq + row0 + r] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
 template <int D, int NW, int MODE>
 hipError_t launch_t(bool of32, const AttnParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_items), block(NW * 64);
+  const dim3 grid(MODE == MODE_RANGE && p.sched ? p.n_wgs : p.n_items), block(NW * 64);
   if (of32)
     hipLaunchKernelGGL((attn_fwd_kernel<D, NW, MODE, true>), grid, block, 0, stream, p);
   else
@@ -580,19 +754,23 @@ hipError_t launch_t(bool of32, const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int NW>
-hipError_t launch_mode(int mode, bool of32, const AttnParams& p, hipStream_t stream) {
-  switch (mode) {
-    case MODE_DENSE: return launch_t<D, NW, MODE_DENSE>(of32, p, stream);
-    case MODE_BLOCKS: return launch_t<D, NW, MODE_BLOCKS>(of32, p, stream);
-    default: return launch_t<D, NW, MODE_VARLEN>(of32, p, stream);
-  }
+template <int D>
+hipError_t launch_d(int mode, int nwaves, bool of32, const AttnParams& p, hipStream_t stream) {
+  if (mode == MODE_RANGE) return launch_t<D, 4, MODE_RANGE>(of32, p, stream);
+  return nwaves == 2 ? launch_t<D, 2, MODE_BLOCKS>(of32, p, stream)
+                     : launch_t<D, 4, MODE_BLOCKS>(of32, p, stream);
 }
 
 template <int D>
-hipError_t launch_d(int mode, int nwaves, bool of32, const AttnParams& p, hipStream_t stream) {
-  return nwaves == 2 ? launch_mode<D, 2>(mode, of32, p, stream)
-                     : launch_mode<D, 4>(mode, of32, p, stream);
+int slots_d() {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per, reinterpret_cast<const void*>(&attn_fwd_kernel<D, 4, MODE_RANGE, false>),
+          4 * 64, 0) != hipSuccess)
+    return 0;
+  return cus * per;
 }
 
 }  // namespace
@@ -602,6 +780,34 @@ hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32, const Att
   if (p.n_items <= 0) return hipSuccess;
   return d == 64 ? launch_d<64>(mode, nwaves, out_f32, p, stream)
                  : launch_d<128>(mode, nwaves, out_f32, p, stream);
+}
+
+hipError_t launch_split_merge(int d, bool out_f32, const AttnParams& p, hipStream_t stream) {
+  const int64_t items = (int64_t)p.n_heads * p.n_qtiles;
+  if (items <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(items * (kRangeRows / (1024 / d)))), block(256);
+  if (d == 64) {
+    if (out_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<64, false>), grid, block, 0, stream, p);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_merge_kernel<128, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+int attention_slots(int d) {
+  // per device and head dim, computed once
+  static int cache[2][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int di = d == 64 ? 0 : 1;
+  int v = __atomic_load_n(&cache[di][dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    v = d == 64 ? slots_d<64>() : slots_d<128>();
+    __atomic_store_n(&cache[di][dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
 }
 
 }  // namespace chunkattn

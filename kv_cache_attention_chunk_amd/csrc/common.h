@@ -16,10 +16,17 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-enum Mode { MODE_DENSE = 0, MODE_BLOCKS = 1, MODE_VARLEN = 2 };
+// Key-set modes of the attention kernel.  MODE_RANGE: each head attends to a
+// contiguous token range, either all Nkv tokens of the dense cache or its span
+// [cu[bh], cu[bh+1]) of the flat ragged buffers.  MODE_BLOCKS: each query
+// block attends to the blocks listed in its CSR row.
+enum Mode { MODE_RANGE = 0, MODE_BLOCKS = 1 };
 
 constexpr int kMaxHeadsPerLaunch = 1024;
-constexpr int kTileKeys = 64;     // keys per KV tile (and max KV block size)
+constexpr int kMaxSchedHeads = 256;   // heads of one launch under the balanced schedule
+constexpr int kTileKeys = 64;         // keys per KV tile (and max KV block size)
+constexpr int kRangeRows = 128;       // query rows per workgroup in range mode
+constexpr uint16_t kFlatHead = 0x8000;  // heads[] flag: the head reads the flat buffers
 
 // Kernel arguments of the fused attention kernel (passed by value).
 struct AttnParams {
@@ -43,20 +50,53 @@ struct AttnParams {
   int kv_block, kv_seg, kv_bps, nkb;
   uint32_t kv_bps_magic;      // floor(2^32 / kv_bps): id / kv_bps by multiply-high
   int q_block, q_seg, q_bps, nqb, q_sub;
-  // ragged mode
+  // flat ragged buffers (range mode): head bh owns rows [cu[bh], cu[bh+1])
+  const uint16_t* kf;
+  const uint16_t* vf;
+  int64_t kfs_n;              // row stride of the flat buffers, elements
   const int32_t* cu;
   int total_kv;
+  int all_flat;               // use_list == 0: every head reads the flat buffers
   // work decomposition
-  int n_qtiles;               // query tiles per head (dense / ragged)
+  int n_qtiles;               // query tiles per head (range mode)
   int n_items;                // logical work items of this launch
   int n_heads;                // heads covered by this launch
-  int use_list;               // heads[] maps launch-local head -> b*H + h
-  int16_t heads[kMaxHeadsPerLaunch];
+  int use_list;               // heads[] maps launch-local head -> b*H + h (| kFlatHead)
+  // Balanced schedule (range mode, sched = 1): the launch's work is
+  // n_units = n_qtiles * tprefix[n_heads] units of one (query tile, key tile)
+  // pair, ordered head, query tile, key tile; head i has tprefix[i+1] -
+  // tprefix[i] >= 1 key tiles.  Workgroup g (of n_wgs) takes units
+  // [g*n_units/n_wgs, (g+1)*n_units/n_wgs).  A query tile whose units fall to
+  // more than one workgroup is written as float32 partials (O / l, LSE) into
+  // ws: slot 2g holds a workgroup's first segment, slot 2g+1 its last; each
+  // slot is kRangeRows x d floats of O followed by kRangeRows LSE values.
+  int sched;
+  int n_units;
+  int n_wgs;
+  float* ws;
+  int32_t tprefix[kMaxSchedHeads + 1];
+  uint16_t heads[kMaxHeadsPerLaunch];
 };
+
+// First unit of workgroup g under the balanced schedule, and the workgroup
+// that owns unit u (exact integer forms: g_of_unit(u) = g iff
+// unit_begin(g) <= u < unit_begin(g + 1), for 1 <= n_wgs <= n_units).
+__host__ __device__ __forceinline__ int unit_begin(int g, int n_units, int n_wgs) {
+  return (int)(((int64_t)g * n_units) / n_wgs);
+}
+__host__ __device__ __forceinline__ int g_of_unit(int u, int n_units, int n_wgs) {
+  return (int)((((int64_t)u + 1) * n_wgs - 1) / n_units);
+}
 
 // Launchers implemented in attn_fwd.hip / select.hip / merge.hip.
 hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32,
                             const AttnParams& p, hipStream_t stream);
+// Combines the float32 partials of the query tiles the balanced schedule
+// split across workgroups (runs after launch_attention on the same stream).
+hipError_t launch_split_merge(int d, bool out_f32, const AttnParams& p, hipStream_t stream);
+// Workgroups of the range-mode attention kernel resident on the whole device
+// at once (0 on failure).
+int attention_slots(int d);
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
                              const int64_t* xs, int block, int seg, int bps, int nb,
                              float* out, float* out_total, hipStream_t stream);
