@@ -177,6 +177,15 @@ def per_config(reps=10, wan=None):
     kvb = 2.0 * w.Nkv * w.H * w.d * 2
     out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps), f, kvb)
     out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
+    # local (sink + chunk frames) and full attention from one pass over each head's list
+    row = np.array(w.meta["local_blocks"] + w.meta["history_blocks"], np.int32)
+    dip, dix = i32(np.arange(w.B * w.H + 1) * len(row)), i32(np.tile(row, w.B * w.H))
+    n_loc = len(w.meta["local_blocks"])
+    f_loc = 4.0 * w.d * w.Nq * w.B * w.H * float(_block_len(w.meta["local_blocks"]).sum())
+    out["wan_dual_output"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_dual_fwd(
+        q, k, v, dip, dix, n_loc, kv_block=64, kv_seg=1560, q_block=w.Nq, q_seg=w.Nq,
+        scale=w.scale, out_dtype=torch.float32), reps), f, kvb,
+        local_gflop_shared=round(f_loc / 1e9, 2))
     # block-sparse path at the three top-K ratios (selection included)
     km = ca.block_mean(k, 64, 1560)
     nqb = ca.num_blocks(w.Nq, 64, 1560)

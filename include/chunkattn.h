@@ -139,6 +139,30 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dual-output chunk attention (ISPA page, section 2 item 1: the dual-stream
+ * warmup computes attention over the local tokens — the current frames and
+ * the sink — and over the full history side by side).  Block-list mode as in
+ * ca_chunk_attn_fwd, where the first local_count ids of every CSR row form
+ * the local key set and the whole row the full key set.  One pass over each
+ * row writes both:
+ *   o_local, lse_local  attention over the row's first local_count blocks
+ *                       (all of them when the row is shorter; an empty local
+ *                       set gives O = 0, LSE = -inf)
+ *   o, lse              attention over the whole row
+ *   o_local             [B, Nq, H, d] of o_dtype, strides o_local_strides (host);
+ *                       lse_local float32 [B, H, Nq].  Neither may alias o, lse.
+ * Other arguments as in ca_chunk_attn_fwd (no o_init, no workspace).
+ */
+int ca_chunk_attn_dual_fwd(const void* q, const void* k, const void* v,
+                           int B, int H, int Nq, int Nkv, int d,
+                           const int64_t* q_strides, const int64_t* kv_strides,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
+                           int kv_block, int kv_seg, int q_block, int q_seg, int local_count,
+                           float scale, void* o_local, const int64_t* o_local_strides,
+                           float* lse_local, void* o, const int64_t* o_strides, int o_dtype,
+                           float* lse, void* stream);
+
+/*
  * Chunk attention over ragged per-head caches (Pyramid Forcing page, section
  * 3, ragged-cache attention): head (b, h) owns rows
  * [cu_seqlens[b*H+h], cu_seqlens[b*H+h+1]) of the flat K/V buffers, no padding.

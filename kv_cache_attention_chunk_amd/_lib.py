@@ -34,6 +34,9 @@ SIGNATURES = {
     "ca_chunk_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
                                _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i64p, _p,
                                _p, _i, _p, _p, _sz, _p]),
+    "ca_chunk_attn_dual_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i32p, _i32p,
+                                    _i, _i, _i, _i, _i, _i, _f, _p, _i64p, _p, _p, _i64p, _i,
+                                    _p, _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
                                       _i64p, _i64, _i64p, _f, _p, _i, _p, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,

@@ -170,6 +170,36 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return o, l
 
 
+def chunk_attn_dual_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        kv_indptr: torch.Tensor, kv_indices: torch.Tensor, local_count: int, *,
+                        kv_block: int = 64, kv_seg: Optional[int] = None, q_block: int = 64,
+                        q_seg: Optional[int] = None, scale: Optional[float] = None,
+                        out_dtype=torch.bfloat16):
+    """One pass over each CSR row giving attention over the row's first
+    local_count blocks (the local branch: sink + current frames) and over
+    the whole row (full attention).  Returns (o_local, lse_local, o, lse)."""
+    _bshd("q", q), _bshd("k", k), _bshd("v", v)
+    B, Nq, H, d = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, d) or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k, v must be [B, Nkv, H, d] matching q, with equal strides")
+    _i32("kv_indptr", kv_indptr), _i32("kv_indices", kv_indices)
+    _check_indptr(kv_indptr, B * H, Nq, q_block, q_seg)
+    ol = _out(B, Nq, H, d, out_dtype, q.device, None)
+    ll = _lse_out(B, H, Nq, q.device, None)
+    o = _out(B, Nq, H, d, out_dtype, q.device, None)
+    l = _lse_out(B, H, Nq, q.device, None)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().ca_chunk_attn_dual_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d, _st(q), _st(k),
+        kv_indptr.data_ptr(), kv_indices.data_ptr(), kv_indices.numel(), kv_block,
+        kv_seg or max(Nkv, 1), q_block, q_seg or max(Nq, 1), int(local_count), sc,
+        ol.data_ptr(), _st(ol), ll.data_ptr(), o.data_ptr(), _st(o), _DT[out_dtype],
+        l.data_ptr(), _stream())
+    check(st)
+    return ol, ll, o, l
+
+
 def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.Tensor,
                           cu_seqlens: torch.Tensor, *, cu_seqlens_host: Optional[np.ndarray] = None,
                           scale: Optional[float] = None, out_dtype=None,

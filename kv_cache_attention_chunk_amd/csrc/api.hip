@@ -93,6 +93,7 @@ int check_common(const Common& c) {
 }
 
 void fill_common(AttnParams& p, const Common& c) {
+  p.snap = -1;
   p.q = static_cast<const uint16_t*>(c.q);
   p.o = c.o;
   p.lse = c.lse;
@@ -315,6 +316,43 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
   const std::vector<int> tiles(Nkv > 0 ? B * H : 0, (Nkv + kTileKeys - 1) / kTileKeys);
   return launch_range(c, p, words, tiles, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream));
+}
+
+int ca_chunk_attn_dual_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq,
+                           int Nkv, int d, const int64_t* q_strides, const int64_t* kv_strides,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
+                           int kv_block, int kv_seg, int q_block, int q_seg, int local_count,
+                           float scale, void* o_local, const int64_t* o_local_strides,
+                           float* lse_local, void* o, const int64_t* o_strides, int o_dtype,
+                           float* lse, void* stream) {
+  Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
+  if (int r = check_common(c)) return r;
+  if (local_count < 0) return fail(CA_EINVAL, "local_count < 0");
+  if (!o_local || !lse_local) return fail(CA_EINVAL, "o_local and lse_local must be non-NULL");
+  if (!aligned16(o_local) || !aligned16(lse_local)) return fail(CA_EINVAL, "o_local, lse_local must be 16-byte aligned");
+  if (int r = check_strides("o_local", o_local_strides, o_dtype == CA_BF16 ? 8 : 4)) return r;
+  if (o_local == o || lse_local == lse) return fail(CA_EINVAL, "local and full outputs must not alias");
+  if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
+  if (Nkv > 0 && (!k || !v)) return fail(CA_EINVAL, "k and v must be non-NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
+  if (int r = check_strides("kv", kv_strides, 8)) return r;
+  if (kv_strides[1] < d || kv_strides[1] > (1 << 23)) return fail(CA_ERANGE, "kv row stride outside [d, 2^23]");
+  if (int r = check_csr(kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+  if (int r = check_device()) return r;
+  if ((int64_t)B * H * Nq == 0) return ok();
+  static thread_local AttnParams p;
+  p = AttnParams{};
+  fill_common(p, c);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.ks_b = kv_strides[0]; p.ks_n = kv_strides[1]; p.ks_h = kv_strides[2];
+  p.Nkv = Nkv;
+  p.snap = local_count;
+  p.o_snap = o_local;
+  p.lse_snap = lse_local;
+  p.ss_b = o_local_strides[0]; p.ss_n = o_local_strides[1]; p.ss_h = o_local_strides[2];
+  fill_blocks(p, Nq, Nkv, kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg);
+  return launch_blocks(c, p, {}, static_cast<hipStream_t>(stream));
 }
 
 int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_flat,

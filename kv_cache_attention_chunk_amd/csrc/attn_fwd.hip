@@ -548,6 +548,59 @@ void attn_fwd_kernel(const AttnParams p) {
     dlen[j] = 0;
   }
 
+  // Writes the softmax state of the tiles processed so far: O = acc / l and
+  // LSE = ln 2 (m + log2 l) (empty key set: O = 0, LSE = -inf), to the
+  // snapshot outputs (to_snap), else to the float32 partial slot of a split
+  // query tile or to the final outputs.
+  auto emit_state = [&](bool to_snap) {
+    const float lt = half_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_row = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    if (!qvalid) return;
+    if (!to_snap && slot >= 0) {
+      // partial state of a split query tile: O / l and LSE, float32
+      float* part = p.ws + (int64_t)slot * BM * (D + 1);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d0 = 32 * dt + 8 * r + 4 * hg;
+          f32x4_t v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
+          *reinterpret_cast<f32x4_t*>(part + qr * D + d0) = v4;
+        }
+      }
+      if (hg == 0) part[BM * D + qr] = lse_row;
+      return;
+    }
+    void* const obuf = to_snap ? p.o_snap : p.o;
+    float* const lbuf = to_snap ? p.lse_snap : p.lse;
+    const int64_t obase = to_snap ? b * p.ss_b + (int64_t)qrow * p.ss_n + h * p.ss_h
+                                  : b * p.os_b + (int64_t)qrow * p.os_n + h * p.os_h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * dt + 8 * r + 4 * hg;
+        f32x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
+        if (OF32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(obuf) + obase + d0) = v4;
+        } else {
+          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+          const bf16x4_t bv = __builtin_convertvector(v4, bf16x4_t);
+          *reinterpret_cast<bf16x4_t*>(reinterpret_cast<uint16_t*>(obuf) + obase + d0) = bv;
+        }
+      }
+    }
+    if (hg == 0) lbuf[(int64_t)bh * p.Nq + qrow] = lse_row;
+  };
+  // Dual output (block mode): after the first `snap` tiles of the list the
+  // state is also written to the snapshot outputs.
+  const int snap = (MODE == MODE_BLOCKS && p.snap >= 0) ? (p.snap < ntiles ? p.snap : ntiles) : -1;
+
   // One iteration: the first operand reads of the fused body go out right
   // after the barrier, ahead of the load issue and the rescale.
   float rawmax = -INFINITY;     // raw row max of the tile in `cur`
@@ -585,9 +638,11 @@ void attn_fwd_kernel(const AttnParams p) {
       if ((it > last_it || last_slot < 1) && it + KA < ntiles) ++after;   // K(it + KA)
     }
     wait_vm(after);
+    if (MODE == MODE_BLOCKS && t == snap - 1) emit_state(true);
   };
 
   f32x16_t sa[2], sb[2];
+  if (MODE == MODE_BLOCKS && snap == 0) emit_state(true);
   if (ntiles > 0) {
 #pragma unroll
     for (int j = 0; j < KA; ++j)
@@ -614,45 +669,7 @@ void attn_fwd_kernel(const AttnParams p) {
   }
 
   // ---- epilogue --------------------------------------------------------------
-  const float lt = half_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse_row = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-  if (qvalid && slot >= 0) {
-    // partial state of a split query tile: O / l and LSE, float32
-    float* part = p.ws + (int64_t)slot * BM * (D + 1);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * dt + 8 * r + 4 * hg;
-        f32x4_t v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
-        *reinterpret_cast<f32x4_t*>(part + qr * D + d0) = v4;
-      }
-    }
-    if (hg == 0) part[BM * D + qr] = lse_row;
-  } else if (qvalid) {
-    const int64_t obase = b * p.os_b + (int64_t)qrow * p.os_n + h * p.os_h;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * dt + 8 * r + 4 * hg;
-        f32x4_t v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
-        if (OF32) {
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.o) + obase + d0) = v4;
-        } else {
-          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-          const bf16x4_t bv = __builtin_convertvector(v4, bf16x4_t);
-          *reinterpret_cast<bf16x4_t*>(reinterpret_cast<uint16_t*>(p.o) + obase + d0) = bv;
-        }
-      }
-    }
-    if (hg == 0) p.lse[(int64_t)bh * p.Nq + qrow] = lse_row;
-  }
+  emit_state(false);
   if (MODE == MODE_BLOCKS || !p.sched) return;
   }   // segment loop
 }

@@ -43,6 +43,12 @@ struct AttnParams {
   int64_t is_b, is_n, is_h;
   int B, H, Nq, Nkv;
   float scale_log2;           // softmax scale * log2(e)
+  // dual output (block mode): after the first `snap` list entries (-1: none)
+  // the state is also written to o_snap (dtype of o) and lse_snap
+  int snap;
+  void* o_snap;
+  float* lse_snap;
+  int64_t ss_b, ss_n, ss_h;
   // block-list mode
   const int32_t* indptr;
   const int32_t* indices;
