@@ -252,6 +252,51 @@ def block_score_topk(q_mean, k_mean, cand_begin: int, cand_count: int, K: int,
     return {"idx": idx, "score": sc, "gap": gap, "near_tie": near}
 
 
+def persistent_update(q_mean, k_mean, persistent, evict_begin: int, evict_count: int, C: int,
+                      tie_eps: float = 1e-4) -> Dict[str, np.ndarray]:
+    """Persistent-memory update when the local window slides (Sparse Forcing
+    page, section 2 item 1, memory management): the blocks evicted from the
+    local window, [evict_begin, evict_begin + evict_count), join the head's
+    current persistent blocks as candidates, and the C best by coarse score
+    against the query representative q_mean [B, H, 1, d] (the chunk-mean
+    query) form the new persistent set.
+
+    Candidates are the set union: a persistent id inside the evicted range,
+    or outside [0, NB), is not a second candidate.  Scores, ordering and tie
+    rule as in block_score_topk (float32 scores, higher first, lower id first
+    on equal scores); the kept ids are returned ascending, padded with -1 (and
+    score -inf) when fewer than C candidates exist.  Also returns gap and
+    near_tie as block_score_topk does."""
+    qm = np.asarray(q_mean, dtype=np.float32).astype(np.float64)
+    km = np.asarray(k_mean, dtype=np.float32).astype(np.float64)
+    pers = np.asarray(persistent, dtype=np.int64)
+    B, H, _, d = qm.shape
+    NB = km.shape[2]
+    ev = set(range(evict_begin, evict_begin + evict_count))
+    idx = np.full((B, H, C), -1, dtype=np.int32)
+    sc = np.full((B, H, C), -np.inf, dtype=np.float32)
+    gap = np.full((B, H), np.inf)
+    near = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            cand = sorted(ev | {int(x) for x in pers[b, h] if 0 <= x < NB})
+            cand = np.array(cand, dtype=np.int64)
+            s = np.array([np.float32(np.dot(qm[b, h, 0], km[b, h, c])) for c in cand],
+                         dtype=np.float32)
+            order = np.lexsort((cand, -s.astype(np.float64)))
+            k = min(C, len(cand))
+            top = order[:k]
+            asc = top[np.argsort(cand[top])]
+            idx[b, h, :k] = cand[asc]
+            sc[b, h, :k] = s[asc]
+            if k:
+                kth = float(s[order[k - 1]])
+                if k < len(cand):
+                    gap[b, h] = kth - float(s[order[k]])
+                near[b, h] = int(np.sum(np.abs(s.astype(np.float64) - kth) < tie_eps))
+    return {"idx": idx, "score": sc, "gap": gap, "near_tie": near}
+
+
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
                    persistent: Optional[np.ndarray], topk: Optional[np.ndarray],
                    topk_offset: int) -> Tuple[np.ndarray, np.ndarray]:

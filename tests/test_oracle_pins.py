@@ -461,3 +461,89 @@ def test_planted_tiling_and_tiebreak_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oc, "block_score_topk", reversed_ties)
     with pytest.raises(AssertionError):
         test_topk_planted_order_and_ties()
+
+
+# ---------------------------------------------------------------------------
+# persistent-memory update (Sparse Forcing page, section 2 item 1: evicted
+# local-window blocks join the persistent set as candidates; the top C by
+# coarse score stay)
+# ---------------------------------------------------------------------------
+def _planted_update_inputs():
+    d = 4
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[..., 1] = 2.0                                      # score = 2 * k[..., 1]
+    k = np.zeros((1, 1, 20, d), np.float32)
+    # persistent blocks 2, 5, 9 with scores 6, 2, 10; evicted window 14..17 with 8, 2, 12, -4
+    for blk, s in [(2, 6.0), (5, 2.0), (9, 10.0), (14, 8.0), (15, 2.0), (16, 12.0), (17, -4.0)]:
+        k[0, 0, blk, 1] = s / 2.0
+    k[0, 0, 0, 1] = 100.0                                # not a candidate
+    pers = np.array([[[2, 5, 9]]], np.int32)
+    return q, k, pers
+
+
+def test_persistent_update_planted_scores_and_ties():
+    q, k, pers = _planted_update_inputs()
+    r = oc.persistent_update(q, k, pers, 14, 4, 3)
+    # candidates by score: 16 (12), 9 (10), 14 (8), 2 (6), 5 (2), 15 (2), 17 (-4)
+    assert r["idx"][0, 0].tolist() == [9, 14, 16]
+    assert r["score"][0, 0].tolist() == [10.0, 8.0, 12.0]
+    assert r["gap"][0, 0] == 2.0
+    r5 = oc.persistent_update(q, k, pers, 14, 4, 5)
+    # the 2.0 tie between persistent block 5 and evicted block 15: lower id 5 stays
+    assert r5["idx"][0, 0].tolist() == [2, 5, 9, 14, 16]
+    assert r5["gap"][0, 0] == 0.0 and r5["near_tie"][0, 0] == 2
+    # C as large as the candidate set keeps everything, then pads with -1
+    r8 = oc.persistent_update(q, k, pers, 14, 4, 8)
+    assert r8["idx"][0, 0].tolist() == [2, 5, 9, 14, 15, 16, 17, -1]
+    assert r8["score"][0, 0, -1] == -np.inf
+
+
+def test_persistent_update_set_union_rules():
+    q, k, pers = _planted_update_inputs()
+    # a persistent id inside the evicted range is one candidate, not two;
+    # ids outside [0, NB) are dropped
+    p2 = np.array([[[9, 16, 25, -3]]], np.int32)
+    r = oc.persistent_update(q, k, p2, 14, 4, 6)
+    assert r["idx"][0, 0].tolist() == [9, 14, 15, 16, 17, -1]
+    # evicted blocks all below the persistent ones: the set is unchanged
+    k_low = k.copy()
+    k_low[0, 0, 14:18, 1] = -50.0
+    assert oc.persistent_update(q, k_low, pers, 14, 4, 3)["idx"][0, 0].tolist() == [2, 5, 9]
+    # evicted blocks all above: the set becomes the best evicted blocks
+    k_high = k.copy()
+    k_high[0, 0, 14:18, 1] = [60.0, 50.0, 70.0, 40.0]
+    assert oc.persistent_update(q, k_high, pers, 14, 4, 3)["idx"][0, 0].tolist() == [14, 15, 16]
+
+
+def test_persistent_update_matches_bruteforce_random():
+    rng = np.random.default_rng(31)
+    B, H, NB, d, C = 2, 3, 120, 16, 7
+    qm = _rand(rng, B, H, 1, d)
+    km = _rand(rng, B, H, NB, d)
+    pers = np.stack([np.sort(rng.choice(np.arange(0, 80), C, replace=False))
+                     for _ in range(B * H)]).reshape(B, H, C).astype(np.int32)
+    r = oc.persistent_update(qm, km, pers, 90, 25, C)
+    for b, h in itertools.product(range(B), range(H)):
+        cand = sorted(set(range(90, 115)) | set(pers[b, h].tolist()))
+        sc = [float(np.float32(math.fsum(float(a) * float(c) for a, c in zip(qm[b, h, 0], km[b, h, j]))))
+              for j in cand]
+        assert r["idx"][b, h].tolist() == brute_topk(sc, cand, C)
+
+
+def test_planted_persistent_update_mistakes_are_caught(monkeypatch):
+    real = oc.persistent_update
+
+    def evicted_only(q, k, pers, eb, ec, C, tie_eps=1e-4):
+        # forgets the current persistent blocks as candidates
+        return real(q, k, np.full_like(np.asarray(pers), -1), eb, ec, C, tie_eps)
+    monkeypatch.setattr(oc, "persistent_update", evicted_only)
+    with pytest.raises(AssertionError):
+        test_persistent_update_planted_scores_and_ties()
+    monkeypatch.undo()
+
+    def lowest_scores(q, k, pers, eb, ec, C, tie_eps=1e-4):
+        # keeps the C worst candidates (sign flipped)
+        return real(-np.asarray(q), k, pers, eb, ec, C, tie_eps)
+    monkeypatch.setattr(oc, "persistent_update", lowest_scores)
+    with pytest.raises(AssertionError):
+        test_persistent_update_planted_scores_and_ties()
