@@ -212,6 +212,16 @@ def per_config(reps=10, wan=None):
         f_dense = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
         out[f"sparse_K{lay['K']}"] = _rec(ms, f, kvb, ratio=ratio,
                                           dense_equiv_tflops=round(f_dense / (ms * 1e-3) / 1e12, 1))
+    # persistent-memory update when the window slides: the chunk's 75 local
+    # blocks are evicted into the candidates of each head's 32 persistent blocks
+    lay = wl.sparse_layout(w, 0.125)
+    _, cm = ca.block_mean(q, 64, 1560, with_total=True)
+    pers = ca.block_score_topk(cm, km, lay["C"], cand_begin=lay["hist_begin"],
+                               cand_count=lay["hist_count"])[:, :, 0, :].contiguous()
+    ms = _time_ms(torch, lambda: ca.persistent_update(cm, km, pers, lay["local_begin"],
+                                                      lay["local_count"], lay["C"]), reps)
+    out["persistent_update"] = {"us": round(ms * 1e3, 1), "candidates_per_head":
+                                lay["C"] + lay["local_count"], "C": lay["C"], "heads": w.H}
     del q, k, v, km
     # ragged per-head caches
     w = wl.ragged(seed=0)

@@ -255,6 +255,30 @@ int ca_block_score_topk(const float* q_mean, const float* k_mean,
                         int32_t* out_idx, float* out_score, void* stream);
 
 /*
+ * Persistent-memory update when the local window slides (Sparse Forcing
+ * page, section 2 item 1, memory management: blocks evicted from the local
+ * window are candidates, and the top C by coarse score are kept or updated as
+ * persistent memory).  Per (b, h), the candidates are the set union of the
+ * evicted blocks [evict_begin, evict_begin + evict_count) and the current
+ * persistent ids persistent[b,h,:] that lie in [0, NKB); each is scored
+ * <q_mean[b,h,0,:], k_mean[b,h,id,:]> in float32 (q_mean: the query
+ * representative, e.g. the chunk-mean query from ca_block_mean's out_total)
+ * and the C highest are kept, equal scores resolved toward the lower block
+ * id, written in ascending id order.  Slots past the number of candidates get
+ * id -1 (score -inf).
+ *   q_mean     float32 [B, H, 1, d] contiguous; k_mean float32 [B, H, NKB, d]
+ *   persistent int32 [B, H, C_in] (distinct ids per head); NULL with C_in = 0
+ *   out        int32 [B, H, C]; may be the persistent array itself when
+ *              C == C_in (updated in place)
+ *   out_score  optional float32 [B, H, C]
+ *   limits     d a multiple of 4, <= 512; 1 <= C; C_in + evict_count <= 4096,
+ *              C <= 4096; the evicted range inside [0, NKB)
+ */
+int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H, int NKB, int d,
+                         const int32_t* persistent, int C_in, int evict_begin, int evict_count,
+                         int C, int32_t* out, float* out_score, void* stream);
+
+/*
  * PBSA block lists (Sparse Forcing page, section 2 item 3): CSR row
  * (b*H + h)*NQB + qb = sorted union, duplicates removed, of the sink blocks
  * [sink_begin, sink_begin + sink_count), persistent[b,h,:] (C ids, ascending,

@@ -46,6 +46,7 @@ SIGNATURES = {
                           _i64p, _i64p, _i64p, _p]),
     "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),
     "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "ca_persistent_update": (_i, [_p, _p, _i, _i, _i, _i, _i32p, _i, _i, _i, _i, _p, _p, _p]),
     "ca_build_kv_index": (_i, [_i, _i, _i, _i, _i, _i32p, _i, _i32p, _i, _i, _p, _p, _p]),
 }
 

@@ -344,6 +344,40 @@ def block_score_topk(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *, cand
     return (idx, sc) if return_scores else idx
 
 
+def persistent_update(q_mean: torch.Tensor, k_mean: torch.Tensor,
+                      persistent: Optional[torch.Tensor], evict_begin: int, evict_count: int,
+                      C: int, *, out: Optional[torch.Tensor] = None, return_scores: bool = False):
+    """New persistent block set per head when the local window slides: the
+    top C of (current persistent ids) U (evicted blocks [evict_begin,
+    evict_begin + evict_count)) by <q_mean, k_mean[id]>, ids ascending, -1
+    padding.  `out` may be `persistent` itself (in-place update)."""
+    for n, t in (("q_mean", q_mean), ("k_mean", k_mean)):
+        if t.dtype != torch.float32 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 GPU tensor [B, H, N, d]")
+    B, H, one, d = q_mean.shape
+    NKB = k_mean.shape[2]
+    if one != 1 or tuple(k_mean.shape) != (B, H, NKB, d):
+        raise ValueError("q_mean must be [B, H, 1, d] and k_mean [B, H, NKB, d]")
+    C_in = 0
+    if persistent is not None:
+        _i32("persistent", persistent)
+        if persistent.dim() != 3 or tuple(persistent.shape[:2]) != (B, H):
+            raise ValueError("persistent must be [B, H, C_in]")
+        C_in = persistent.shape[2]
+    if out is None:
+        out = torch.empty((B, H, C), dtype=torch.int32, device=q_mean.device)
+    else:
+        _i32("out", out)
+        if tuple(out.shape) != (B, H, C):
+            raise ValueError("out must be [B, H, C]")
+    sc = torch.empty((B, H, C), dtype=torch.float32, device=q_mean.device) if return_scores else None
+    st = lib().ca_persistent_update(q_mean.data_ptr(), k_mean.data_ptr(), B, H, NKB, d,
+                                    _ptr(persistent), C_in, evict_begin, evict_count, C,
+                                    out.data_ptr(), _ptr(sc), _stream())
+    check(st)
+    return (out, sc) if return_scores else out
+
+
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
                    persistent: Optional[torch.Tensor], topk: Optional[torch.Tensor],
                    topk_offset: int = 0, device=None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -550,6 +550,28 @@ int ca_block_score_topk(const float* q_mean, const float* k_mean, int B, int H, 
                   "block_score_topk launch");
 }
 
+int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H, int NKB, int d,
+                         const int32_t* persistent, int C_in, int evict_begin, int evict_count,
+                         int C, int32_t* out, float* out_score, void* stream) {
+  if (B < 0 || H < 0 || NKB < 0 || C_in < 0 || evict_count < 0 || evict_begin < 0)
+    return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 4 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 4, <= 512)", d);
+  if (!q_mean || !k_mean || !out) return fail(CA_EINVAL, "NULL pointer");
+  if (C_in > 0 && !persistent) return fail(CA_EINVAL, "persistent is NULL with C_in > 0");
+  if (!aligned16(q_mean) || !aligned16(k_mean)) return fail(CA_EINVAL, "means must be 16-byte aligned");
+  if (evict_begin + (int64_t)evict_count > NKB) return fail(CA_ERANGE, "evicted range outside [0, NKB)");
+  if (C < 1 || (int64_t)C_in + evict_count > 4096 || C > 4096)
+    return fail(CA_ERANGE, "need 1 <= C and C_in + evict_count, C <= 4096");
+  if ((const void*)out == (const void*)persistent && C != C_in)
+    return fail(CA_EINVAL, "in-place update needs C == C_in");
+  if ((int64_t)B * H > 65535) return fail(CA_ERANGE, "B*H above 65535");
+  if (int r = check_device()) return r;
+  return launched(launch_persistent_update(q_mean, k_mean, B, H, NKB, d, persistent, C_in,
+                                           evict_begin, evict_count, C, out, out_score,
+                                           static_cast<hipStream_t>(stream)),
+                  "persistent_update launch");
+}
+
 int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
                       const int32_t* persistent, int C, const int32_t* topk, int K,
                       int topk_offset, int32_t* indptr, int32_t* indices, void* stream) {

@@ -109,6 +109,10 @@ hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
 hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int NQB,
                              int NKB, int d, int cand_begin, int cand_count, int K,
                              int32_t* out_idx, float* out_score, hipStream_t stream);
+hipError_t launch_persistent_update(const float* qm, const float* km, int B, int H, int NKB,
+                                   int d, const int32_t* pers, int C_in, int evict_begin,
+                                   int evict_count, int C, int32_t* out, float* out_score,
+                                   hipStream_t stream);
 hipError_t launch_build_kv_index(int rows, int sink_begin, int sink_count,
                                  const int32_t* persistent, int C, int NQB,
                                  const int32_t* topk, int K, int topk_offset,

@@ -439,6 +439,92 @@ __global__ __launch_bounds__(kIndexThreads) void build_index_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent-memory update (Sparse Forcing page, section 2 item 1, memory
+// management): when the local window slides, its evicted blocks [eb, eb + ne)
+// join the head's persistent blocks as candidates and the C best by coarse
+// score <q_mean, k_mean[id]> stay.  One workgroup per (b, h):
+//   * candidates in LDS: the evicted range, then the persistent ids that lie
+//     in [0, NKB) and outside the evicted range (a set union; persistent ids
+//     are distinct by contract);
+//   * float32 scores (a NaN score ranks as -inf);
+//   * rank(i) = #{j : s_j > s_i} + #{j : s_j = s_i, id_j < id_i}, i.e. the
+//     position in (score descending, block id ascending) order;
+//   * the rank < C candidates are written at their position in ascending id
+//     order; slots past the candidate count get id -1 and score -inf.
+// The persistent row is read into LDS before anything is written, so the
+// output may overwrite it in place (same C).
+// ---------------------------------------------------------------------------
+constexpr int kUpdThreads = 256;
+
+__global__ __launch_bounds__(kUpdThreads) void persistent_update_kernel(
+    const float* __restrict__ qm, const float* __restrict__ km, int NKB, int d,
+    const int32_t* pers, int C_in, int eb, int ne, int C, int32_t* out,
+    float* __restrict__ out_score) {
+  __shared__ int ids[kTopkMaxCand];
+  __shared__ float sc[kTopkMaxCand];
+  __shared__ int rk[kTopkMaxCand];
+  __shared__ int wcount[kUpdThreads / 64];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < ne; i += kUpdThreads) ids[i] = eb + i;
+  // compact the kept persistent ids behind the evicted range
+  int n = ne;
+  for (int c0 = 0; c0 < C_in; c0 += kUpdThreads) {
+    const int i = c0 + tid;
+    const int id = i < C_in ? pers[(int64_t)bh * C_in + i] : -1;
+    const bool keep = i < C_in && id >= 0 && id < NKB && !(id >= eb && id < eb + ne);
+    const unsigned long long m = __ballot(keep);
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int wpre = 0, tot = 0;
+    for (int w = 0; w < kUpdThreads / 64; ++w) {
+      wpre += w < wave ? wcount[w] : 0;
+      tot += wcount[w];
+    }
+    if (keep) ids[n + wpre + __popcll(m & ((1ull << lane) - 1))] = id;
+    n += tot;
+    __syncthreads();
+  }
+  // scores
+  const float* q = qm + (int64_t)bh * d;
+  const float* kb = km + (int64_t)bh * NKB * d;
+  for (int i = tid; i < n; i += kUpdThreads) {
+    const float* kr = kb + (int64_t)ids[i] * d;
+    float acc = 0.f;
+    for (int c = 0; c < d; c += 4) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + c);
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(kr + c);
+      acc = fmaf(a[3], x[3], fmaf(a[2], x[2], fmaf(a[1], x[1], fmaf(a[0], x[0], acc))));
+    }
+    sc[i] = acc != acc ? -INFINITY : acc;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kUpdThreads) {
+    const float si = sc[i];
+    const int idi = ids[i];
+    int r = 0;
+    for (int j = 0; j < n; ++j) {
+      const float sj = sc[j];
+      r += (int)(sj > si) + (int)(sj == si && ids[j] < idi);
+    }
+    rk[i] = r;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kUpdThreads) {
+    if (rk[i] >= C) continue;
+    const int idi = ids[i];
+    int pos = 0;
+    for (int j = 0; j < n; ++j) pos += (int)(rk[j] < C && ids[j] < idi);
+    out[(int64_t)bh * C + pos] = idi;
+    if (out_score) out_score[(int64_t)bh * C + pos] = sc[i];
+  }
+  for (int pos = n + tid; pos < C; pos += kUpdThreads) {
+    out[(int64_t)bh * C + pos] = -1;
+    if (out_score) out_score[(int64_t)bh * C + pos] = -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d, const int64_t* xs,
@@ -476,6 +562,16 @@ hipError_t launch_build_kv_index(int rows, int sink_begin, int sink_count,
   hipLaunchKernelGGL(build_index_kernel, dim3(1), dim3(kIndexThreads), 0, stream, rows,
                      sink_begin, sink_count, persistent, C, NQB, topk, K, topk_offset, indptr,
                      indices);
+  return hipGetLastError();
+}
+
+hipError_t launch_persistent_update(const float* qm, const float* km, int B, int H, int NKB,
+                                   int d, const int32_t* pers, int C_in, int evict_begin,
+                                   int evict_count, int C, int32_t* out, float* out_score,
+                                   hipStream_t stream) {
+  if (B * H == 0) return hipSuccess;
+  hipLaunchKernelGGL(persistent_update_kernel, dim3(B * H), dim3(kUpdThreads), 0, stream, qm, km,
+                     NKB, d, pers, C_in, evict_begin, evict_count, C, out, out_score);
   return hipGetLastError();
 }
 

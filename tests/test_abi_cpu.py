@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -137,6 +137,14 @@ def test_merge_mean_topk_index_checks(L):
     assert t(cb=451) == CA_ERANGE
     assert t(cc=5000) == CA_ERANGE
     assert L.ca_build_kv_index(1, 2, 75, 0, 25, None, 32, FAKE, 10, 0, FAKE, FAKE, None) == CA_EINVAL
+    u = lambda **kw: L.ca_persistent_update(FAKE, FAKE, 1, 12, 525, kw.get("d", 128), kw.get("p", FAKE),
+                                            kw.get("cin", 32), kw.get("eb", 450), kw.get("ne", 75),
+                                            kw.get("C", 32), kw.get("out", FAKE + 4096), None, None)
+    assert u(d=6) == CA_EUNSUPPORTED
+    assert u(p=None) == CA_EINVAL                      # C_in > 0 without persistent ids
+    assert u(eb=460) == CA_ERANGE                      # evicted range past NKB
+    assert u(C=0) == CA_ERANGE
+    assert u(out=FAKE, C=16) == CA_EINVAL              # in place with a different C
     assert L.ca_build_kv_index(1, 1000, 75, 0, 25, FAKE, 32, FAKE, 10, 0, FAKE, FAKE, None) == CA_ERANGE
 
 
