@@ -159,6 +159,64 @@ def chunk_attn_varlen(Q, K_flat, V_flat, cu_seqlens, scale: float, rows=None, he
 
 
 # ---------------------------------------------------------------------------
+# Ragged cache packing (Pyramid Forcing page, section 2: per-head cache
+# policies keep a per-head set of frames -- stride or periodic samples, or
+# adjacent frames merged into one -- and section 3: the variable-length caches
+# are stored as flat sequences with boundary indices).
+# ---------------------------------------------------------------------------
+def _bf16_rne(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest, ties to even (NaN kept
+    as a quiet NaN)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x32)
+    r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+def pack_ragged(k_bits, v_bits, frame_ptr, frame_src, frame_tokens: int):
+    """Flatten per-head frame selections of a dense cache.
+
+    k_bits, v_bits  uint16 bf16 bit patterns [B, N, H, d] (the dense cache)
+    frame_ptr       int [B*H + 1]: head bh owns output frames
+                    [frame_ptr[bh], frame_ptr[bh+1]), heads in order
+    frame_src       int [F, 2]: output frame j copies source frame a =
+                    frame_src[j, 0] of its head, or, when b = frame_src[j, 1]
+                    is not -1, merges frames a and b: each element is the
+                    float32 sum of the two bf16 values times 1/2, rounded to
+                    bf16 (nearest, ties to even).  A source frame outside the
+                    cache contributes zeros.
+    Returns (k_flat, v_flat) uint16 [F * frame_tokens, d] and cu_seqlens
+    int32 [B*H + 1] = frame_ptr * frame_tokens."""
+    B, N, H, d = k_bits.shape
+    nf = N // frame_tokens
+    frame_ptr = np.asarray(frame_ptr, dtype=np.int64)
+    frame_src = np.asarray(frame_src, dtype=np.int64).reshape(-1, 2)
+    F = int(frame_ptr[-1])
+    outs = []
+    for src in (k_bits, v_bits):
+        flat = np.zeros((F * frame_tokens, d), dtype=np.uint16)
+        for bh in range(B * H):
+            b, h = divmod(bh, H)
+            for j in range(int(frame_ptr[bh]), int(frame_ptr[bh + 1])):
+                def frame(f):
+                    if 0 <= f < nf:
+                        rows = src[b, f * frame_tokens:(f + 1) * frame_tokens, h, :]
+                        return (rows.astype(np.uint32) << 16).view(np.float32)
+                    return np.zeros((frame_tokens, d), dtype=np.float32)
+                a, c = int(frame_src[j, 0]), int(frame_src[j, 1])
+                if c == -1:
+                    bits = _bf16_rne(frame(a))
+                else:
+                    s32 = (frame(a) + frame(c)).astype(np.float32)   # one float32 rounding
+                    bits = _bf16_rne((s32 * np.float32(0.5)).astype(np.float32))
+                flat[j * frame_tokens:(j + 1) * frame_tokens] = bits
+        outs.append(flat)
+    cu = (frame_ptr * frame_tokens).astype(np.int32)
+    return outs[0], outs[1], cu
+
+
+# ---------------------------------------------------------------------------
 # LSE merge (ISPA page, section 2 item 1: local and history branches combined
 # after the fact through their LSE states).
 # ---------------------------------------------------------------------------

@@ -547,3 +547,70 @@ def test_planted_persistent_update_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oc, "persistent_update", lowest_scores)
     with pytest.raises(AssertionError):
         test_persistent_update_planted_scores_and_ties()
+
+
+# ---------------------------------------------------------------------------
+# ragged cache packing (Pyramid Forcing page, sections 2-3)
+# ---------------------------------------------------------------------------
+def test_pack_ragged_copies_equal_the_gathered_frames():
+    # copies only: the packed buffers equal the generator's own flattening of
+    # the same frame subsets (a separate, data-layout-only implementation)
+    w = wl.ragged(seed=3, H=4, d=16, frames_q=1, frames_kv=8, frame_tokens=5)
+    fr = w.ragged_frames
+    ptr = np.zeros(w.B * w.H + 1, np.int64)
+    ptr[1:] = np.cumsum([len(fr[bh]) for bh in range(w.B * w.H)])
+    src = np.array([[f, -1] for bh in range(w.B * w.H) for f in fr[bh]], np.int32)
+    kf, vf, cu = oc.pack_ragged(w.k.bits, w.v.bits, ptr, src, 5)
+    assert np.array_equal(kf, w.k_flat.bits) and np.array_equal(vf, w.v_flat.bits)
+    assert np.array_equal(cu, w.cu_seqlens)
+
+
+def test_pack_ragged_merge_values_and_rounding():
+    T, d = 2, 4
+    k = np.zeros((1, 3 * T, 1, d), np.float32)
+    k[0, 0:T, 0] = [1.0, 2.0, -3.0, 1.0]                  # frame 0
+    k[0, T:2 * T, 0] = [2.0, 2.0, 3.0, 1.0078125]         # frame 1 (1 + 2^-7 is one bf16 ulp above 1)
+    k[0, 2 * T:, 0] = [8.0, -8.0, 0.5, 0.25]              # frame 2
+    # second token rows: averages on and off bf16 rounding ties
+    k[0, 1, 0] = [1.0, 1.0, 1.0, -1.0]
+    k[0, T + 1, 0] = [1.0234375, 1.01171875, 1.0078125, -1.0234375]
+    kb = wl.bf16_bits(k)
+    ptr = np.array([0, 4])
+    src = np.array([[0, 1], [1, -1], [2, 0], [5, -1]])   # merge, copy, merge, out of range
+    kf, vf, cu = oc.pack_ragged(kb, kb, ptr, src, T)
+    val = wl.bf16_to_f32(kf).reshape(4, T, d)
+    assert val[0, 0].tolist() == [1.5, 2.0, 0.0, 1.0]     # (1 + 1 + 2^-7)/2 = 1 + 2^-8: tie -> even (1.0)
+    # 1 + 3*2^-8: tie between odd 1 + 2^-7 and even 1 + 2^-6 -> 1 + 2^-6;
+    # 1 + 3*2^-9 (above the tie at 1 + 2^-8) -> 1 + 2^-7; 1 + 2^-8 -> 1.0; sign kept
+    assert val[0, 1].tolist() == [1.015625, 1.0078125, 1.0, -1.015625]
+    assert val[1, 0].tolist() == [2.0, 2.0, 3.0, 1.0078125]
+    assert val[2, 0].tolist() == [4.5, -3.0, -1.25, 0.625]
+    assert np.all(val[3] == 0.0)
+    assert cu.tolist() == [0, 4 * T]
+    assert np.array_equal(kf, vf)
+
+
+def test_pack_ragged_merge_of_a_frame_with_itself_is_a_copy():
+    rng = np.random.default_rng(9)
+    k = wl.bf16_bits(rng.standard_normal((1, 12, 2, 8), dtype=np.float32))
+    ptr = np.array([0, 2, 3])
+    kf_m, _, _ = oc.pack_ragged(k, k, ptr, np.array([[1, 1], [2, 2], [0, 0]]), 4)
+    kf_c, _, _ = oc.pack_ragged(k, k, ptr, np.array([[1, -1], [2, -1], [0, -1]]), 4)
+    assert np.array_equal(kf_m, kf_c)
+
+
+def test_planted_packing_mistakes_are_caught(monkeypatch):
+    def truncate(x32):
+        return (np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    monkeypatch.setattr(oc, "_bf16_rne", truncate)
+    with pytest.raises(AssertionError):
+        test_pack_ragged_merge_values_and_rounding()
+    monkeypatch.undo()
+    real = oc.pack_ragged
+
+    def swapped_heads(k, v, ptr, src, T):
+        kf, vf, cu = real(k, v, ptr, src, T)
+        return vf, kf, cu                                   # K and V exchanged
+    monkeypatch.setattr(oc, "pack_ragged", swapped_heads)
+    with pytest.raises(AssertionError):
+        test_pack_ragged_copies_equal_the_gathered_frames()
