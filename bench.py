@@ -232,7 +232,17 @@ def per_config(reps=10, wan=None):
     out["ragged"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_varlen_fwd(
         q, kf, vf, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
         sum_len=tot, lengths_frames=w.meta["n_frames"])
-    del q, kf, vf
+    # packing those ragged caches from the dense per-head cache (HBM-bound:
+    # every packed K/V row read once and written once)
+    kd, vd = dev(w.k), dev(w.v)
+    frames = [w.ragged_frames[bh] for bh in range(w.B * w.H)]
+    ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, frames, 1560), reps)
+    moved = 2.0 * 2.0 * tot * w.d * 2
+    out["ragged_pack"] = {"us": round(ms * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
+                          "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "note": "includes host-side list upload"}
+    del q, kf, vf, kd, vd
     # mixed 40-head layer (dense / block lists / ragged per head)
     w = wl.mixed(seed=0)
     lay = w.meta["sparse"]

@@ -185,6 +185,38 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged cache packing (Pyramid Forcing page, section 2: per-head cache
+ * policies -- adaptive-stride or periodic frame sampling, or merging adjacent
+ * frames -- plus the shared sink and forced recent frames; section 3: the
+ * variable-length caches are stored flat with boundary indices and packed in
+ * one vectorized pass).  Builds the inputs of ca_chunk_attn_varlen_fwd from a
+ * dense per-head cache in one launch.
+ *
+ *   k, v         bf16 dense cache [B, N, H, d], strides kv_strides (host);
+ *                frame f of a head is its tokens [f T, (f + 1) T),
+ *                T = frame_tokens; only whole frames (f < N / T) are frames
+ *   frame_ptr    int32 [B*H + 1], device: head b*H + h owns output frames
+ *                [frame_ptr[bh], frame_ptr[bh+1]), nondecreasing from 0 to
+ *                total_frames.  frame_ptr_host: optional host copy, checked
+ *                when given
+ *   frame_src    int32 [total_frames, 2], device: output frame j copies
+ *                source frame frame_src[j][0] of its head, or, when
+ *                frame_src[j][1] != -1, merges the two source frames: each
+ *                element = bf16(round to nearest even of (float32(a + b) /
+ *                2)).  Source frames outside [0, N / T) contribute zeros.
+ *   k_flat,      bf16 [total_frames * T, d] outputs, row stride
+ *   v_flat       flat_row_stride elements (a multiple of 8, >= d)
+ *   cu_seqlens   int32 [B*H + 1] output: frame_ptr * T
+ *   limits       d a multiple of 8, <= 512; 1 <= B*H <= 32767;
+ *                total_frames <= 65535
+ */
+int ca_pack_ragged(const void* k, const void* v, int B, int N, int H, int d,
+                   const int64_t* kv_strides, int frame_tokens, const int32_t* frame_ptr,
+                   const int32_t* frame_ptr_host, int total_frames, const int32_t* frame_src,
+                   void* k_flat, void* v_flat, int64_t flat_row_stride, int32_t* cu_seqlens,
+                   void* stream);
+
+/*
  * Mixed per-head cache modes in one call (Pyramid Forcing page, section 3:
  * heads with different cache layouts served together to cut launches).
  * head_mode (host, int32 [B*H]) picks CA_MODE_DENSE (k, v dense cache),

@@ -378,6 +378,40 @@ def persistent_update(q_mean: torch.Tensor, k_mean: torch.Tensor,
     return (out, sc) if return_scores else out
 
 
+def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
+    """Flatten per-head frame selections of a dense cache k, v [B, N, H, d]
+    into k_flat, v_flat [sum of frames * frame_tokens, d] + cu_seqlens.
+    frames[bh] lists head bh's output frames in order; an entry is a source
+    frame id (copied) or a pair (a, b) of frames merged into one (float32
+    average rounded to bf16).  Returns (k_flat, v_flat, cu_seqlens,
+    cu_seqlens_host)."""
+    _bshd("k", k), _bshd("v", v)
+    B, N, H, d = k.shape
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must match in shape and strides")
+    if len(frames) != B * H:
+        raise ValueError("frames must list B*H heads")
+    ptr = np.zeros(B * H + 1, np.int32)
+    src = []
+    for bh, fl in enumerate(frames):
+        for f in fl:
+            a, b = (int(f[0]), int(f[1])) if isinstance(f, (tuple, list)) else (int(f), -1)
+            src.append((a, b))
+        ptr[bh + 1] = len(src)
+    F = len(src)
+    src_d = torch.tensor(np.array(src, np.int32).reshape(-1) if F else np.zeros(2, np.int32),
+                         device=k.device)
+    ptr_d = torch.from_numpy(ptr).to(k.device)
+    kf = torch.empty((F * frame_tokens, d), dtype=torch.bfloat16, device=k.device)
+    vf = torch.empty_like(kf)
+    cu = torch.empty(B * H + 1, dtype=torch.int32, device=k.device)
+    st = lib().ca_pack_ragged(k.data_ptr(), v.data_ptr(), B, N, H, d, _st(k), frame_tokens,
+                              ptr_d.data_ptr(), ptr.ctypes.data, F, src_d.data_ptr(),
+                              kf.data_ptr(), vf.data_ptr(), d, cu.data_ptr(), _stream())
+    check(st)
+    return kf, vf, cu, ptr * frame_tokens
+
+
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
                    persistent: Optional[torch.Tensor], topk: Optional[torch.Tensor],
                    topk_offset: int = 0, device=None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -572,6 +572,39 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
                   "persistent_update launch");
 }
 
+int ca_pack_ragged(const void* k, const void* v, int B, int N, int H, int d,
+                   const int64_t* kv_strides, int frame_tokens, const int32_t* frame_ptr,
+                   const int32_t* frame_ptr_host, int total_frames, const int32_t* frame_src,
+                   void* k_flat, void* v_flat, int64_t flat_row_stride, int32_t* cu_seqlens,
+                   void* stream) {
+  if (B < 0 || H < 0 || N < 0 || total_frames < 0) return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 8 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 8, <= 512)", d);
+  if (frame_tokens < 1) return fail(CA_EINVAL, "frame_tokens must be >= 1");
+  if ((int64_t)B * H < 1 || (int64_t)B * H > 32767) return fail(CA_ERANGE, "B*H outside 1..32767");
+  if (!frame_ptr || !cu_seqlens) return fail(CA_EINVAL, "frame_ptr and cu_seqlens must be non-NULL");
+  if (total_frames > 0 && (!k || !v || !frame_src || !k_flat || !v_flat))
+    return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_flat) || !aligned16(v_flat))
+    return fail(CA_EINVAL, "k, v, k_flat, v_flat must be 16-byte aligned");
+  if (int r = check_strides("kv", kv_strides, 8)) return r;
+  if (flat_row_stride < d || flat_row_stride % 8) return fail(CA_EINVAL, "flat_row_stride must be >= d and a multiple of 8");
+  if ((int64_t)total_frames * frame_tokens > 0x7FFFFFFF || total_frames > 65535)
+    return fail(CA_ERANGE, "too many output frames (at most 65535)");
+  if (frame_ptr_host) {
+    if (frame_ptr_host[0] != 0) return fail(CA_EINVAL, "frame_ptr[0] != 0");
+    for (int i = 0; i < B * H; ++i)
+      if (frame_ptr_host[i + 1] < frame_ptr_host[i]) return fail(CA_EINVAL, "frame_ptr decreasing at %d", i);
+    if (frame_ptr_host[B * H] != total_frames) return fail(CA_EINVAL, "frame_ptr[B*H] != total_frames");
+  }
+  if (int r = check_device()) return r;
+  return launched(launch_pack_ragged(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                     B, N, H, d, kv_strides, frame_tokens, frame_ptr, total_frames,
+                                     frame_src, static_cast<uint16_t*>(k_flat),
+                                     static_cast<uint16_t*>(v_flat), flat_row_stride, cu_seqlens,
+                                     static_cast<hipStream_t>(stream)),
+                  "pack_ragged launch");
+}
+
 int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
                       const int32_t* persistent, int C, const int32_t* topk, int K,
                       int topk_offset, int32_t* indptr, int32_t* indices, void* stream) {

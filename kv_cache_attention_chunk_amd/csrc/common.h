@@ -113,6 +113,10 @@ hipError_t launch_persistent_update(const float* qm, const float* km, int B, int
                                    int d, const int32_t* pers, int C_in, int evict_begin,
                                    int evict_count, int C, int32_t* out, float* out_score,
                                    hipStream_t stream);
+hipError_t launch_pack_ragged(const uint16_t* k, const uint16_t* v, int B, int N, int H, int d,
+                              const int64_t* ks, int T, const int32_t* frame_ptr,
+                              int total_frames, const int32_t* src, uint16_t* kf, uint16_t* vf,
+                              int64_t fs, int32_t* cu, hipStream_t stream);
 hipError_t launch_build_kv_index(int rows, int sink_begin, int sink_count,
                                  const int32_t* persistent, int C, int NQB,
                                  const int32_t* topk, int K, int topk_offset,
