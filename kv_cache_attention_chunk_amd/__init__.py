@@ -9,7 +9,7 @@ not load the library; the first call does, and fails if it is not built.
 from .api import (  # noqa: F401
     block_mean, block_score_topk, block_sparse_fwd, build_kv_index, chunk_attn_dual_fwd,
     chunk_attn_fwd,
-    chunk_attn_mixed_fwd, chunk_attn_varlen_fwd, lse_merge, num_blocks, pack_ragged,
+    chunk_attn_mixed_fwd, chunk_attn_varlen_fwd, lse_merge, num_blocks, pack_plan, pack_ragged,
     persistent_update,
     workspace_bytes,
 )
@@ -17,5 +17,5 @@ from .api import (  # noqa: F401
 __all__ = [
     "chunk_attn_fwd", "chunk_attn_dual_fwd", "chunk_attn_varlen_fwd", "chunk_attn_mixed_fwd", "lse_merge",
     "block_mean", "block_score_topk", "build_kv_index", "block_sparse_fwd", "num_blocks",
-    "pack_ragged", "persistent_update", "workspace_bytes",
+    "pack_plan", "pack_ragged", "persistent_update", "workspace_bytes",
 ]

@@ -378,20 +378,11 @@ def persistent_update(q_mean: torch.Tensor, k_mean: torch.Tensor,
     return (out, sc) if return_scores else out
 
 
-def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
-    """Flatten per-head frame selections of a dense cache k, v [B, N, H, d]
-    into k_flat, v_flat [sum of frames * frame_tokens, d] + cu_seqlens.
-    frames[bh] lists head bh's output frames in order; an entry is a source
-    frame id (copied) or a pair (a, b) of frames merged into one (float32
-    average rounded to bf16).  Returns (k_flat, v_flat, cu_seqlens,
-    cu_seqlens_host)."""
-    _bshd("k", k), _bshd("v", v)
-    B, N, H, d = k.shape
-    if k.shape != v.shape or k.stride() != v.stride():
-        raise ValueError("k and v must match in shape and strides")
-    if len(frames) != B * H:
-        raise ValueError("frames must list B*H heads")
-    ptr = np.zeros(B * H + 1, np.int32)
+def pack_plan(frames, device) -> dict:
+    """Device-side frame lists for pack_ragged: frames[bh] lists head bh's
+    output frames in order; an entry is a source frame id (copied) or a pair
+    (a, b) of frames merged into one."""
+    ptr = np.zeros(len(frames) + 1, np.int32)
     src = []
     for bh, fl in enumerate(frames):
         for f in fl:
@@ -399,17 +390,34 @@ def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
             src.append((a, b))
         ptr[bh + 1] = len(src)
     F = len(src)
-    src_d = torch.tensor(np.array(src, np.int32).reshape(-1) if F else np.zeros(2, np.int32),
-                         device=k.device)
-    ptr_d = torch.from_numpy(ptr).to(k.device)
+    src_np = np.array(src, np.int32).reshape(-1) if F else np.zeros(2, np.int32)
+    return {"heads": len(frames), "frames": F, "ptr_host": ptr,
+            "ptr": torch.from_numpy(ptr).to(device), "src": torch.from_numpy(src_np).to(device)}
+
+
+def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
+    """Flatten per-head frame selections of a dense cache k, v [B, N, H, d]
+    into k_flat, v_flat [sum of frames * frame_tokens, d] + cu_seqlens.
+    `frames` is a list per head (see pack_plan) or a plan from pack_plan.
+    Merged frames are the float32 average rounded to bf16.  Returns (k_flat,
+    v_flat, cu_seqlens, cu_seqlens_host)."""
+    _bshd("k", k), _bshd("v", v)
+    B, N, H, d = k.shape
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must match in shape and strides")
+    plan = frames if isinstance(frames, dict) else pack_plan(frames, k.device)
+    if plan["heads"] != B * H:
+        raise ValueError("frames must list B*H heads")
+    F = plan["frames"]
     kf = torch.empty((F * frame_tokens, d), dtype=torch.bfloat16, device=k.device)
     vf = torch.empty_like(kf)
     cu = torch.empty(B * H + 1, dtype=torch.int32, device=k.device)
     st = lib().ca_pack_ragged(k.data_ptr(), v.data_ptr(), B, N, H, d, _st(k), frame_tokens,
-                              ptr_d.data_ptr(), ptr.ctypes.data, F, src_d.data_ptr(),
-                              kf.data_ptr(), vf.data_ptr(), d, cu.data_ptr(), _stream())
+                              plan["ptr"].data_ptr(), plan["ptr_host"].ctypes.data, F,
+                              plan["src"].data_ptr(), kf.data_ptr(), vf.data_ptr(), d,
+                              cu.data_ptr(), _stream())
     check(st)
-    return kf, vf, cu, ptr * frame_tokens
+    return kf, vf, cu, plan["ptr_host"] * frame_tokens
 
 
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
