@@ -50,15 +50,16 @@ def src_hash() -> str:
 
 
 def traffic_from_counters():
-    """HBM bytes per dense launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per dense call (its attention launch plus the split merge of
+    the balanced schedule) from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
     if c.get("attn_fwd_sha256_16") != src_hash():
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(w):
@@ -297,6 +298,13 @@ def main():
                     help="'dense' times the dense kernel alone (for counter runs); 'copy' "
                          "runs a plain 1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["plain", "balanced"], default="plain",
+                    help="dense launch: one workgroup per (head, query tile) (default; what the "
+                         "library picks for a uniform cache) or the key-range split over the "
+                         "resident workgroups")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="with --only dense: keep launching for this many seconds before the "
+                         "timed steps (for power and clock sampling)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload timings (tiny, Wan dense/merge, sparse at three "
                          "top-K ratios, ragged, mixed 40-head)")
@@ -357,7 +365,8 @@ def main():
     lay = wl.sparse_layout(w, args.topk_ratio)
 
     def dense():
-        ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_dense, lse=l_dense)
+        ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_dense, lse=l_dense,
+                          balanced="always" if args.schedule == "balanced" else "never")
 
     def merged():
         for ip, ix, ob, lb, _ in branch:
@@ -397,6 +406,15 @@ def main():
     f_step = f_dense + f_merge + f_sparse if args.only == "step" else f_dense
 
     stream = torch.cuda.current_stream()
+    if args.sustain > 0:
+        t_s = time.perf_counter()
+        n_s = 0
+        while time.perf_counter() - t_s < args.sustain:
+            for _ in range(20):
+                dense()
+            torch.cuda.synchronize()
+            n_s += 20
+        log(f"sustained {n_s} dense launches over {time.perf_counter() - t_s:.1f} s")
     for _ in range(args.warmup):
         dense()
         if args.only == "step":
@@ -453,7 +471,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_fwd_kernel<128,4,dense,bf16>",
+                     "kernel": ("attn_fwd_kernel<128,4,range,bf16> + split_merge_kernel<128,bf16>"
+                                if args.schedule == "balanced" else
+                                "attn_fwd_kernel<128,4,range,bf16>"),
+                     "schedule": args.schedule,
                      "avg_launch_ms": round(t_dense, 4)},
         "kv_gbs": {"dense": round(kv_bytes / (t_dense * 1e-3) / 1e9, 1),
                    "frac_hbm": round(kv_bytes / (t_dense * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

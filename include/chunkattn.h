@@ -50,6 +50,12 @@ enum ca_status {
 
 enum ca_dtype { CA_BF16 = 0, CA_F32 = 1 };
 
+/* key-range split policy of the dense / ragged launches (see
+ * ca_attn_workspace_bytes): taken when it shortens a launch by more than a
+ * fifth (AUTO), never, or whenever it applies (ALWAYS: a workspace is given,
+ * head lengths are known and there is enough work) */
+enum ca_split_policy { CA_SPLIT_AUTO = 0, CA_SPLIT_NEVER = 1, CA_SPLIT_ALWAYS = 2 };
+
 /* per-head cache mode for ca_chunk_attn_mixed_fwd */
 enum ca_head_mode { CA_MODE_DENSE = 0, CA_MODE_BLOCKS = 1, CA_MODE_VARLEN = 2 };
 
@@ -81,10 +87,10 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  * the workgroups leave in the workspace: attention over consecutive key
  * ranges recombined through the LSE state (ISPA page, section 2 item 1).
  * The result is the same attention up to float32 rounding.  The schedule is
- * taken only when it shortens the launch (heads of unequal length, or more
- * query tiles than the device holds at once, not a whole multiple of it);
- * it needs every head's key count on the host (always for the dense cache;
- * for ragged heads only with cu_seqlens_host).  Calls sharing one workspace
+ * taken only when it shortens the launch by more than a fifth by tile count
+ * (chiefly heads of unequal length); it needs every head's key count on the
+ * host (always for the dense cache; for ragged heads only with
+ * cu_seqlens_host).  Calls sharing one workspace
  * must be ordered on one stream.  NULL = no workspace: one workgroup per
  * (head, query tile).
  */
@@ -123,6 +129,7 @@ size_t ca_attn_workspace_bytes(int d);
  *                alias lse_init.
  *   o            [B, Nq, H, d] of o_dtype (CA_BF16 or CA_F32), strides o_strides
  *   lse          float32 [B, H, Nq]; an empty key set gives O = 0, LSE = -inf
+ *   split        a ca_split_policy value (CA_SPLIT_AUTO unless tuning)
  *   workspace,   optional (NULL, 0 allowed), see ca_attn_workspace_bytes; used
  *   workspace_bytes  by the dense cache only (block lists and o_init ignore
  *                it).  A workspace smaller than the schedule needs is
@@ -135,7 +142,7 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
                       int kv_block, int kv_seg, int q_block, int q_seg, float scale,
                       const float* o_init, const int64_t* o_init_strides, const float* lse_init,
-                      void* o, int o_dtype, float* lse,
+                      void* o, int o_dtype, float* lse, int split,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -181,7 +188,7 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
                              int total_kv, int B, int H, int Nq, int d,
                              const int64_t* q_strides, int64_t kv_row_stride,
                              const int64_t* o_strides, float scale,
-                             void* o, int o_dtype, float* lse,
+                             void* o, int o_dtype, float* lse, int split,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -236,7 +243,7 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v,
                             const void* k_flat, const void* v_flat,
                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                             int total_kv, int64_t kv_row_stride, float scale,
-                            void* o, int o_dtype, float* lse,
+                            void* o, int o_dtype, float* lse, int split,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*

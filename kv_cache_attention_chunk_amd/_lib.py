@@ -16,6 +16,7 @@ ABI_VERSION = 2
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
 CA_BF16, CA_F32 = 0, 1
 CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
+CA_SPLIT_AUTO, CA_SPLIT_NEVER, CA_SPLIT_ALWAYS = 0, 1, 2
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -33,15 +34,15 @@ SIGNATURES = {
     "ca_attn_workspace_bytes": (_sz, [_i]),
     "ca_chunk_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
                                _i32p, _i32p, _i, _i, _i, _i, _i, _f, _p, _i64p, _p,
-                               _p, _i, _p, _p, _sz, _p]),
+                               _p, _i, _p, _i, _p, _sz, _p]),
     "ca_chunk_attn_dual_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i32p, _i32p,
                                     _i, _i, _i, _i, _i, _i, _f, _p, _i64p, _p, _p, _i64p, _i,
                                     _p, _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
-                                      _i64p, _i64, _i64p, _f, _p, _i, _p, _p, _sz, _p]),
+                                      _i64p, _i64, _i64p, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
                                      _i32p, _i32p, _i32p, _i, _i, _i, _i, _i, _p, _p,
-                                     _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _p, _sz, _p]),
+                                     _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
                           _i64p, _i64p, _i64p, _p]),
     "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),

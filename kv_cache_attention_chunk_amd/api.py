@@ -80,6 +80,14 @@ def _check_indptr(indptr, BH, Nq, q_block, q_seg):
 
 
 _WS_BYTES = {}
+_SPLIT = {True: _lib.CA_SPLIT_AUTO, "auto": _lib.CA_SPLIT_AUTO, False: _lib.CA_SPLIT_NEVER,
+          "never": _lib.CA_SPLIT_NEVER, "always": _lib.CA_SPLIT_ALWAYS}
+
+
+def _split(balanced) -> int:
+    if balanced not in _SPLIT:
+        raise ValueError("balanced must be True/'auto', False/'never' or 'always'")
+    return _SPLIT[balanced]
 
 
 def workspace_bytes(d: int) -> int:
@@ -131,8 +139,10 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     With (o_init float32 [B,Nq,H,d], lse_init [B,H,Nq]) from attention over a
     disjoint key set, the result is their LSE merge with this key set.
     The output dtype is out_dtype, else out's dtype, else bf16.  `balanced`
-    lets a dense launch split key ranges evenly over the device's resident
-    workgroups (a workspace is allocated for it)."""
+    is the key-range split policy of a dense launch: True/'auto' (split key
+    ranges evenly over the device's resident workgroups when that shortens
+    the launch by more than a fifth), False/'never', or 'always' (whenever it
+    applies); a workspace is allocated for it unless one is given."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q), _bshd("k", k), _bshd("v", v)
     B, Nq, H, d = q.shape
@@ -157,7 +167,7 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                 not lse_init.is_contiguous():
             raise ValueError("lse_init must be contiguous float32 [B, H, Nq]")
     ws, wsb = (None, 0)
-    if balanced and kv_indptr is None and o_init is None:
+    if _split(balanced) != _lib.CA_SPLIT_NEVER and kv_indptr is None and o_init is None:
         ws, wsb = _workspace(d, q.device, workspace)
     st = lib().ca_chunk_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d,
@@ -165,7 +175,7 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
         _ptr(kv_indptr), _ptr(kv_indices), nnz, kv_block, kv_seg or max(Nkv, 1),
         q_block, q_seg or max(Nq, 1), sc, _ptr(o_init),
         None if o_init is None else _st(o_init), _ptr(lse_init),
-        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _split(balanced), _ptr(ws), wsb, _stream())
     check(st)
     return o, l
 
@@ -228,12 +238,13 @@ def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.T
     o = _out(B, Nq, H, d, out_dtype, q.device, out)
     l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    ws, wsb = _workspace(d, q.device, workspace) if (balanced and host is not None) else (None, 0)
+    use = _split(balanced) != _lib.CA_SPLIT_NEVER and host is not None
+    ws, wsb = _workspace(d, q.device, workspace) if use else (None, 0)
     st = lib().ca_chunk_attn_varlen_fwd(
         q.data_ptr(), k_flat.data_ptr(), v_flat.data_ptr(), cu_seqlens.data_ptr(),
         None if host is None else host.ctypes.data, k_flat.shape[0], B, H, Nq, d,
         _st(q), k_flat.stride(0) if k_flat.numel() else d, _st(o), sc,
-        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
+        o.data_ptr(), _DT[out_dtype], l.data_ptr(), _split(balanced), _ptr(ws), wsb, _stream())
     check(st)
     return o, l
 
@@ -267,7 +278,8 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
     l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     kvs = _st(k) if k is not None else strides3((0, 0, 0))
-    ws, wsb = _workspace(d, q.device, workspace) if balanced else (None, 0)
+    use = _split(balanced) != _lib.CA_SPLIT_NEVER
+    ws, wsb = _workspace(d, q.device, workspace) if use else (None, 0)
     st = lib().ca_chunk_attn_mixed_fwd(
         q.data_ptr(), _ptr(k), _ptr(v), B, H, Nq, Nkv, d, _st(q), kvs,
         _st(o), mode.ctypes.data, _ptr(kv_indptr), _ptr(kv_indices),
@@ -275,7 +287,8 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
         q_block, q_seg or max(Nq, 1), _ptr(k_flat), _ptr(v_flat), _ptr(cu_seqlens),
         None if host is None else host.ctypes.data,
         0 if k_flat is None else k_flat.shape[0], d if k_flat is None else k_flat.stride(0),
-        sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _ptr(ws), wsb, _stream())
+        sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), _split(balanced), _ptr(ws), wsb,
+        _stream())
     check(st)
     return o, l
 

@@ -139,15 +139,20 @@ size_t workspace_bytes(int slots, int d) {
 // Range mode over a list of head words (b*H + h, | kFlatHead for heads that
 // read the flat buffers).  tiles[i] (host) is head i's key-tile count when
 // known (empty vector: unknown).  With a workspace and known tile counts a
-// launch takes the balanced schedule when that shortens it: the plain grid
-// runs one workgroup per (head, query tile), so its length is set by the
-// longest head and by how many rounds of workgroups the device needs; the
-// balanced grid gives every resident workgroup the same number of key tiles.
+// launch takes the balanced schedule when that shortens it by more than a
+// fifth: the plain grid runs one workgroup per (head, query tile), so its
+// length is set by the longest head and by how many rounds of workgroups the
+// device needs; the balanced grid gives every resident workgroup the same
+// number of key tiles.  The margin is there because the balanced grid reads
+// each head's keys in two phase-shifted streams, which roughly doubles the
+// L2 fill traffic, and because on a uniform cache its gain from filling idle
+// CUs is mostly returned as a lower clock under the power limit.
 int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& words,
-                 const std::vector<int>& tiles, void* ws, size_t ws_bytes, hipStream_t stream) {
+                 const std::vector<int>& tiles, int split, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   const int nh = (int)words.size();
   p.n_qtiles = (c.Nq + kRangeRows - 1) / kRangeRows;
-  const int slots = ws ? attention_slots(c.d) : 0;
+  const int slots = (ws && split != CA_SPLIT_NEVER) ? attention_slots(c.d) : 0;
   for (int h0 = 0; h0 < nh;) {
     int n = std::min(kMaxHeadsPerLaunch, nh - h0);
     p.sched = 0;
@@ -165,8 +170,8 @@ int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& wo
       const int64_t est_plain = (items + slots - 1) / slots * (int64_t)max_nt;
       const int64_t est_bal = g > 0 ? (units + g - 1) / g + 2 : INT64_MAX;
       // (the merge grid has 16 workgroups per query tile; keep it in range)
-      if (units <= 0x7FFFFFFF && items * 16 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 &&
-          est_bal * 20 < est_plain * 19) {
+      const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 5 < est_plain * 4;
+      if (units <= 0x7FFFFFFF && items * 16 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
         if (ws_bytes < workspace_bytes((int)g, c.d))
           return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
                       ws_bytes, workspace_bytes((int)g, c.d));
@@ -195,7 +200,8 @@ int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& wo
   return ok();
 }
 
-int check_workspace(const void* ws, size_t ws_bytes) {
+int check_workspace(int split, const void* ws, size_t ws_bytes) {
+  if (split < CA_SPLIT_AUTO || split > CA_SPLIT_ALWAYS) return fail(CA_EINVAL, "split policy %d", split);
   if (ws && !aligned16(ws)) return fail(CA_EINVAL, "workspace must be 16-byte aligned");
   if (!ws && ws_bytes) return fail(CA_EINVAL, "workspace_bytes given without a workspace");
   return CA_OK;
@@ -270,11 +276,11 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
                       const int32_t* kv_indices, int kv_nnz, int kv_block, int kv_seg,
                       int q_block, int q_seg, float scale, const float* o_init,
                       const int64_t* o_init_strides, const float* lse_init, void* o,
-                      int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      int o_dtype, float* lse, int split, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
-  if (int r = check_workspace(workspace, workspace_bytes)) return r;
+  if (int r = check_workspace(split, workspace, workspace_bytes)) return r;
   if ((o_init == nullptr) != (lse_init == nullptr))
     return fail(CA_EINVAL, "o_init and lse_init must be given together");
   if (o_init) {
@@ -314,7 +320,7 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
   std::vector<uint16_t> words(B * H);
   std::iota(words.begin(), words.end(), 0);
   const std::vector<int> tiles(Nkv > 0 ? B * H : 0, (Nkv + kTileKeys - 1) / kTileKeys);
-  return launch_range(c, p, words, tiles, workspace, workspace_bytes,
+  return launch_range(c, p, words, tiles, split, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -359,11 +365,11 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
                              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                              int total_kv, int B, int H, int Nq, int d, const int64_t* q_strides,
                              int64_t kv_row_stride, const int64_t* o_strides, float scale,
-                             void* o, int o_dtype, float* lse, void* workspace,
+                             void* o, int o_dtype, float* lse, int split, void* workspace,
                              size_t workspace_bytes, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
-  if (int r = check_workspace(workspace, workspace_bytes)) return r;
+  if (int r = check_workspace(split, workspace, workspace_bytes)) return r;
   if (!cu_seqlens) return fail(CA_EINVAL, "cu_seqlens must be non-NULL");
   if (total_kv > 0 && (!k_flat || !v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be non-NULL");
   if (!aligned16(k_flat) || !aligned16(v_flat)) return fail(CA_EINVAL, "k_flat, v_flat must be 16-byte aligned");
@@ -399,7 +405,7 @@ int ca_chunk_attn_varlen_fwd(const void* q, const void* k_flat, const void* v_fl
   } else {
     for (int bh : all) words.push_back((uint16_t)(bh | kFlatHead));
   }
-  return launch_range(c, p, words, tiles, workspace, workspace_bytes,
+  return launch_range(c, p, words, tiles, split, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -410,11 +416,11 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
                             int kv_block, int kv_seg, int q_block, int q_seg,
                             const void* k_flat, const void* v_flat, const int32_t* cu_seqlens,
                             const int32_t* cu_seqlens_host, int total_kv, int64_t kv_row_stride,
-                            float scale, void* o, int o_dtype, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            float scale, void* o, int o_dtype, float* lse, int split,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
   if (int r = check_common(c)) return r;
-  if (int r = check_workspace(workspace, workspace_bytes)) return r;
+  if (int r = check_workspace(split, workspace, workspace_bytes)) return r;
   if (!head_mode) return fail(CA_EINVAL, "head_mode is NULL");
   std::vector<int> hd, hb, hv;
   for (int i = 0; i < B * H; ++i) {
@@ -475,7 +481,7 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
       if (known)
         tiles.push_back((cu_seqlens_host[bh + 1] - cu_seqlens_host[bh] + kTileKeys - 1) / kTileKeys);
     }
-    if (int r = launch_range(c, p, words, tiles, workspace, workspace_bytes, s)) return r;
+    if (int r = launch_range(c, p, words, tiles, split, workspace, workspace_bytes, s)) return r;
   }
   if (!hb.empty()) {
     p = AttnParams{};

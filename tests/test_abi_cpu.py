@@ -46,12 +46,13 @@ def test_num_blocks(L):
 def fwd(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=12, Nq=4680, Nkv=32760, d=128, qs=S, kvs=S, os=S,
              indptr=None, indices=None, nnz=0, kb=64, ks=1560, qb=64, qseg=1560, scale=0.088,
-             oi=None, ois=None, li=None, o=FAKE, odt=0, lse=FAKE, ws=None, wsb=0, stream=None)
+             oi=None, ois=None, li=None, o=FAKE, odt=0, lse=FAKE, split=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return L.ca_chunk_attn_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["Nq"], a["Nkv"], a["d"],
                                a["qs"], a["kvs"], a["os"], a["indptr"], a["indices"], a["nnz"],
                                a["kb"], a["ks"], a["qb"], a["qseg"], a["scale"], a["oi"], a["ois"],
-                               a["li"], a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], a["stream"])
+                               a["li"], a["o"], a["odt"], a["lse"], a["split"], a["ws"], a["wsb"],
+                               a["stream"])
 
 
 def test_attention_argument_errors(L):
@@ -71,6 +72,7 @@ def test_attention_argument_errors(L):
     assert fwd(L, kvs=strides3((0, 64, 8))) == CA_ERANGE        # row stride below d
     assert fwd(L, ws=FAKE + 8, wsb=1 << 20) == CA_EINVAL         # misaligned workspace
     assert fwd(L, ws=None, wsb=1 << 20) == CA_EINVAL             # size without a workspace
+    assert fwd(L, split=3) == CA_EINVAL                          # unknown split policy
     fwd(L, d=96)
     assert b"head dim 96" in L.ca_last_error()
 
@@ -86,16 +88,16 @@ def test_varlen_host_checks(L):
     cu = np.array([0, 10, 5], dtype=np.int32)
     st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu.ctypes.data, 100, 1, 2, 16, 64,
                                     strides3((16 * 2 * 64, 128, 64)), 64,
-                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None, 0, None)
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL
     cu = np.array([0, 10, 500], dtype=np.int32)
     st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, cu.ctypes.data, 100, 1, 2, 16, 64,
                                     strides3((16 * 2 * 64, 128, 64)), 64,
-                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None, 0, None)
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_ERANGE
     st = L.ca_chunk_attn_varlen_fwd(FAKE, FAKE, FAKE, FAKE, None, 100, 1, 2, 16, 64,
                                     strides3((16 * 2 * 64, 128, 64)), 60,
-                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, None, 0, None)
+                                    strides3((16 * 2 * 64, 128, 64)), 0.125, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL
 
 
@@ -103,12 +105,12 @@ def test_mixed_mode_checks(L):
     bad = np.array([0, 3], dtype=np.int32)
     st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, bad.ctypes.data,
                                    None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
-                                   0.1, FAKE, 0, FAKE, None, 0, None)
+                                   0.1, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL
     blocks = np.array([1, 1], dtype=np.int32)
     st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, blocks.ctypes.data,
                                    None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
-                                   0.1, FAKE, 0, FAKE, None, 0, None)
+                                   0.1, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL        # block heads without a CSR
 
 

@@ -130,3 +130,17 @@ def test_workspace_too_small_is_rejected():
     ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError, match="workspace"):
         ca.chunk_attn_fwd(q, k, k, workspace=ws)
+
+
+def test_balanced_forced_on_the_wan_layer():
+    say("balanced schedule forced on the Wan dense layer")
+    w = wl.wan_dense(seed=0)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    ws = _nan_ws(w.d)
+    o, l = ca.chunk_attn_fwd(q, k, v, scale=w.scale, balanced="always", workspace=ws)
+    torch.cuda.synchronize()
+    assert _touched(ws), "balanced schedule not taken"
+    rows = np.r_[0:40, 2300:2330, 4600:4680]
+    Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale, rows=rows)
+    assert_o(o[:, rows], Or, True, "wan balanced")
+    assert_lse(l[:, :, rows], Lr, "wan balanced")
