@@ -20,7 +20,10 @@ against the pages by eye:
   indices -- Pyramid Forcing page, section 3 "ragged-cache attention";
 * block representatives (one token per block: the mean) and coarse scoring
   by representative dot products, followed by exact top-K -- Sparse Forcing
-  page, section 2 item 2 and item 1 "memory management".
+  page, section 2 item 2 and item 1 "memory management", including the
+  persistent-set update when blocks leave the local window;
+* per-head frame selections and adjacent-frame merges packed into flat
+  buffers with boundary indices -- Pyramid Forcing page, sections 2-3.
 
 Floating point: inputs are bf16 values given as exactly equal float32 arrays;
 attention, merge and block means are computed in float64.  Where a floating
