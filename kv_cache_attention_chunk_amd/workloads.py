@@ -268,6 +268,29 @@ def mixed(seed: int = 0, H: int = 40, d: int = 128, frames_q: int = CHUNK_FRAMES
     return w
 
 
+def wan_mla(seed: int = 0, H: int = 12, d_nope: int = 96, d_rope: int = 32, d_c: int = 192,
+            d_v: int = 128, frames_q: int = CHUNK_FRAMES, frames_kv: int = CACHE_FRAMES,
+            frame_tokens: int = FRAME_TOKENS) -> Dict:
+    """Latent-KV (VideoMLA page, method) layer at the Wan-1.3B shape: per
+    token a shared content latent (d_c = 192) and one shared rotated position
+    key (d_rope = 32) -- 224 cached values per token instead of 2 x 12 x 128 --
+    and per-head up-projections.  bf16 N(0,1) queries, latents and position
+    keys; random up-projections N(0, 1/d_c), so reconstructed keys and values
+    have unit variance (no trained weights exist here; they are not needed
+    for kernel parity).  The latent cache is one [B, N, d_c + d_rope] array
+    (content latent first); `c_kv` and `k_rope` are its two column ranges."""
+    B = 1
+    rng = np.random.default_rng(seed)
+    Nq, Nkv = frames_q * frame_tokens, frames_kv * frame_tokens
+    q = _normal_bf16(rng, (B, Nq, H, d_nope + d_rope))
+    kv_lat = _normal_bf16(rng, (B, Nkv, d_c + d_rope))
+    w_uk = Bf16Tensor.from_f32(rng.standard_normal((H, d_nope, d_c), dtype=np.float32) / np.sqrt(d_c))
+    w_uv = Bf16Tensor.from_f32(rng.standard_normal((H, d_v, d_c), dtype=np.float32) / np.sqrt(d_c))
+    return {"B": B, "H": H, "Nq": Nq, "Nkv": Nkv, "d_nope": d_nope, "d_rope": d_rope,
+            "d_c": d_c, "d_v": d_v, "q": q, "kv_lat": kv_lat, "w_uk": w_uk, "w_uv": w_uv,
+            "scale": 1.0 / np.sqrt(d_nope + d_rope), "seed": seed}
+
+
 def kv_cache_bytes(H: int, d: int, tokens: int, layers: int, elem_bytes: int = 2) -> int:
     """Bytes of a per-head dense K+V cache for `layers` layers."""
     return 2 * H * d * elem_bytes * tokens * layers

@@ -7,6 +7,6 @@ with the HIP path.
 from .chunk_attention import (  # noqa: F401
     NEG_INF, attention, block_mean, block_score_topk, block_spans, block_tokens,
     build_kv_index, chunk_attn_blocks, chunk_attn_dense, chunk_attn_varlen,
-    chunk_mean_query, lse_merge, lse_merge_bshd, pack_ragged, persistent_update,
+    chunk_mean_query, lse_merge, lse_merge_bshd, mla_chunk_attn, pack_ragged, persistent_update,
     sparse_selection,
 )

@@ -220,6 +220,38 @@ def pack_ragged(k_bits, v_bits, frame_ptr, frame_src, frame_tokens: int):
 
 
 # ---------------------------------------------------------------------------
+# Latent KV cache (VideoMLA page, method): the cache keeps per token a content
+# latent c_t (d_c values shared by all heads) and one rotated position key
+# k^R_t (d_rope values, shared by all heads).  Head h reconstructs its keys
+# and values on demand with up-projections: k_{t,h} = [W^K_h c_t ; k^R_t]
+# (content part d_nope = W^K_h's rows, position part d_rope) and
+# v_{t,h} = W^V_h c_t.  Queries carry the same split [q^nope ; q^R].
+# ---------------------------------------------------------------------------
+def mla_chunk_attn(q, c_kv, k_rope, w_uk, w_uv, scale: float, rows=None, heads=None):
+    """q [B, Nq, H, d_nope + d_rope], c_kv [B, N, d_c], k_rope [B, N, d_rope],
+    w_uk [H, d_nope, d_c], w_uv [H, d_v, d_c] -> O [B, R, H', d_v], LSE
+    [B, H', R]: for each head the keys and values are reconstructed from the
+    latent cache and attended with plain softmax attention."""
+    q = np.asarray(q, dtype=np.float64)
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    k_rope = np.asarray(k_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Nq, H, _ = q.shape
+    r = _rows(Nq, rows)
+    hs = list(range(H)) if heads is None else list(heads)
+    d_v = w_uv.shape[1]
+    O = np.zeros((B, len(r), len(hs), d_v))
+    L = np.full((B, len(hs), len(r)), NEG_INF)
+    for b in range(B):
+        for j, h in enumerate(hs):
+            k_h = np.concatenate([c_kv[b] @ w_uk[h].T, k_rope[b]], axis=1)   # [N, d_nope + d_rope]
+            v_h = c_kv[b] @ w_uv[h].T                                         # [N, d_v]
+            O[b, :, j], L[b, j] = attention(q[b, r, h], k_h, v_h, scale)
+    return O, L
+
+
+# ---------------------------------------------------------------------------
 # LSE merge (ISPA page, section 2 item 1: local and history branches combined
 # after the fact through their LSE states).
 # ---------------------------------------------------------------------------

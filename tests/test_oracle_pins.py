@@ -614,3 +614,89 @@ def test_planted_packing_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oc, "pack_ragged", swapped_heads)
     with pytest.raises(AssertionError):
         test_pack_ragged_copies_equal_the_gathered_frames()
+
+
+# ---------------------------------------------------------------------------
+# latent KV cache (VideoMLA page, method)
+# ---------------------------------------------------------------------------
+def _mla_inputs(rng, B=1, Nq=5, N=9, H=2, dn=3, dr=2, dc=4, dv=3):
+    q = rng.standard_normal((B, Nq, H, dn + dr))
+    c = rng.standard_normal((B, N, dc))
+    kr = rng.standard_normal((B, N, dr))
+    wk = rng.standard_normal((H, dn, dc))
+    wv = rng.standard_normal((H, dv, dc))
+    return q, c, kr, wk, wv
+
+
+def test_mla_matches_bruteforce_loops():
+    rng = np.random.default_rng(41)
+    q, c, kr, wk, wv = _mla_inputs(rng)
+    sc = 0.7
+    O, L = oc.mla_chunk_attn(q, c, kr, wk, wv, sc)
+    B, Nq, H, _ = q.shape
+    N, dn, dv = c.shape[1], wk.shape[1], wv.shape[1]
+    for h in range(H):
+        for i in range(Nq):
+            s = []
+            for t in range(N):
+                k_nope = [math.fsum(wk[h, a, e] * c[0, t, e] for e in range(c.shape[2])) for a in range(dn)]
+                key = k_nope + list(kr[0, t])
+                s.append(sc * math.fsum(float(q[0, i, h, a]) * key[a] for a in range(len(key))))
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            l = math.fsum(w)
+            assert abs(L[0, h, i] - (m + math.log(l))) < 1e-12
+            for a in range(dv):
+                v = [math.fsum(wv[h, a, e] * c[0, t, e] for e in range(c.shape[2])) for t in range(N)]
+                assert abs(O[0, i, h, a] - math.fsum(wi * vi for wi, vi in zip(w, v)) / l) < 1e-12
+
+
+def test_mla_selector_projections_reduce_to_plain_attention():
+    # W^K = [I | 0] and W^V = [0 | I] pick latent columns: keys = [c[:, :dn], k^R],
+    # values = c[:, dc-dv:], i.e. ordinary attention over explicit arrays
+    rng = np.random.default_rng(42)
+    dn, dr, dc, dv = 3, 2, 6, 4
+    q, c, kr, _, _ = _mla_inputs(rng, dn=dn, dr=dr, dc=dc, dv=dv)
+    wk = np.zeros((2, dn, dc)); wv = np.zeros((2, dv, dc))
+    for h in range(2):
+        wk[h, :, :dn] = np.eye(dn)
+        wv[h, :, dc - dv:] = np.eye(dv)
+    O, L = oc.mla_chunk_attn(q, c, kr, wk, wv, 0.5)
+    for h in range(2):
+        K = np.concatenate([c[0, :, :dn], kr[0]], axis=1)
+        Oref, Lref = oc.attention(q[0, :, h], K, c[0, :, dc - dv:], 0.5)
+        assert np.allclose(O[0, :, h], Oref, atol=1e-12) and np.allclose(L[0, h], Lref, atol=1e-12)
+
+
+def test_mla_absorbed_query_form_is_equivalent():
+    # scores through the absorbed query (W^K_h)^T q^nope against the latent,
+    # and outputs through the up-projection of the latent-weighted mean
+    rng = np.random.default_rng(43)
+    dn, dr = 3, 2
+    q, c, kr, wk, wv = _mla_inputs(rng, dn=dn, dr=dr)
+    O, L = oc.mla_chunk_attn(q, c, kr, wk, wv, 0.9)
+    for h in range(2):
+        qt = q[0, :, h, :dn] @ wk[h]                         # [Nq, dc]
+        s = 0.9 * (qt @ c[0].T + q[0, :, h, dn:] @ kr[0].T)
+        lse = special.logsumexp(s, axis=1)
+        p = np.exp(s - lse[:, None])
+        assert np.allclose(L[0, h], lse, atol=1e-12)
+        assert np.allclose(O[0, :, h], (p @ c[0]) @ wv[h].T, atol=1e-12)
+
+
+def test_planted_mla_mistakes_are_caught(monkeypatch):
+    real = oc.mla_chunk_attn
+
+    def permuted_values(q, c, kr, wk, wv, sc, **kw):
+        # value up-projection rows in the wrong order
+        return real(q, c, kr, wk, np.asarray(wv)[:, ::-1, :], sc, **kw)
+    monkeypatch.setattr(oc, "mla_chunk_attn", permuted_values)
+    with pytest.raises(AssertionError):
+        test_mla_absorbed_query_form_is_equivalent()
+    monkeypatch.undo()
+
+    def rope_dropped(q, c, kr, wk, wv, sc, **kw):
+        return real(q, c, np.zeros_like(kr), wk, wv, sc, **kw)
+    monkeypatch.setattr(oc, "mla_chunk_attn", rope_dropped)
+    with pytest.raises(AssertionError):
+        test_mla_matches_bruteforce_loops()
