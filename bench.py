@@ -243,6 +243,20 @@ def per_config(reps=10, wan=None):
                           "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del q, kf, vf, kd, vd
+    # latent KV cache (d_c = 192, d_rope = 32): absorbed query, latent
+    # attention, per-head up-projection
+    m = wl.wan_mla(seed=0)
+    mq, mwk, mwv = dev(m["q"]), dev(m["w_uk"]), dev(m["w_uv"])
+    mkv = ca.cast_bf16_to_f16(dev(m["kv_lat"]))
+    ms_all = _time_ms(torch, lambda: ca.mla_chunk_attn(mq, mkv, mwk, mwv, scale=m["scale"]), reps)
+    rows = m["Nq"] * m["H"]
+    f_att = 2.0 * rows * m["Nkv"] * (224 + 192)
+    f_proj = 2.0 * rows * (96 * 192 + 192 * 128)
+    kvb = m["Nkv"] * 224 * 2.0
+    out["wan_mla"] = _rec(ms_all, f_att + f_proj, kvb, attention_gflop=round(f_att / 1e9, 1),
+                          projection_gflop=round(f_proj / 1e9, 1),
+                          kv_bytes_vs_dense=round(kvb / (2.0 * m["Nkv"] * m["H"] * 128 * 2), 4))
+    del mq, mwk, mwv, mkv
     # mixed 40-head layer (dense / block lists / ragged per head)
     w = wl.mixed(seed=0)
     lay = w.meta["sparse"]

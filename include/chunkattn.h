@@ -318,6 +318,52 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
                          int C, int32_t* out, float* out_score, void* stream);
 
 /*
+ * Latent KV cache (VideoMLA page, method).  The cache keeps per token one
+ * content latent c_t (d_c = 192 values) and one rotated position key k^R_t
+ * (d_rope = 32), shared by all heads, stored together as one row [c_t ; k^R_t]
+ * of 224 fp16 values; head h's keys and values are [W^K_h c_t ; k^R_t] and
+ * W^V_h c_t (d_nope = 96 + d_rope = 32 key values, d_v = 128 value values).
+ * Attention runs in the absorbed form: the query's content part is projected
+ * into the latent space, all (query, head) rows attend to the same latent
+ * rows, and the latent-space output is projected per head:
+ *   ca_mla_absorb_q  q_lat = [(W^K_h)^T q^nope ; q^R]          (fp16)
+ *   ca_mla_attn_fwd  o_lat = sum_t softmax_t(scale q_lat . kv_t) c_t, LSE
+ *   ca_mla_up_proj   o = W^V_h o_lat
+ * which equals attention with the reconstructed per-head keys and values
+ * (associativity).  The pages' configuration d_c = 192, d_rope = 32 (d_nope =
+ * 96, d_v = 128) is the one supported; other sizes are CA_EUNSUPPORTED.
+ *
+ * ca_mla_absorb_q
+ *   q      bf16 [B, Nq, H, 128] (q^nope = first 96 values, q^R = last 32),
+ *          element strides q_strides (host), values contiguous
+ *   w_uk   bf16 [H, 96, 192] (W^K_h: latent -> content key), contiguous
+ *   q_lat  fp16 [B, Nq, H, 224] contiguous output (float32 accumulation,
+ *          one rounding to fp16)
+ * ca_mla_attn_fwd
+ *   q_lat  fp16 [B, Nq, H, 224] contiguous (from ca_mla_absorb_q)
+ *   kv_lat fp16 latent rows [c ; k^R] (224 values): row t of batch entry b at
+ *          kv_lat + b kv_batch_stride + t kv_row_stride (elements; the row
+ *          stride a multiple of 8 and >= 224); a bf16 cache converts with
+ *          ca_cast_bf16_to_f16 (exact for values in fp16's normal range)
+ *   scale  softmax scale (1/sqrt(128) for the pages' model)
+ *   o_lat  float32 [B, Nq, H, 192] contiguous; lse float32 [B, H, Nq]
+ *          (natural log; no keys -> o_lat = 0, LSE = -inf)
+ * ca_mla_up_proj
+ *   o_lat  as above; w_uv bf16 [H, 128, 192] (W^V_h), contiguous
+ *   o      [B, Nq, H, 128] of o_dtype (CA_BF16 or CA_F32), strides o_strides
+ * ca_cast_bf16_to_f16: y[i] = fp16 round-to-nearest-even of bf16 x[i], n a
+ *   multiple of 8, both 16-byte aligned.
+ */
+int ca_mla_absorb_q(const void* q, int B, int Nq, int H, int d_nope, int d_rope, int d_c,
+                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* stream);
+int ca_mla_attn_fwd(const void* q_lat, const void* kv_lat, int B, int Nq, int H, int Nkv, int d_c,
+                    int d_rope, int64_t kv_batch_stride, int64_t kv_row_stride, float scale,
+                    float* o_lat, float* lse, void* stream);
+int ca_mla_up_proj(const float* o_lat, const void* w_uv, int B, int Nq, int H, int d_c, int d_v,
+                   void* o, int o_dtype, const int64_t* o_strides, void* stream);
+int ca_cast_bf16_to_f16(const void* x, void* y, int64_t n, void* stream);
+
+/*
  * PBSA block lists (Sparse Forcing page, section 2 item 3): CSR row
  * (b*H + h)*NQB + qb = sorted union, duplicates removed, of the sink blocks
  * [sink_begin, sink_begin + sink_count), persistent[b,h,:] (C ids, ascending,

@@ -50,6 +50,10 @@ SIGNATURES = {
     "ca_persistent_update": (_i, [_p, _p, _i, _i, _i, _i, _i32p, _i, _i, _i, _i, _p, _p, _p]),
     "ca_pack_ragged": (_i, [_p, _p, _i, _i, _i, _i, _i64p, _i, _i32p, _i32p, _i, _i32p, _p, _p,
                             _i64, _p, _p]),
+    "ca_mla_absorb_q": (_i, [_p, _i, _i, _i, _i, _i, _i, _i64p, _p, _p, _p]),
+    "ca_mla_attn_fwd": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _f, _p, _p, _p]),
+    "ca_mla_up_proj": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _i, _i64p, _p]),
+    "ca_cast_bf16_to_f16": (_i, [_p, _p, _i64, _p]),
     "ca_build_kv_index": (_i, [_i, _i, _i, _i, _i, _i32p, _i, _i32p, _i, _i, _p, _p, _p]),
 }
 

@@ -433,6 +433,46 @@ def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
     return kf, vf, cu, plan["ptr_host"] * frame_tokens
 
 
+def cast_bf16_to_f16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16 copy (round to nearest even) of a contiguous bf16 GPU tensor."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 GPU tensor")
+    y = torch.empty(x.shape, dtype=torch.float16, device=x.device) if out is None else out
+    check(lib().ca_cast_bf16_to_f16(x.data_ptr(), y.data_ptr(), x.numel(), _stream()))
+    return y
+
+
+def mla_chunk_attn(q: torch.Tensor, kv_lat: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                   *, scale: Optional[float] = None, out_dtype=torch.bfloat16):
+    """Chunk attention over a latent KV cache (d_c = 192, d_rope = 32):
+    q bf16 [B, Nq, H, 128] (content 96 + position 32), kv_lat fp16
+    [B, N, 224] (rows [c ; k^R]), w_uk bf16 [H, 96, 192], w_uv bf16
+    [H, 128, 192].  Absorbs W^K into the queries, attends every (query, head)
+    row to the latent rows, projects with W^V.  Returns (o, lse, o_lat)."""
+    _bshd("q", q)
+    B, Nq, H, dq = q.shape
+    if kv_lat.dtype != torch.float16 or kv_lat.dim() != 3 or kv_lat.shape[0] != B or \
+            kv_lat.shape[2] != 224 or kv_lat.stride(2) != 1:
+        raise ValueError("kv_lat must be fp16 [B, N, 224] with contiguous rows")
+    for n, w, shp in (("w_uk", w_uk, (H, 96, 192)), ("w_uv", w_uv, (H, 128, 192))):
+        if w.dtype != torch.bfloat16 or tuple(w.shape) != shp or not w.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous bf16 tensor {shp}")
+    N = kv_lat.shape[1]
+    sc = 1.0 / math.sqrt(dq) if scale is None else float(scale)
+    q_lat = torch.empty((B, Nq, H, 224), dtype=torch.float16, device=q.device)
+    check(lib().ca_mla_absorb_q(q.data_ptr(), B, Nq, H, 96, dq - 96, 192, _st(q), w_uk.data_ptr(),
+                                q_lat.data_ptr(), _stream()))
+    o_lat = torch.empty((B, Nq, H, 192), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    check(lib().ca_mla_attn_fwd(q_lat.data_ptr(), kv_lat.data_ptr(), B, Nq, H, N, 192, 32,
+                                kv_lat.stride(0) if N else 0, kv_lat.stride(1) if N else 224, sc,
+                                o_lat.data_ptr(), lse.data_ptr(), _stream()))
+    o = torch.empty((B, Nq, H, 128), dtype=out_dtype, device=q.device)
+    check(lib().ca_mla_up_proj(o_lat.data_ptr(), w_uv.data_ptr(), B, Nq, H, 192, 128, o.data_ptr(),
+                               _DT[out_dtype], _st(o), _stream()))
+    return o, lse, o_lat
+
+
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
                    persistent: Optional[torch.Tensor], topk: Optional[torch.Tensor],
                    topk_offset: int = 0, device=None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -611,6 +611,76 @@ int ca_pack_ragged(const void* k, const void* v, int B, int N, int H, int d,
                   "pack_ragged launch");
 }
 
+// ---- latent KV cache (VideoMLA page, method) --------------------------------
+namespace {
+constexpr int kMlaNope = 96, kMlaRope = 32, kMlaLat = 192, kMlaVal = 128;
+
+int check_mla_dims(int d_nope, int d_rope, int d_c, int d_v) {
+  if (d_nope != kMlaNope || d_rope != kMlaRope || d_c != kMlaLat || d_v != kMlaVal)
+    return fail(CA_EUNSUPPORTED, "latent dims (d_nope %d, d_rope %d, d_c %d, d_v %d); supported: 96, 32, 192, 128",
+                d_nope, d_rope, d_c, d_v);
+  return CA_OK;
+}
+}  // namespace
+
+int ca_mla_absorb_q(const void* q, int B, int Nq, int H, int d_nope, int d_rope, int d_c,
+                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* stream) {
+  if (B < 0 || Nq < 0 || H < 0) return fail(CA_EINVAL, "negative size");
+  if (int r = check_mla_dims(d_nope, d_rope, d_c, kMlaVal)) return r;
+  if (!q || !w_uk || !q_lat) return fail(CA_EINVAL, "NULL pointer");
+  if (int r = check_strides("q", q_strides, 1)) return r;
+  if ((int64_t)B * Nq * H > 0x7FFFFFFF / 256) return fail(CA_ERANGE, "too many rows");
+  if (int r = check_device()) return r;
+  return launched(launch_mla_absorb(static_cast<const uint16_t*>(q), B, Nq, H, q_strides,
+                                    static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_lat),
+                                    static_cast<hipStream_t>(stream)),
+                  "mla absorb launch");
+}
+
+int ca_mla_attn_fwd(const void* q_lat, const void* kv_lat, int B, int Nq, int H, int Nkv, int d_c,
+                    int d_rope, int64_t kv_batch_stride, int64_t kv_row_stride, float scale,
+                    float* o_lat, float* lse, void* stream) {
+  if (B < 0 || Nq < 0 || H < 0 || Nkv < 0) return fail(CA_EINVAL, "negative size");
+  if (int r = check_mla_dims(kMlaNope, d_rope, d_c, kMlaVal)) return r;
+  if (!q_lat || !o_lat || !lse || (Nkv > 0 && !kv_lat)) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(q_lat) || !aligned16(kv_lat) || !aligned16(o_lat)) return fail(CA_EINVAL, "q_lat, kv_lat, o_lat must be 16-byte aligned");
+  if (kv_row_stride < d_c + d_rope || kv_row_stride % 8 || kv_row_stride > (1 << 22))
+    return fail(CA_EINVAL, "kv_row_stride must be a multiple of 8 in [d_c + d_rope, 2^22]");
+  if (kv_batch_stride < 0 || kv_batch_stride % 8) return fail(CA_EINVAL, "kv_batch_stride must be a non-negative multiple of 8");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if ((int64_t)Nq * H > 0x7FFFFFFF / 2 || (int64_t)B * ((int64_t)Nq * H + 127) / 128 > 0x7FFFFFFF)
+    return fail(CA_ERANGE, "too many rows");
+  if (int r = check_device()) return r;
+  return launched(launch_mla_attn(static_cast<const uint16_t*>(q_lat), static_cast<const uint16_t*>(kv_lat),
+                                  kv_batch_stride, kv_row_stride, B, Nq, H, Nkv, scale, o_lat, lse,
+                                  static_cast<hipStream_t>(stream)),
+                  "mla attention launch");
+}
+
+int ca_mla_up_proj(const float* o_lat, const void* w_uv, int B, int Nq, int H, int d_c, int d_v,
+                   void* o, int o_dtype, const int64_t* o_strides, void* stream) {
+  if (B < 0 || Nq < 0 || H < 0) return fail(CA_EINVAL, "negative size");
+  if (int r = check_mla_dims(kMlaNope, kMlaRope, d_c, d_v)) return r;
+  if (o_dtype != CA_BF16 && o_dtype != CA_F32) return fail(CA_EUNSUPPORTED, "o_dtype %d", o_dtype);
+  if (!o_lat || !w_uv || !o) return fail(CA_EINVAL, "NULL pointer");
+  if (int r = check_strides("o", o_strides, 1)) return r;
+  if ((int64_t)B * Nq * H > 0x7FFFFFFF / 256) return fail(CA_ERANGE, "too many rows");
+  if (int r = check_device()) return r;
+  return launched(launch_mla_up(o_lat, B, Nq, H, static_cast<const uint16_t*>(w_uv), o, o_dtype == CA_F32,
+                                o_strides, static_cast<hipStream_t>(stream)),
+                  "mla up-projection launch");
+}
+
+int ca_cast_bf16_to_f16(const void* x, void* y, int64_t n, void* stream) {
+  if (n < 0 || n % 8) return fail(CA_EINVAL, "n must be a non-negative multiple of 8");
+  if (n > 0 && (!x || !y)) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(CA_EINVAL, "x, y must be 16-byte aligned");
+  if (int r = check_device()) return r;
+  return launched(launch_cast_bf16_f16(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), n,
+                                       static_cast<hipStream_t>(stream)),
+                  "cast launch");
+}
+
 int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
                       const int32_t* persistent, int C, const int32_t* topk, int K,
                       int topk_offset, int32_t* indptr, int32_t* indices, void* stream) {

@@ -1,0 +1,432 @@
+// Chunk attention over a latent KV cache (VideoMLA page, method): the cache
+// keeps per token one content latent c_t (DC = 192 values) and one rotated
+// position key k^R_t (DR = 32), shared by all heads; head h's keys and values
+// are [W^K_h c_t ; k^R_t] and W^V_h c_t.  Folding W^K_h into the query
+// (q~ = (W^K_h)^T q^nope) and W^V_h into the output turns every (query, head)
+// pair into a row attending to the same latent rows:
+//   s = scale ([q~ ; q^R] . [c_t ; k^R_t]),   o~ = sum_t softmax(s)_t c_t,
+//   o_h = W^V_h o~.
+// Three kernels: the per-head projections (query absorption, value
+// up-projection) and the latent attention.
+//
+// Latent attention (mla_attn_kernel).  One workgroup = 4 waves x 32 rows of
+// one batch entry; rows are (query, head) pairs, so every row of the grid
+// streams the same 64-token latent tiles.  A tile [64 x 224] serves as K (all
+// 224 values) and as V (the first 192).  The operands are fp16: the absorbed
+// query is rounded once to fp16 (11-bit significand; bf16 would put its
+// rounding error on every score), the latent cache is kept in fp16 (a bf16
+// cache converts exactly in its normal range, see ca_cast_bf16_to_f16), and P
+// is rounded to fp16 for the PV product; all accumulation is float32.  Tiles
+// go from global memory to LDS with buffer loads (no staging registers) into
+// rows padded to 512 bytes, two stages.  Chunk c of row r sits at
+// c ^ (4 (r & 3) + ((r >> 2) & 3)): sixteen consecutive rows take sixteen
+// distinct chunk slots (the S = K Q^T operand reads) and four consecutive
+// rows take four disjoint groups of four slots (the transposing V^T reads),
+// so both read patterns are free of bank conflicts.
+#include "common.h"
+
+namespace chunkattn {
+
+namespace {
+
+constexpr int kMlaDC = 192;               // content latent
+constexpr int kMlaDR = 32;                // position key
+constexpr int kMlaDK = kMlaDC + kMlaDR;   // 224 cached values per token
+constexpr int kMlaRowB = 512;             // LDS bytes per latent row (448 used)
+constexpr int kMlaTileB = kTileKeys * kMlaRowB;
+constexpr int kMlaNW = 4;
+constexpr float kLn2f = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ int mla_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+__device__ __forceinline__ float mla_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float mla_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr int kBufWord3 = 0x00020000;      // raw buffer resource, gfx9 family
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ lds_void_t* mla_dma_dst(char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_char_t*)p;
+  return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(a);
+}
+
+struct MlaParams {
+  const uint16_t* q;       // fp16 [B, Nq, H, 224] contiguous (absorbed query ; q^R)
+  const uint16_t* kv;      // fp16 latent rows, 224 values each
+  int64_t kv_bs, kv_rs;    // batch and row strides of kv, elements
+  float* o;                // float32 [B, Nq, H, 192] contiguous
+  float* lse;              // float32 [B, H, Nq]
+  int B, Nq, H, Nkv;
+  int rows_per_b;          // Nq * H
+  int wg_per_b;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(kMlaNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mla_attn_kernel(const MlaParams p) {
+  constexpr int BM = kMlaNW * 32;
+  constexpr int NST = kMlaDK / 16;        // 14 k-steps of S
+  constexpr int NDT = kMlaDC / 32;        // 6 d-tiles of O^T
+  constexpr int CPR = kMlaDK / 8;         // 28 16-byte chunks per latent row
+  constexpr int NLD = kMlaTileB / (1024 * kMlaNW);   // 8 buffer->LDS loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char lat[2 * kMlaTileB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hg = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = item / p.wg_per_b;
+  const int r0 = (item - b * p.wg_per_b) * BM;
+  const int qr = wave * 32 + col;
+  const int rloc = r0 + qr;                          // row within batch entry b
+  const bool qvalid = rloc < p.rows_per_b;
+  const int64_t rglob = (int64_t)b * p.rows_per_b + rloc;
+
+  // Q^T operands: row rloc, values 16 st + 8 hg .. + 8
+  f16x8_t qreg[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (qvalid) x = *reinterpret_cast<const u32x4_t*>(p.q + rglob * kMlaDK + 16 * st + 8 * hg);
+    qreg[st] = __builtin_bit_cast(f16x8_t, x);
+  }
+
+  // Tile loads: wave w's instruction j fills LDS bytes [(NLD w + j) KB, +1 KB),
+  // lane i the 16-byte slot at +16 i = physical row pr, slot ps; it loads
+  // logical chunk ps ^ swz(pr) of latent row pr, or nothing (zeros) for the
+  // padding slots (logical chunk >= 28) and rows past the cache.
+  // Slot of lane i in instruction j: physical row pr = 2 (NLD w + j) + i / 32,
+  // slot ps = i % 32, loading logical chunk ps ^ swz(pr); pr & 15 = (2 j +
+  // i / 32) & 15, so the swizzle depends on j and the lane half only.  Each
+  // instruction's buffer starts at its row pair (a uniform base), whose valid
+  // bytes bound the range check: rows past the cache and padding slots
+  // (logical chunk >= 28, given an out-of-range offset) read as zeros.
+  const uint32_t rs_bytes = (uint32_t)(p.kv_rs * 2);
+  const uint16_t* kvb = p.kv + b * p.kv_bs;
+  const int ntiles = (p.Nkv + kTileKeys - 1) / kTileKeys;
+  auto issue_tile = [&](int t, int stage) {
+    const int valid = p.Nkv - t * kTileKeys < kTileKeys ? p.Nkv - t * kTileKeys : kTileKeys;
+    char* base = lat + stage * kMlaTileB;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int pr0 = 2 * (NLD * wave + j);
+      const int here = valid - pr0;                     // valid rows from pr0 on
+      const int nrec = here >= 2 ? (int)rs_bytes + 2 * kMlaDK : (here == 1 ? 2 * kMlaDK : 0);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kvb + ((int64_t)t * kTileKeys + pr0) * p.kv_rs), (short)0, nrec,
+          kBufWord3);
+      // (the empty asm keeps this offset at the load instead of a live register)
+      int cl = col, h1 = hg;
+      asm volatile("" : "+v"(cl), "+v"(h1));
+      const int c = cl ^ mla_swz(2 * j + h1);
+      const uint32_t voff = c < CPR ? (uint32_t)h1 * rs_bytes + 16u * c : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, mla_dma_dst(base + (NLD * wave + j) * 1024), 16,
+                                               (int)voff, 0, 0, 0);
+    }
+  };
+  auto block_sync = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  f32x16_t acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x16_t{};
+  float m = -INFINITY, l = 0.f;
+
+  if (ntiles > 0) {
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x3F70);     // vmcnt(0)
+    block_sync();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int stg = t & 1;
+    const char* tb = lat + stg * kMlaTileB;
+    // stage stg^1 was last read in iteration t-1, which ended with a barrier
+    if (t + 1 < ntiles) issue_tile(t + 1, stg ^ 1);
+    // S^T = K Q^T for the two 32-key halves
+    f32x16_t sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt] = f32x16_t{};
+      const int r = 32 * kt + col;
+      const char* rp = tb + r * kMlaRowB;
+      const int z = mla_swz(r);
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(rp + 16 * ((2 * st + hg) ^ z));
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[st], sc[kt], 0, 0, 0);
+      }
+    }
+    // online softmax (log2 domain); keys past Nkv are masked
+    const int len = p.Nkv - t * kTileKeys;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
+        if (len < kTileKeys && key >= len) sc[kt][i] = -INFINITY;
+        mx = fmaxf(mx, sc[kt][i]);
+      }
+    mx = mla_half_max(mx) * p.scale_log2;
+    const bool grow = mx > m;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    // O^T += V^T P^T, key group g = 16 keys
+    const int vcol16 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kt = g >> 1, u = g & 1;
+      f32x8_t pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * u + e], p.scale_log2, -m_use));
+        l += pf[e];
+      }
+      const f16x8_t pb = __builtin_convertvector(pf, f16x8_t);
+      // V^T operand rows: key rows 32 kt + 16 u + 4 hg + (lane & 15) / 4 (+ 8),
+      // values 32 dt + 8 vcol16 + 4 (lane & 1)
+      const int vrow = 32 * kt + 16 * u + 4 * hg + ((lane & 15) >> 2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int c = 4 * dt + vcol16;
+        const char* p0 = tb + vrow * kMlaRowB + 16 * (c ^ mla_swz(vrow)) + 8 * (lane & 1);
+        const char* p1 = tb + (vrow + 8) * kMlaRowB + 16 * (c ^ mla_swz(vrow + 8)) + 8 * (lane & 1);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p0)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p1)));
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, acc[dt], 0, 0, 0);
+      }
+    }
+    // tile t+1 landed (own loads), then every wave's loads and reads are done
+    __builtin_amdgcn_s_waitcnt(0x3F70);     // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+    block_sync();
+  }
+
+  const float lt = mla_half_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qvalid) {
+    float* ob = p.o + rglob * kMlaDC;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * dt + 8 * r + 4 * hg;
+        f32x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
+        *reinterpret_cast<f32x4_t*>(ob + d0) = v4;
+      }
+    if (hg == 0) {
+      const int n = rloc / p.H, h = rloc - (rloc / p.H) * p.H;
+      p.lse[((int64_t)b * p.H + h) * p.Nq + n] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
+    }
+  }
+}
+
+// bf16 -> fp16, round to nearest even; 8 values per thread
+__global__ __launch_bounds__(256) void cast_bf16_f16_kernel(const uint16_t* __restrict__ x,
+                                                            uint16_t* __restrict__ y, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4_t v = reinterpret_cast<const u32x4_t*>(x)[i];
+  f32x8_t f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(v[e] << 16);
+    f[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+  }
+  reinterpret_cast<u32x4_t*>(y)[i] = __builtin_bit_cast(u32x4_t, __builtin_convertvector(f, f16x8_t));
+}
+
+// ---------------------------------------------------------------------------
+// Per-head projection: out[r, h, j] = sum_i in[r, h, i] * W(h, i, j) for the
+// rows r of one (b, query) range and head h, float32 accumulation.
+//   W_IN_MAJOR: W stored [H, K, N] (W(h, i, j) = w[h][i][j]) -- the absorbed
+//               query uses (W^K_h)^T, i.e. W^K stored [H, d_nope, d_c]
+//   else:       W stored [H, N, K] (W(h, i, j) = w[h][j][i]) -- the value
+//               up-projection W^V stored [H, d_v, d_c]
+// One workgroup = 64 rows x all N outputs of one head; the weights and the
+// rows are staged in LDS as float32 (bf16 weights are exact in float32).
+// TIN: 0 = bf16 input, 1 = float32 input.  TOUT: 0 = bf16, 1 = float32,
+// 2 = fp16.  Optional tail copy: the input values [K, K + tail) of each row
+// go to outputs [N, N + tail) converted to the output type (the query's
+// position part next to its absorbed content part).
+// ---------------------------------------------------------------------------
+constexpr int kProjRows = 64;
+constexpr int kProjThreads = 256;
+
+struct ProjParams {
+  const void* in;
+  int64_t is_r, is_h;        // input row and head strides (elements); values contiguous
+  const uint16_t* w;         // bf16 weights
+  void* out;
+  int64_t os_r, os_h;
+  int rows, H, K, N, tail;
+};
+
+template <int K, int N, bool W_IN_MAJOR, int TIN, int TOUT>
+__global__ __launch_bounds__(kProjThreads) void head_proj_kernel(const ProjParams p) {
+  __shared__ float ws[K * N];
+  __shared__ float xs[kProjRows * (K + 1)];
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kProjRows;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < K * N; e += kProjThreads) {
+    // ws[i * N + j] = W(h, i, j)
+    const int i = e / N, j = e - (e / N) * N;
+    const uint16_t bits = W_IN_MAJOR ? p.w[((int64_t)h * K + i) * N + j] : p.w[((int64_t)h * N + j) * K + i];
+    ws[e] = __uint_as_float((uint32_t)bits << 16);
+  }
+  for (int e = tid; e < kProjRows * K; e += kProjThreads) {
+    const int rr = e / K, i = e - (e / K) * K;
+    const int r = r0 + rr;
+    float x = 0.f;
+    if (r < p.rows) {
+      const int64_t o = r * p.is_r + h * p.is_h + i;
+      x = TIN == 1 ? reinterpret_cast<const float*>(p.in)[o]
+                   : __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p.in)[o] << 16);
+    }
+    xs[rr * (K + 1) + i] = x;
+  }
+  __syncthreads();
+  // thread -> 4 rows x N/16 columns: rows rg + 16 k, columns cg + 16 j
+  constexpr int NC = N / 16;
+  const int rg = tid >> 4, cg = tid & 15;
+  float a[4][NC];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) a[k][j] = 0.f;
+  for (int i = 0; i < K; ++i) {
+    float x[4], w[NC];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = xs[(rg + 16 * k) * (K + 1) + i];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) w[j] = ws[i * N + cg + 16 * j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) a[k][j] = fmaf(x[k], w[j], a[k][j]);
+  }
+  auto put = [&](int64_t o, float v) {
+    if (TOUT == 1) reinterpret_cast<float*>(p.out)[o] = v;
+    else if (TOUT == 2) reinterpret_cast<_Float16*>(p.out)[o] = (_Float16)v;
+    else reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)v;
+  };
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + rg + 16 * k;
+    if (r >= p.rows) continue;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) put(r * p.os_r + h * p.os_h + cg + 16 * j, a[k][j]);
+  }
+  // tail copy
+  for (int e = tid; e < kProjRows * p.tail; e += kProjThreads) {
+    const int rr = e / p.tail, i = e - (e / p.tail) * p.tail;
+    const int r = r0 + rr;
+    if (r >= p.rows) continue;
+    const int64_t o = r * p.is_r + h * p.is_h + K + i;
+    const float x = TIN == 1 ? reinterpret_cast<const float*>(p.in)[o]
+                             : __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p.in)[o] << 16);
+    put(r * p.os_r + h * p.os_h + N + i, x);
+  }
+}
+
+}  // namespace
+
+// Absorbed query: q_lat[b, n, h, :] = [(W^K_h)^T q[b, n, h, :96] ; q[b, n, h, 96:128]]
+// (fp16), from bf16 q [B, Nq, H, 128] with element strides (qs_b, qs_n, qs_h)
+// and bf16 W^K [H, 96, 192].
+hipError_t launch_mla_absorb(const uint16_t* q, int B, int Nq, int H, const int64_t* qs,
+                             const uint16_t* w_uk, uint16_t* q_lat, hipStream_t stream) {
+  for (int b = 0; b < B; ++b) {
+    ProjParams p{};
+    p.in = q + b * qs[0];
+    p.is_r = qs[1]; p.is_h = qs[2];
+    p.w = w_uk;
+    p.out = q_lat + (int64_t)b * Nq * H * kMlaDK;
+    p.os_r = (int64_t)H * kMlaDK; p.os_h = kMlaDK;
+    p.rows = Nq; p.H = H; p.K = 96; p.N = kMlaDC; p.tail = kMlaDR;
+    const dim3 grid((Nq + kProjRows - 1) / kProjRows, H);
+    if (Nq > 0 && H > 0)
+      hipLaunchKernelGGL((head_proj_kernel<96, kMlaDC, true, 0, 2>), grid, dim3(kProjThreads), 0,
+                         stream, p);
+  }
+  return hipGetLastError();
+}
+
+// Output: o[b, n, h, :] = W^V_h o_lat[b, n, h, :] from float32 o_lat
+// [B, Nq, H, 192] and bf16 W^V [H, 128, 192]; o bf16 or float32 with element
+// strides (os_b, os_n, os_h).
+hipError_t launch_mla_up(const float* o_lat, int B, int Nq, int H, const uint16_t* w_uv,
+                         void* o, bool o_f32, const int64_t* os, hipStream_t stream) {
+  for (int b = 0; b < B; ++b) {
+    ProjParams p{};
+    p.in = o_lat + (int64_t)b * Nq * H * kMlaDC;
+    p.is_r = (int64_t)H * kMlaDC; p.is_h = kMlaDC;
+    p.w = w_uv;
+    p.out = o_f32 ? static_cast<void*>(static_cast<float*>(o) + b * os[0])
+                  : static_cast<void*>(static_cast<uint16_t*>(o) + b * os[0]);
+    p.os_r = os[1]; p.os_h = os[2];
+    p.rows = Nq; p.H = H; p.K = kMlaDC; p.N = 128; p.tail = 0;
+    const dim3 grid((Nq + kProjRows - 1) / kProjRows, H);
+    if (Nq == 0 || H == 0) continue;
+    if (o_f32)
+      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 1>), grid, dim3(kProjThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 0>), grid, dim3(kProjThreads), 0,
+                         stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  if (n8 > 0)
+    hipLaunchKernelGGL(cast_bf16_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                       stream, x, y, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_attn(const uint16_t* q_lat, const uint16_t* kv, int64_t kv_bs, int64_t kv_rs,
+                           int B, int Nq, int H, int Nkv, float scale, float* o_lat, float* lse,
+                           hipStream_t stream) {
+  MlaParams p{};
+  p.q = q_lat; p.kv = kv; p.kv_bs = kv_bs; p.kv_rs = kv_rs;
+  p.o = o_lat; p.lse = lse;
+  p.B = B; p.Nq = Nq; p.H = H; p.Nkv = Nkv;
+  p.rows_per_b = Nq * H;
+  p.wg_per_b = (p.rows_per_b + kMlaNW * 32 - 1) / (kMlaNW * 32);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const int grid = B * p.wg_per_b;
+  if (grid > 0)
+    hipLaunchKernelGGL(mla_attn_kernel, dim3(grid), dim3(kMlaNW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace chunkattn
