@@ -335,10 +335,10 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
  *
  * ca_mla_absorb_q
  *   q      bf16 [B, Nq, H, 128] (q^nope = first 96 values, q^R = last 32),
- *          element strides q_strides (host), values contiguous
+ *          element strides q_strides (host, multiples of 8), values contiguous
  *   w_uk   bf16 [H, 96, 192] (W^K_h: latent -> content key), contiguous
- *   q_lat  fp16 [B, Nq, H, 224] contiguous output (float32 accumulation,
- *          one rounding to fp16)
+ *   q_lat  fp16 [B, Nq, H, 224] contiguous output (exact bf16 products,
+ *          float32 accumulation, one rounding to fp16)
  * ca_mla_attn_fwd
  *   q_lat  fp16 [B, Nq, H, 224] contiguous (from ca_mla_absorb_q)
  *   kv_lat fp16 latent rows [c ; k^R] (224 values): row t of batch entry b at
@@ -350,7 +350,10 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
  *          (natural log; no keys -> o_lat = 0, LSE = -inf)
  * ca_mla_up_proj
  *   o_lat  as above; w_uv bf16 [H, 128, 192] (W^V_h), contiguous
- *   o      [B, Nq, H, 128] of o_dtype (CA_BF16 or CA_F32), strides o_strides
+ *   o      [B, Nq, H, 128] of o_dtype (CA_BF16 or CA_F32), element strides
+ *          o_strides (host, multiples of 4); float32 o_lat enters the product
+ *          as a sum of two bf16 parts (relative residual 2^-17)
+ * All pointers of the three calls are 16-byte aligned (else CA_EINVAL).
  * ca_cast_bf16_to_f16: y[i] = fp16 round-to-nearest-even of bf16 x[i], n a
  *   multiple of 8, both 16-byte aligned.
  */

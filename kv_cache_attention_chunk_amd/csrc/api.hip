@@ -628,7 +628,8 @@ int ca_mla_absorb_q(const void* q, int B, int Nq, int H, int d_nope, int d_rope,
   if (B < 0 || Nq < 0 || H < 0) return fail(CA_EINVAL, "negative size");
   if (int r = check_mla_dims(d_nope, d_rope, d_c, kMlaVal)) return r;
   if (!q || !w_uk || !q_lat) return fail(CA_EINVAL, "NULL pointer");
-  if (int r = check_strides("q", q_strides, 1)) return r;
+  if (!aligned16(q) || !aligned16(w_uk) || !aligned16(q_lat)) return fail(CA_EINVAL, "q, w_uk, q_lat must be 16-byte aligned");
+  if (int r = check_strides("q", q_strides, 8)) return r;
   if ((int64_t)B * Nq * H > 0x7FFFFFFF / 256) return fail(CA_ERANGE, "too many rows");
   if (int r = check_device()) return r;
   return launched(launch_mla_absorb(static_cast<const uint16_t*>(q), B, Nq, H, q_strides,
@@ -663,7 +664,8 @@ int ca_mla_up_proj(const float* o_lat, const void* w_uv, int B, int Nq, int H, i
   if (int r = check_mla_dims(kMlaNope, kMlaRope, d_c, d_v)) return r;
   if (o_dtype != CA_BF16 && o_dtype != CA_F32) return fail(CA_EUNSUPPORTED, "o_dtype %d", o_dtype);
   if (!o_lat || !w_uv || !o) return fail(CA_EINVAL, "NULL pointer");
-  if (int r = check_strides("o", o_strides, 1)) return r;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(o)) return fail(CA_EINVAL, "o_lat, w_uv, o must be 16-byte aligned");
+  if (int r = check_strides("o", o_strides, 4)) return r;
   if ((int64_t)B * Nq * H > 0x7FFFFFFF / 256) return fail(CA_ERANGE, "too many rows");
   if (int r = check_device()) return r;
   return launched(launch_mla_up(o_lat, B, Nq, H, static_cast<const uint16_t*>(w_uv), o, o_dtype == CA_F32,

@@ -264,20 +264,28 @@ __global__ __launch_bounds__(256) void cast_bf16_f16_kernel(const uint16_t* __re
 
 // ---------------------------------------------------------------------------
 // Per-head projection: out[r, h, j] = sum_i in[r, h, i] * W(h, i, j) for the
-// rows r of one (b, query) range and head h, float32 accumulation.
+// rows r of one batch entry and head h, on the bf16 MFMA with float32
+// accumulation.
 //   W_IN_MAJOR: W stored [H, K, N] (W(h, i, j) = w[h][i][j]) -- the absorbed
 //               query uses (W^K_h)^T, i.e. W^K stored [H, d_nope, d_c]
 //   else:       W stored [H, N, K] (W(h, i, j) = w[h][j][i]) -- the value
 //               up-projection W^V stored [H, d_v, d_c]
-// One workgroup = 64 rows x all N outputs of one head; the weights and the
-// rows are staged in LDS as float32 (bf16 weights are exact in float32).
-// TIN: 0 = bf16 input, 1 = float32 input.  TOUT: 0 = bf16, 1 = float32,
-// 2 = fp16.  Optional tail copy: the input values [K, K + tail) of each row
-// go to outputs [N, N + tail) converted to the output type (the query's
-// position part next to its absorbed content part).
+// The product is computed transposed, out^T = W^T in^T with
+// v_mfma_f32_32x32x16_bf16: A = W^T (rows j, staged in LDS as bf16 [N][K + 8]
+// once per workgroup), B = in^T straight from global memory (lane = row r,
+// 8 consecutive i per lane), so each lane ends up holding 4 consecutive
+// outputs j of its row per accumulator group.
+// TIN: 0 = bf16 input (exact MFMA operand); 1 = float32 input, split as
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) and both halves multiplied
+// (2^-17 relative residual, i.e. float32-grade products).
+// TOUT: 0 = bf16, 1 = float32, 2 = fp16 (one round-to-nearest-even).
+// Optional tail copy: input values [K, K + 32) of each row go to outputs
+// [N, N + 32) in the output type (the query's position part next to its
+// absorbed content part).
+// One workgroup = 4 waves x 32 rows of one head.
 // ---------------------------------------------------------------------------
-constexpr int kProjRows = 64;
-constexpr int kProjThreads = 256;
+constexpr int kProjWaves = 4;
+constexpr int kProjRows = kProjWaves * 32;
 
 struct ProjParams {
   const void* in;
@@ -285,74 +293,120 @@ struct ProjParams {
   const uint16_t* w;         // bf16 weights
   void* out;
   int64_t os_r, os_h;
-  int rows, H, K, N, tail;
+  int rows, H, tail;
 };
 
 template <int K, int N, bool W_IN_MAJOR, int TIN, int TOUT>
-__global__ __launch_bounds__(kProjThreads) void head_proj_kernel(const ProjParams p) {
-  __shared__ float ws[K * N];
-  __shared__ float xs[kProjRows * (K + 1)];
+__global__ __launch_bounds__(kProjWaves * 64) void head_proj_kernel(const ProjParams p) {
+  constexpr int WR = K + 8;                 // LDS row of W^T, bf16 elements (16 B pad)
+  constexpr int NKS = K / 16;               // MFMA k-steps
+  constexpr int NJB = N / 32;               // 32-row blocks of out^T
+  static_assert(K % 16 == 0 && N % 32 == 0, "projection tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t ws[N * WR];
   const int h = blockIdx.y;
-  const int r0 = blockIdx.x * kProjRows;
   const int tid = threadIdx.x;
-  for (int e = tid; e < K * N; e += kProjThreads) {
-    // ws[i * N + j] = W(h, i, j)
-    const int i = e / N, j = e - (e / N) * N;
-    const uint16_t bits = W_IN_MAJOR ? p.w[((int64_t)h * K + i) * N + j] : p.w[((int64_t)h * N + j) * K + i];
-    ws[e] = __uint_as_float((uint32_t)bits << 16);
-  }
-  for (int e = tid; e < kProjRows * K; e += kProjThreads) {
-    const int rr = e / K, i = e - (e / K) * K;
-    const int r = r0 + rr;
-    float x = 0.f;
-    if (r < p.rows) {
-      const int64_t o = r * p.is_r + h * p.is_h + i;
-      x = TIN == 1 ? reinterpret_cast<const float*>(p.in)[o]
-                   : __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p.in)[o] << 16);
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31, hg = lane >> 5;
+
+  // W^T into LDS: ws[j * WR + i] = W(h, i, j)
+  if (W_IN_MAJOR) {
+    // 16-byte loads of 8 consecutive j for one i, scattered to 8 LDS rows
+    for (int c = tid; c < K * N / 8; c += kProjWaves * 64) {
+      const int i = c / (N / 8), j0 = 8 * (c - i * (N / 8));
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p.w + ((int64_t)h * K + i) * N + j0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ws[(j0 + 2 * e) * WR + i] = (uint16_t)(x[e] & 0xFFFFu);
+        ws[(j0 + 2 * e + 1) * WR + i] = (uint16_t)(x[e] >> 16);
+      }
     }
-    xs[rr * (K + 1) + i] = x;
+  } else {
+    for (int c = tid; c < K * N / 8; c += kProjWaves * 64) {
+      const int j = c / (K / 8), i0 = 8 * (c - j * (K / 8));
+      *reinterpret_cast<u32x4_t*>(ws + j * WR + i0) =
+          *reinterpret_cast<const u32x4_t*>(p.w + ((int64_t)h * N + j) * K + i0);
+    }
+  }
+
+  // in^T operands of row r (lane column), values 16 ks + 8 hg .. + 8
+  const int r = blockIdx.x * kProjRows + wave * 32 + col;
+  const bool rvalid = r < p.rows;
+  const int64_t ibase = (int64_t)r * p.is_r + (int64_t)h * p.is_h;
+  bf16x8_t xb[NKS], xl[TIN == 1 ? NKS : 1];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int i0 = 16 * ks + 8 * hg;
+    if (TIN == 0) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (rvalid) x = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(p.in) + ibase + i0);
+      xb[ks] = __builtin_bit_cast(bf16x8_t, x);
+    } else {
+      f32x8_t x = {};
+      if (rvalid) {
+        const float* ip = reinterpret_cast<const float*>(p.in) + ibase + i0;
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(ip);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(ip + 4);
+        x = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const bf16x8_t hi = __builtin_convertvector(x, bf16x8_t);
+      xb[ks] = hi;
+      xl[(TIN == 1) ? ks : 0] = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8_t), bf16x8_t);
+    }
   }
   __syncthreads();
-  // thread -> 4 rows x N/16 columns: rows rg + 16 k, columns cg + 16 j
-  constexpr int NC = N / 16;
-  const int rg = tid >> 4, cg = tid & 15;
-  float a[4][NC];
+
+  f32x16_t acc[NJB];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int jb = 0; jb < NJB; ++jb) acc[jb] = f32x16_t{};
 #pragma unroll
-    for (int j = 0; j < NC; ++j) a[k][j] = 0.f;
-  for (int i = 0; i < K; ++i) {
-    float x[4], w[NC];
+  for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = xs[(rg + 16 * k) * (K + 1) + i];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) w[j] = ws[i * N + cg + 16 * j];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < NC; ++j) a[k][j] = fmaf(x[k], w[j], a[k][j]);
+    for (int jb = 0; jb < NJB; ++jb) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ws + (32 * jb + col) * WR + 16 * ks + 8 * hg);
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[ks], acc[jb], 0, 0, 0);
+      if (TIN == 1)
+        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xl[(TIN == 1) ? ks : 0], acc[jb], 0, 0, 0);
+    }
   }
-  auto put = [&](int64_t o, float v) {
-    if (TOUT == 1) reinterpret_cast<float*>(p.out)[o] = v;
-    else if (TOUT == 2) reinterpret_cast<_Float16*>(p.out)[o] = (_Float16)v;
-    else reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)v;
-  };
+  if (!rvalid) return;
+
+  // out^T block jb, register 4 g + e = output j = 32 jb + 8 g + 4 hg + e of row r
+  const int64_t obase = (int64_t)r * p.os_r + (int64_t)h * p.os_h;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = r0 + rg + 16 * k;
-    if (r >= p.rows) continue;
+  for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-    for (int j = 0; j < NC; ++j) put(r * p.os_r + h * p.os_h + cg + 16 * j, a[k][j]);
-  }
-  // tail copy
-  for (int e = tid; e < kProjRows * p.tail; e += kProjThreads) {
-    const int rr = e / p.tail, i = e - (e / p.tail) * p.tail;
-    const int r = r0 + rr;
-    if (r >= p.rows) continue;
-    const int64_t o = r * p.is_r + h * p.is_h + K + i;
-    const float x = TIN == 1 ? reinterpret_cast<const float*>(p.in)[o]
-                             : __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p.in)[o] << 16);
-    put(r * p.os_r + h * p.os_h + N + i, x);
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = 32 * jb + 8 * g + 4 * hg;
+      const f32x4_t v = {acc[jb][4 * g], acc[jb][4 * g + 1], acc[jb][4 * g + 2], acc[jb][4 * g + 3]};
+      if (TOUT == 1)
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.out) + obase + j0) = v;
+      else if (TOUT == 2)
+        *reinterpret_cast<f16x4_t*>(reinterpret_cast<_Float16*>(p.out) + obase + j0) =
+            __builtin_convertvector(v, f16x4_t);
+      else
+        *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(p.out) + obase + j0) =
+            __builtin_convertvector(v, bf16x4_t);
+    }
+  // tail copy: lane half hg moves values K + 16 hg .. + 16 (bf16 input only)
+  if (TIN == 0 && p.tail == 32) {
+    const uint16_t* tp = reinterpret_cast<const uint16_t*>(p.in) + ibase + K + 16 * hg;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(tp + 8 * c);
+      const f32x8_t f = __builtin_convertvector(__builtin_bit_cast(bf16x8_t, x), f32x8_t);
+      const int64_t o = obase + N + 16 * hg + 8 * c;
+      if (TOUT == 2) {
+        typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_o;
+        *reinterpret_cast<f16x8_o*>(reinterpret_cast<_Float16*>(p.out) + o) = __builtin_convertvector(f, f16x8_o);
+      } else if (TOUT == 1) {
+        *reinterpret_cast<f32x8_t*>(reinterpret_cast<float*>(p.out) + o) = f;
+      } else {
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p.out) + o) = x;
+      }
+    }
   }
 }
 
@@ -370,10 +424,10 @@ hipError_t launch_mla_absorb(const uint16_t* q, int B, int Nq, int H, const int6
     p.w = w_uk;
     p.out = q_lat + (int64_t)b * Nq * H * kMlaDK;
     p.os_r = (int64_t)H * kMlaDK; p.os_h = kMlaDK;
-    p.rows = Nq; p.H = H; p.K = 96; p.N = kMlaDC; p.tail = kMlaDR;
+    p.rows = Nq; p.H = H; p.tail = kMlaDR;
     const dim3 grid((Nq + kProjRows - 1) / kProjRows, H);
     if (Nq > 0 && H > 0)
-      hipLaunchKernelGGL((head_proj_kernel<96, kMlaDC, true, 0, 2>), grid, dim3(kProjThreads), 0,
+      hipLaunchKernelGGL((head_proj_kernel<96, kMlaDC, true, 0, 2>), grid, dim3(kProjWaves * 64), 0,
                          stream, p);
   }
   return hipGetLastError();
@@ -392,14 +446,14 @@ hipError_t launch_mla_up(const float* o_lat, int B, int Nq, int H, const uint16_
     p.out = o_f32 ? static_cast<void*>(static_cast<float*>(o) + b * os[0])
                   : static_cast<void*>(static_cast<uint16_t*>(o) + b * os[0]);
     p.os_r = os[1]; p.os_h = os[2];
-    p.rows = Nq; p.H = H; p.K = kMlaDC; p.N = 128; p.tail = 0;
+    p.rows = Nq; p.H = H; p.tail = 0;
     const dim3 grid((Nq + kProjRows - 1) / kProjRows, H);
     if (Nq == 0 || H == 0) continue;
     if (o_f32)
-      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 1>), grid, dim3(kProjThreads), 0,
+      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 1>), grid, dim3(kProjWaves * 64), 0,
                          stream, p);
     else
-      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 0>), grid, dim3(kProjThreads), 0,
+      hipLaunchKernelGGL((head_proj_kernel<kMlaDC, 128, false, 1, 0>), grid, dim3(kProjWaves * 64), 0,
                          stream, p);
   }
   return hipGetLastError();
