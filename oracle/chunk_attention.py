@@ -23,7 +23,10 @@ against the pages by eye:
   page, section 2 item 2 and item 1 "memory management", including the
   persistent-set update when blocks leave the local window;
 * per-head frame selections and adjacent-frame merges packed into flat
-  buffers with boundary indices -- Pyramid Forcing page, sections 2-3.
+  buffers with boundary indices -- Pyramid Forcing page, sections 2-3;
+* attention over a latent KV cache: every head's keys and values rebuilt
+  from the shared content latent and rotated position key by the head's
+  up-projections, then plain attention -- VideoMLA page, method.
 
 Floating point: inputs are bf16 values given as exactly equal float32 arrays;
 attention, merge and block means are computed in float64.  Where a floating
