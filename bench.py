@@ -62,6 +62,21 @@ def traffic_from_counters():
     return c.get("hbm_bytes_per_call")
 
 
+def effective_schedule(ca, q, k, v, scale, policy):
+    """Which schedule a dense call under `policy` runs: its output is compared
+    bit for bit with the plain grid's and the balanced schedule's (the two
+    round split query tiles differently)."""
+    import torch
+    outs = {}
+    for name, pol in (("run", policy), ("plain", "never"), ("balanced", "always")):
+        outs[name] = ca.chunk_attn_fwd(q, k, v, scale=scale, balanced=pol)
+    torch.cuda.synchronize()
+    for name in ("plain", "balanced"):
+        if all(torch.equal(a, b) for a, b in zip(outs["run"], outs[name])):
+            return name
+    return "unknown"
+
+
 def cpu_baseline(w):
     """Time the CPU oracle, as it stands, on a bounded sample of the same
     workload: the full dense layer (all 12 heads, all 4680 query rows vs
@@ -312,10 +327,10 @@ def main():
                     help="'dense' times the dense kernel alone (for counter runs); 'copy' "
                          "runs a plain 1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", choices=["plain", "balanced"], default="plain",
-                    help="dense launch: one workgroup per (head, query tile) (default; what the "
-                         "library picks for a uniform cache) or the key-range split over the "
-                         "resident workgroups")
+    ap.add_argument("--schedule", choices=["auto", "plain", "balanced"], default="auto",
+                    help="dense launch: the library's own choice (default), one workgroup per "
+                         "(head, query tile), or the key-range split over the resident "
+                         "workgroups")
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="with --only dense: keep launching for this many seconds before the "
                          "timed steps (for power and clock sampling)")
@@ -378,9 +393,10 @@ def main():
     l_merge = torch.empty_like(l_dense)
     lay = wl.sparse_layout(w, args.topk_ratio)
 
+    policy = {"auto": "auto", "plain": "never", "balanced": "always"}[args.schedule]
+
     def dense():
-        ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_dense, lse=l_dense,
-                          balanced="always" if args.schedule == "balanced" else "never")
+        ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_dense, lse=l_dense, balanced=policy)
 
     def merged():
         for ip, ix, ob, lb, _ in branch:
@@ -464,6 +480,7 @@ def main():
         res["sparse_path_ms"] = sum(e[2].elapsed_time(e[3]) for e in ev) / n
     log(f"timed {n} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / n:.3f}), {res}")
 
+    schedule = effective_schedule(ca, q, k, v, w.scale, policy)
     achieved = f_dense / (t_dense * 1e-3) / 1e12
     kv_bytes = 2.0 * Nkv * H * d * 2 * B
     traffic = traffic_from_counters()
@@ -485,10 +502,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": ("attn_fwd_kernel<128,4,range,bf16> + split_merge_kernel<128,bf16>"
-                                if args.schedule == "balanced" else
-                                "attn_fwd_kernel<128,4,range,bf16>"),
-                     "schedule": args.schedule,
+                     "kernel": ("attn_fwd_kernel<128,8,range,bf16> + split_merge_kernel<128,bf16>"
+                                if schedule == "balanced" else
+                                "attn_fwd_kernel<128,8,range,bf16>"),
+                     "schedule": schedule if args.schedule == "auto" else args.schedule,
                      "avg_launch_ms": round(t_dense, 4)},
         "kv_gbs": {"dense": round(kv_bytes / (t_dense * 1e-3) / 1e9, 1),
                    "frac_hbm": round(kv_bytes / (t_dense * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

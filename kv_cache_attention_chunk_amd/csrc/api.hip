@@ -103,7 +103,7 @@ void fill_common(AttnParams& p, const Common& c) {
   p.scale_log2 = c.scale * 1.4426950408889634f;
 }
 
-constexpr int kDenseWaves = 4;            // 128 query rows per workgroup (range mode)
+constexpr int kDenseWaves = 8;            // 256 query rows per workgroup (range mode)
 constexpr int kMinUnitsPerWg = 8;         // balanced schedule: key tiles per workgroup, at least
 
 // Block mode: one workgroup per query block (or row slice of one), over a
@@ -114,7 +114,7 @@ int launch_blocks(const Common& c, AttnParams& p, const std::vector<int>& heads,
   const bool all = heads.empty();
   const int nh = all ? c.B * c.H : (int)heads.size();
   const int maxq = std::min(std::min(p.q_block, p.q_seg), std::max(c.Nq, 1));
-  const int nwaves = maxq <= 64 ? 2 : 4;
+  const int nwaves = maxq <= 64 ? 2 : (maxq <= 128 ? 4 : 8);
   p.q_sub = (maxq + nwaves * 32 - 1) / (nwaves * 32);
   for (int h0 = 0; h0 < nh; h0 += kMaxHeadsPerLaunch) {
     const int n = std::min(kMaxHeadsPerLaunch, nh - h0);
@@ -140,13 +140,13 @@ size_t workspace_bytes(int slots, int d) {
 // read the flat buffers).  tiles[i] (host) is head i's key-tile count when
 // known (empty vector: unknown).  With a workspace and known tile counts a
 // launch takes the balanced schedule when that shortens it by more than a
-// fifth: the plain grid runs one workgroup per (head, query tile), so its
+// twentieth: the plain grid runs one workgroup per (head, query tile), so its
 // length is set by the longest head and by how many rounds of workgroups the
 // device needs; the balanced grid gives every resident workgroup the same
-// number of key tiles.  The margin is there because the balanced grid reads
-// each head's keys in two phase-shifted streams, which roughly doubles the
-// L2 fill traffic, and because on a uniform cache its gain from filling idle
-// CUs is mostly returned as a lower clock under the power limit.
+// number of key tiles.  The margin covers the merge pass and the balanced
+// grid's second, phase-shifted stream over each head's keys (roughly double
+// the L2 fill traffic); on a uniform cache part of the gain from filling idle
+// CUs is returned as a lower clock under the power limit.
 int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& words,
                  const std::vector<int>& tiles, int split, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
@@ -169,9 +169,9 @@ int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& wo
       const int64_t g = std::min<int64_t>(slots, units / kMinUnitsPerWg);
       const int64_t est_plain = (items + slots - 1) / slots * (int64_t)max_nt;
       const int64_t est_bal = g > 0 ? (units + g - 1) / g + 2 : INT64_MAX;
-      // (the merge grid has 16 workgroups per query tile; keep it in range)
-      const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 5 < est_plain * 4;
-      if (units <= 0x7FFFFFFF && items * 16 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
+      // (the merge grid has 32 workgroups per query tile; keep it in range)
+      const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 20 < est_plain * 19;
+      if (units <= 0x7FFFFFFF && items * 32 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
         if (ws_bytes < workspace_bytes((int)g, c.d))
           return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
                       ws_bytes, workspace_bytes((int)g, c.d));

@@ -42,8 +42,9 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
-// LDS ring of K and V tile stages: K x2 and V x2 (64 KB at d = 128, so two
-// 4-wave workgroups share a CU).  With two stages each, the stage of every
+// LDS ring of K and V tile stages: K x2 and V x2 (64 KB at d = 128).  An
+// 8-wave workgroup (256 query rows) holds a CU's 8 waves, so each K/V tile
+// goes from L2 to LDS once per CU for 256 rows.  With two stages each, the stage of every
 // read is a compile-time constant in the two-iteration unrolled loop.
 template <int D, int NW>
 struct Layout {
@@ -161,8 +162,8 @@ struct TileLoader {
   }
 };
 
-// Two waves per SIMD: caps VGPR + AGPR at 256 per lane so that two 4-wave
-// workgroups share a CU.
+// Two waves per SIMD: caps VGPR + AGPR at 256 per lane, so a CU holds 8 waves
+// (one 8-wave workgroup, or two of 4 waves, or four of 2).
 template <int D, int NW, int MODE, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const AttnParams p) {
@@ -773,9 +774,10 @@ hipError_t launch_t(bool of32, const AttnParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(int mode, int nwaves, bool of32, const AttnParams& p, hipStream_t stream) {
-  if (mode == MODE_RANGE) return launch_t<D, 4, MODE_RANGE>(of32, p, stream);
+  if (mode == MODE_RANGE) return launch_t<D, 8, MODE_RANGE>(of32, p, stream);
   return nwaves == 2 ? launch_t<D, 2, MODE_BLOCKS>(of32, p, stream)
-                     : launch_t<D, 4, MODE_BLOCKS>(of32, p, stream);
+       : nwaves == 4 ? launch_t<D, 4, MODE_BLOCKS>(of32, p, stream)
+                     : launch_t<D, 8, MODE_BLOCKS>(of32, p, stream);
 }
 
 template <int D>
@@ -784,8 +786,8 @@ int slots_d() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&attn_fwd_kernel<D, 4, MODE_RANGE, false>),
-          4 * 64, 0) != hipSuccess)
+          &per, reinterpret_cast<const void*>(&attn_fwd_kernel<D, 8, MODE_RANGE, false>),
+          8 * 64, 0) != hipSuccess)
     return 0;
   return cus * per;
 }

@@ -25,7 +25,7 @@ enum Mode { MODE_RANGE = 0, MODE_BLOCKS = 1 };
 constexpr int kMaxHeadsPerLaunch = 1024;
 constexpr int kMaxSchedHeads = 256;   // heads of one launch under the balanced schedule
 constexpr int kTileKeys = 64;         // keys per KV tile (and max KV block size)
-constexpr int kRangeRows = 128;       // query rows per workgroup in range mode
+constexpr int kRangeRows = 256;       // query rows per workgroup in range mode (8 waves)
 constexpr uint16_t kFlatHead = 0x8000;  // heads[] flag: the head reads the flat buffers
 
 // Kernel arguments of the fused attention kernel (passed by value).

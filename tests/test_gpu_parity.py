@@ -389,10 +389,13 @@ def wan_dev(wan):
     return to_dev(wan.q), to_dev(wan.k), to_dev(wan.v)
 
 
-def test_wan_dense_full_size(wan, wan_dev):
-    say("wan dense 12x4680x32760 d128")
+@pytest.mark.parametrize("policy", ["auto", "never"])
+def test_wan_dense_full_size(wan, wan_dev, policy):
+    # auto: the schedule bench.py times; never: the plain grid, one workgroup
+    # per (head, 256-query tile)
+    say(f"wan dense 12x4680x32760 d128, split policy {policy}")
     q, k, v = wan_dev
-    o, l = ca.chunk_attn_fwd(q, k, v, scale=wan.scale)
+    o, l = ca.chunk_attn_fwd(q, k, v, scale=wan.scale, balanced=policy)
     torch.cuda.synchronize()
     Or, Lr = orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale, rows=WAN_ROWS)
     assert_o(o[:, WAN_ROWS], Or, True, "wan dense")
