@@ -52,7 +52,7 @@ enum ca_dtype { CA_BF16 = 0, CA_F32 = 1 };
 
 /* key-range split policy of the dense / ragged launches (see
  * ca_attn_workspace_bytes): taken when it shortens a launch by more than a
- * twentieth (AUTO), never, or whenever it applies (ALWAYS: a workspace is given,
+ * fifth (AUTO), never, or whenever it applies (ALWAYS: a workspace is given,
  * head lengths are known and there is enough work) */
 enum ca_split_policy { CA_SPLIT_AUTO = 0, CA_SPLIT_NEVER = 1, CA_SPLIT_ALWAYS = 2 };
 
@@ -87,8 +87,8 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  * the workgroups leave in the workspace: attention over consecutive key
  * ranges recombined through the LSE state (ISPA page, section 2 item 1).
  * The result is the same attention up to float32 rounding.  The schedule is
- * taken only when it shortens the launch by more than a twentieth by tile
- * count (heads of unequal length, or a grid that leaves CUs idle); it needs every head's key count on the
+ * taken only when it shortens the launch by more than a fifth by tile count
+ * (chiefly heads of unequal length); it needs every head's key count on the
  * host (always for the dense cache; for ragged heads only with
  * cu_seqlens_host).  Calls sharing one workspace
  * must be ordered on one stream.  NULL = no workspace: one workgroup per

@@ -141,7 +141,7 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     The output dtype is out_dtype, else out's dtype, else bf16.  `balanced`
     is the key-range split policy of a dense launch: True/'auto' (split key
     ranges evenly over the device's resident workgroups when that shortens
-    the launch by more than a twentieth), False/'never', or 'always' (whenever it
+    the launch by more than a fifth), False/'never', or 'always' (whenever it
     applies); a workspace is allocated for it unless one is given."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q), _bshd("k", k), _bshd("v", v)

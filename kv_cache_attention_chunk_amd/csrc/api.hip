@@ -140,13 +140,14 @@ size_t workspace_bytes(int slots, int d) {
 // read the flat buffers).  tiles[i] (host) is head i's key-tile count when
 // known (empty vector: unknown).  With a workspace and known tile counts a
 // launch takes the balanced schedule when that shortens it by more than a
-// twentieth: the plain grid runs one workgroup per (head, query tile), so its
+// fifth: the plain grid runs one workgroup per (head, query tile), so its
 // length is set by the longest head and by how many rounds of workgroups the
 // device needs; the balanced grid gives every resident workgroup the same
 // number of key tiles.  The margin covers the merge pass and the balanced
 // grid's second, phase-shifted stream over each head's keys (roughly double
-// the L2 fill traffic); on a uniform cache part of the gain from filling idle
-// CUs is returned as a lower clock under the power limit.
+// the L2 fill traffic), and on a uniform cache the gain from filling idle CUs
+// is returned as a lower clock under the power limit (measured: the dense
+// Wan layer runs no faster balanced).
 int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& words,
                  const std::vector<int>& tiles, int split, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
@@ -170,7 +171,7 @@ int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& wo
       const int64_t est_plain = (items + slots - 1) / slots * (int64_t)max_nt;
       const int64_t est_bal = g > 0 ? (units + g - 1) / g + 2 : INT64_MAX;
       // (the merge grid has 32 workgroups per query tile; keep it in range)
-      const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 20 < est_plain * 19;
+      const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 5 < est_plain * 4;
       if (units <= 0x7FFFFFFF && items * 32 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
         if (ws_bytes < workspace_bytes((int)g, c.d))
           return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
