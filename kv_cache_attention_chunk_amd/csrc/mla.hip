@@ -9,7 +9,7 @@
 // Three kernels: the per-head projections (query absorption, value
 // up-projection) and the latent attention.
 //
-// Latent attention (mla_attn_kernel).  One workgroup = 4 waves x 32 rows of
+// Latent attention (mla_attn_kernel).  One workgroup = 8 waves x 32 rows of
 // one batch entry; rows are (query, head) pairs, so every row of the grid
 // streams the same 64-token latent tiles.  A tile [64 x 224] serves as K (all
 // 224 values) and as V (the first 192).  The operands are fp16: the absorbed
@@ -34,7 +34,7 @@ constexpr int kMlaDR = 32;                // position key
 constexpr int kMlaDK = kMlaDC + kMlaDR;   // 224 cached values per token
 constexpr int kMlaRowB = 512;             // LDS bytes per latent row (448 used)
 constexpr int kMlaTileB = kTileKeys * kMlaRowB;
-constexpr int kMlaNW = 4;
+constexpr int kMlaNW = 8;                 // 256 rows per workgroup, one per CU
 constexpr float kLn2f = 0.6931471805599453f;
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
@@ -79,7 +79,7 @@ void mla_attn_kernel(const MlaParams p) {
   constexpr int NST = kMlaDK / 16;        // 14 k-steps of S
   constexpr int NDT = kMlaDC / 32;        // 6 d-tiles of O^T
   constexpr int CPR = kMlaDK / 8;         // 28 16-byte chunks per latent row
-  constexpr int NLD = kMlaTileB / (1024 * kMlaNW);   // 8 buffer->LDS loads per wave per tile
+  constexpr int NLD = kMlaTileB / (1024 * kMlaNW);   // buffer->LDS loads per wave per tile
   __shared__ __attribute__((aligned(1024))) char lat[2 * kMlaTileB];
 
   const int tid = threadIdx.x;
@@ -109,8 +109,7 @@ void mla_attn_kernel(const MlaParams p) {
   // logical chunk ps ^ swz(pr) of latent row pr, or nothing (zeros) for the
   // padding slots (logical chunk >= 28) and rows past the cache.
   // Slot of lane i in instruction j: physical row pr = 2 (NLD w + j) + i / 32,
-  // slot ps = i % 32, loading logical chunk ps ^ swz(pr); pr & 15 = (2 j +
-  // i / 32) & 15, so the swizzle depends on j and the lane half only.  Each
+  // slot ps = i % 32, loading logical chunk ps ^ swz(pr).  Each
   // instruction's buffer starts at its row pair (a uniform base), whose valid
   // bytes bound the range check: rows past the cache and padding slots
   // (logical chunk >= 28, given an out-of-range offset) read as zeros.
@@ -131,7 +130,7 @@ void mla_attn_kernel(const MlaParams p) {
       // (the empty asm keeps this offset at the load instead of a live register)
       int cl = col, h1 = hg;
       asm volatile("" : "+v"(cl), "+v"(h1));
-      const int c = cl ^ mla_swz(2 * j + h1);
+      const int c = cl ^ mla_swz(pr0 + h1);
       const uint32_t voff = c < CPR ? (uint32_t)h1 * rs_bytes + 16u * c : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, mla_dma_dst(base + (NLD * wave + j) * 1024), 16,
                                                (int)voff, 0, 0, 0);
