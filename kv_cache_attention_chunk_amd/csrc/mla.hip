@@ -11,19 +11,23 @@
 //
 // Latent attention (mla_attn_kernel).  One workgroup = 8 waves x 32 rows of
 // one batch entry; rows are (query, head) pairs, so every row of the grid
-// streams the same 64-token latent tiles.  A tile [64 x 224] serves as K (all
-// 224 values) and as V (the first 192).  The operands are fp16: the absorbed
+// streams the same latent rows, 32 at a time.  Such a half-tile [32 x 224]
+// serves as K (all 224 values) and as V (the first 192).  The operands are fp16: the absorbed
 // query is rounded once to fp16 (11-bit significand; bf16 would put its
 // rounding error on every score), the latent cache is kept in fp16 (a bf16
 // cache converts exactly in its normal range, see ca_cast_bf16_to_f16), and P
-// is rounded to fp16 for the PV product; all accumulation is float32.  Tiles
-// go from global memory to LDS with buffer loads (no staging registers) into
-// rows padded to 512 bytes, two stages.  Chunk c of row r sits at
+// is rounded to fp16 for the PV product; all accumulation is float32.
+// Half-tiles go from global memory to LDS with buffer loads (no staging
+// registers) into rows padded to 512 bytes, a ring of four stages loaded three
+// steps ahead; each step interleaves the softmax and P V of one half-tile with
+// the scores of the next.  Chunk c of row r sits at
 // c ^ (4 (r & 3) + ((r >> 2) & 3)): sixteen consecutive rows take sixteen
 // distinct chunk slots (the S = K Q^T operand reads) and four consecutive
 // rows take four disjoint groups of four slots (the transposing V^T reads),
 // so both read patterns are free of bank conflicts.
 #include "common.h"
+
+#include <type_traits>
 
 namespace chunkattn {
 
@@ -33,7 +37,6 @@ constexpr int kMlaDC = 192;               // content latent
 constexpr int kMlaDR = 32;                // position key
 constexpr int kMlaDK = kMlaDC + kMlaDR;   // 224 cached values per token
 constexpr int kMlaRowB = 512;             // LDS bytes per latent row (448 used)
-constexpr int kMlaTileB = kTileKeys * kMlaRowB;
 constexpr int kMlaNW = 8;                 // 256 rows per workgroup, one per CU
 constexpr float kLn2f = 0.6931471805599453f;
 
@@ -73,14 +76,25 @@ struct MlaParams {
   float scale_log2;
 };
 
+// Half-tiles of 32 latent rows flow through a ring of four LDS stages
+// (16 KB each): half-tile u sits in stage u % 4 and is loaded three
+// iterations ahead.  Iteration u turns the scores of half-tile u (computed in
+// iteration u - 1) into P, accumulates O^T += V^T P^T for it and computes the
+// scores of half-tile u + 1, the three interleaved segment by segment.
+constexpr int kMlaHalf = 32;                         // latent rows per step
+constexpr int kMlaStages = 4;
+constexpr int kMlaStageB = kMlaHalf * kMlaRowB;      // 16 KB
+
 __global__ __launch_bounds__(kMlaNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mla_attn_kernel(const MlaParams p) {
   constexpr int BM = kMlaNW * 32;
   constexpr int NST = kMlaDK / 16;        // 14 k-steps of S
   constexpr int NDT = kMlaDC / 32;        // 6 d-tiles of O^T
   constexpr int CPR = kMlaDK / 8;         // 28 16-byte chunks per latent row
-  constexpr int NLD = kMlaTileB / (1024 * kMlaNW);   // buffer->LDS loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) char lat[2 * kMlaTileB];
+  constexpr int NLD = kMlaStageB / (1024 * kMlaNW);  // buffer->LDS loads per wave per half-tile
+  static_assert(NLD >= 1 && NLD * 1024 * kMlaNW == kMlaStageB, "the loads must fill a stage");
+  static_assert(NST == 14 && NDT == 6, "the segment plan below is laid out for 224 / 192");
+  __shared__ __attribute__((aligned(1024))) char lat[kMlaStages * kMlaStageB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,28 +118,25 @@ void mla_attn_kernel(const MlaParams p) {
     qreg[st] = __builtin_bit_cast(f16x8_t, x);
   }
 
-  // Tile loads: wave w's instruction j fills LDS bytes [(NLD w + j) KB, +1 KB),
-  // lane i the 16-byte slot at +16 i = physical row pr, slot ps; it loads
-  // logical chunk ps ^ swz(pr) of latent row pr, or nothing (zeros) for the
-  // padding slots (logical chunk >= 28) and rows past the cache.
-  // Slot of lane i in instruction j: physical row pr = 2 (NLD w + j) + i / 32,
-  // slot ps = i % 32, loading logical chunk ps ^ swz(pr).  Each
-  // instruction's buffer starts at its row pair (a uniform base), whose valid
-  // bytes bound the range check: rows past the cache and padding slots
-  // (logical chunk >= 28, given an out-of-range offset) read as zeros.
+  // Loads of half-tile u into stage u % 4: lane i of wave w's instruction j
+  // fills physical row pr = 2 (NLD w + j) + i / 32 of the stage, slot i % 32,
+  // with logical chunk (i % 32) ^ swz(pr).  Each instruction's buffer starts
+  // at its row pair (a uniform base), whose valid bytes bound the range
+  // check: rows past the cache and padding slots (logical chunk >= 28, given
+  // an out-of-range offset) read as zeros.
   const uint32_t rs_bytes = (uint32_t)(p.kv_rs * 2);
   const uint16_t* kvb = p.kv + b * p.kv_bs;
-  const int ntiles = (p.Nkv + kTileKeys - 1) / kTileKeys;
-  auto issue_tile = [&](int t, int stage) {
-    const int valid = p.Nkv - t * kTileKeys < kTileKeys ? p.Nkv - t * kTileKeys : kTileKeys;
-    char* base = lat + stage * kMlaTileB;
+  const int nh = (p.Nkv + kMlaHalf - 1) / kMlaHalf;
+  auto issue = [&](int u) {
+    const int valid = p.Nkv - u * kMlaHalf < kMlaHalf ? p.Nkv - u * kMlaHalf : kMlaHalf;
+    char* base = lat + (u % kMlaStages) * kMlaStageB;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int pr0 = 2 * (NLD * wave + j);
       const int here = valid - pr0;                     // valid rows from pr0 on
       const int nrec = here >= 2 ? (int)rs_bytes + 2 * kMlaDK : (here == 1 ? 2 * kMlaDK : 0);
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(kvb + ((int64_t)t * kTileKeys + pr0) * p.kv_rs), (short)0, nrec,
+          const_cast<uint16_t*>(kvb + ((int64_t)u * kMlaHalf + pr0) * p.kv_rs), (short)0, nrec,
           kBufWord3);
       // (the empty asm keeps this offset at the load instead of a live register)
       int cl = col, h1 = hg;
@@ -142,46 +153,64 @@ void mla_attn_kernel(const MlaParams p) {
     asm volatile("" ::: "memory");
   };
 
+  // MFMA operands.  S^T = K Q^T: A = latent rows (keys) of a stage, row col,
+  // chunk (2 s + hg) ^ swz(col) for k-step s.  O^T += V^T P^T: A = V^T read
+  // with transposing loads; group g covers keys 16 g .. 16 g + 15 of the
+  // half-tile (P values cur[8 g + e], key 16 g + 8 (e / 4) + 4 hg + e % 4):
+  // rows vr = 16 g + 4 hg + (lane & 15) / 4 and vr + 8, chunk 4 dt + vcol16
+  // swizzled by swz(vr) = 4 ((lane & 15) / 4) + hg and swz(vr + 8) = that + 2.
+  // Both swizzles only touch the low four chunk bits, so k-steps s and s + 8
+  // (d-tiles dt and dt + 4) differ by 256 bytes and groups by 16 rows: eight
+  // per-lane offsets for K and eight for V cover every read, the rest is an
+  // immediate.
+  const int zk = mla_swz(col);
+  const int vcol16 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int r4 = (lane & 15) >> 2;
+  int ka[8], va[4], vb[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ka[s] = col * kMlaRowB + 16 * ((2 * s + hg) ^ zk);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    va[q] = (4 * hg + r4) * kMlaRowB + 16 * ((4 * q + vcol16) ^ (4 * r4 + hg)) + 8 * (lane & 1);
+    vb[q] = (4 * hg + r4 + 8) * kMlaRowB + 16 * ((4 * q + vcol16) ^ (4 * r4 + hg + 2)) + 8 * (lane & 1);
+  }
+  auto kfrag = [&](int stg, int s) {
+    return *reinterpret_cast<const f16x8_t*>(lat + stg * kMlaStageB + ka[s & 7] + 256 * (s >> 3));
+  };
+  auto vfrag = [&](int stg, int g, int dt) {
+    const char* sb = lat + stg * kMlaStageB + 16 * g * kMlaRowB + 256 * (dt >> 2);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(sb + va[dt & 3])));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(sb + vb[dt & 3])));
+    return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   f32x16_t acc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = f32x16_t{};
   float m = -INFINITY, l = 0.f;
+  float rawmax = -INFINITY;     // raw row max of the half-tile in `cur`
 
-  if (ntiles > 0) {
-    issue_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x3F70);     // vmcnt(0)
-    block_sync();
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int stg = t & 1;
-    const char* tb = lat + stg * kMlaTileB;
-    // stage stg^1 was last read in iteration t-1, which ended with a barrier
-    if (t + 1 < ntiles) issue_tile(t + 1, stg ^ 1);
-    // S^T = K Q^T for the two 32-key halves
-    f32x16_t sc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt] = f32x16_t{};
-      const int r = 32 * kt + col;
-      const char* rp = tb + r * kMlaRowB;
-      const int z = mla_swz(r);
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(rp + 16 * ((2 * st + hg) ^ z));
-        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[st], sc[kt], 0, 0, 0);
-      }
-    }
-    // online softmax (log2 domain); keys past Nkv are masked
-    const int len = p.Nkv - t * kTileKeys;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+  // Segment plan of one iteration (14 segments):
+  //   QK: k-step s of the next half-tile's scores in segment s;
+  //   exp2 of P group 0 in segments 0-3, of group 1 in 4-7 (two per segment);
+  //   PV: group 0, d-tile s - 4 in segments 4-9; group 1, d-tile s - 8 in 8-13.
+  // Operands of segment s + 1 are read during segment s (two register slots).
+  auto step = [&](int u, auto par, f32x16_t& cur, f32x16_t& nx) {
+    constexpr int P = decltype(par)::value;
+    constexpr int vs = P % kMlaStages, ks = (P + 1) % kMlaStages;
+    if (u + kMlaStages - 1 < nh) issue(u + kMlaStages - 1);   // stage of half-tile u - 1
+    // row max over this half-tile and the accumulator rescale
+    const int len = p.Nkv - u * kMlaHalf;
+    float mx = rawmax;
+    if (len < kMlaHalf) {
+      mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
-        if (len < kTileKeys && key >= len) sc[kt][i] = -INFINITY;
-        mx = fmaxf(mx, sc[kt][i]);
+        const int key = 8 * (i >> 2) + 4 * hg + (i & 3);
+        if (key >= len) cur[i] = -INFINITY;
+        mx = fmaxf(mx, cur[i]);
       }
+    }
     mx = mla_half_max(mx) * p.scale_log2;
     const bool grow = mx > m;
     if (__any(grow)) {
@@ -193,36 +222,69 @@ void mla_attn_kernel(const MlaParams p) {
       for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
     }
     const float m_use = m == -INFINITY ? 0.f : m;
-    // O^T += V^T P^T, key group g = 16 keys
-    const int vcol16 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+
+    f16x8_t kr[2], v0[2], v1[2];
+    auto fetch = [&](int s1) {
+      if (s1 < NST) kr[s1 & 1] = kfrag(ks, s1);
+      if (s1 >= 4 && s1 < 10) v0[s1 & 1] = vfrag(vs, 0, s1 - 4);
+      if (s1 >= 8 && s1 < 14) v1[s1 & 1] = vfrag(vs, 1, s1 - 8);
+    };
+    nx = f32x16_t{};
+    f32x8_t pf;
+    f16x8_t pb0 = {}, pb1 = {};
+    fetch(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kt = g >> 1, u = g & 1;
-      f32x8_t pf;
+    for (int s = 0; s < NST; ++s) {
+      if (s + 1 < NST) fetch(s + 1);
+      if (s < 8) {
+        const int g = s >> 2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * u + e], p.scale_log2, -m_use));
-        l += pf[e];
+        for (int e = 2 * (s & 3); e < 2 * (s & 3) + 2; ++e) {
+          pf[e] = __builtin_amdgcn_exp2f(fmaf(cur[8 * g + e], p.scale_log2, -m_use));
+          l += pf[e];   // float32 weights: the LSE must not carry the fp16 rounding of P
+        }
+        if (s == 3) pb0 = __builtin_convertvector(pf, f16x8_t);
+        if (s == 7) pb1 = __builtin_convertvector(pf, f16x8_t);
       }
-      const f16x8_t pb = __builtin_convertvector(pf, f16x8_t);
-      // V^T operand rows: key rows 32 kt + 16 u + 4 hg + (lane & 15) / 4 (+ 8),
-      // values 32 dt + 8 vcol16 + 4 (lane & 1)
-      const int vrow = 32 * kt + 16 * u + 4 * hg + ((lane & 15) >> 2);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int c = 4 * dt + vcol16;
-        const char* p0 = tb + vrow * kMlaRowB + 16 * (c ^ mla_swz(vrow)) + 8 * (lane & 1);
-        const char* p1 = tb + (vrow + 8) * kMlaRowB + 16 * (c ^ mla_swz(vrow + 8)) + 8 * (lane & 1);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p0)));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p1)));
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, acc[dt], 0, 0, 0);
-      }
+      if (s >= 4 && s < 10) acc[s - 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0[s & 1], pb0, acc[s - 4], 0, 0, 0);
+      if (s >= 8) acc[s - 8] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1[s & 1], pb1, acc[s - 8], 0, 0, 0);
+      nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[s & 1], qreg[s], nx, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // tile t+1 landed (own loads), then every wave's loads and reads are done
-    __builtin_amdgcn_s_waitcnt(0x3F70);     // vmcnt(0)
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+    rawmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, nx[i]);
+    // half-tile u + 2 (issued one iteration earlier) must have landed; this
+    // iteration's load may stay in flight.  Then every wave's loads are
+    // visible and every read of stage u % 4 is done before it is refilled.
+    if (u + kMlaStages - 1 < nh) {
+#define CA_MLA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (0 << 8) | (((n) >> 4) << 14))
+      CA_MLA_WAIT_VM(NLD);
+    } else {
+      CA_MLA_WAIT_VM(0);
+#undef CA_MLA_WAIT_VM
+    }
     block_sync();
+  };
+
+  if (nh > 0) {
+#pragma unroll
+    for (int j = 0; j < kMlaStages - 1; ++j)
+      if (j < nh) issue(j);
+    __builtin_amdgcn_s_waitcnt(0x3F70);     // vmcnt(0)
+    block_sync();
+    f32x16_t sa = f32x16_t{}, sb;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag(0, st), qreg[st], sa, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, sa[i]);
+    for (int u = 0; u < nh; u += kMlaStages) {
+      step(u, std::integral_constant<int, 0>{}, sa, sb);
+      if (u + 1 < nh) step(u + 1, std::integral_constant<int, 1>{}, sb, sa);
+      if (u + 2 < nh) step(u + 2, std::integral_constant<int, 2>{}, sa, sb);
+      if (u + 3 < nh) step(u + 3, std::integral_constant<int, 3>{}, sb, sa);
+    }
   }
 
   const float lt = mla_half_sum(l);
