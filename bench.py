@@ -435,6 +435,11 @@ def main():
     f_sparse = 4.0 * d * (float(shared_toks.sum()) * Nq + float((local_toks * qlen).sum()))
     f_step = f_dense + f_merge + f_sparse if args.only == "step" else f_dense
 
+    # which schedule the dense call runs (found before the warm-up, so that a
+    # kernel trace of this command averages over the timed launches); the
+    # dense-only mode used for counter runs launches nothing else
+    schedule = (effective_schedule(ca, q, k, v, w.scale, policy) if args.only == "step"
+                else args.schedule)
     stream = torch.cuda.current_stream()
     if args.sustain > 0:
         t_s = time.perf_counter()
@@ -480,7 +485,6 @@ def main():
         res["sparse_path_ms"] = sum(e[2].elapsed_time(e[3]) for e in ev) / n
     log(f"timed {n} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / n:.3f}), {res}")
 
-    schedule = effective_schedule(ca, q, k, v, w.scale, policy)
     achieved = f_dense / (t_dense * 1e-3) / 1e12
     kv_bytes = 2.0 * Nkv * H * d * 2 * B
     traffic = traffic_from_counters()
