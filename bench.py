@@ -46,7 +46,15 @@ def log(*a):
 
 
 def src_hash() -> str:
-    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the attention kernel's code: attn_fwd.hip with // comments,
+    surrounding whitespace and blank lines removed, so that counters stay
+    attached to the code they were taken on and not to its comments."""
+    lines = []
+    for line in open(ATTN_SRC, encoding="utf-8").read().splitlines():
+        code = line.split("//", 1)[0].strip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def traffic_from_counters():
@@ -57,7 +65,7 @@ def traffic_from_counters():
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if c.get("attn_fwd_sha256_16") != src_hash():
+    if c.get("attn_fwd_code_sha256_16") != src_hash():
         return None
     return c.get("hbm_bytes_per_call")
 

@@ -162,8 +162,9 @@ struct TileLoader {
   }
 };
 
-// Two waves per SIMD: caps VGPR + AGPR at 256 per lane, so a CU holds 8 waves
-// (one 8-wave workgroup, or two of 4 waves, or four of 2).
+// Two waves per SIMD: caps VGPR + AGPR at 256 per lane, so a CU holds at most
+// 8 waves: one 8-wave workgroup; smaller workgroups are held to two per CU by
+// their 64 KB of LDS (d = 128).
 template <int D, int NW, int MODE, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const AttnParams p) {
