@@ -46,10 +46,16 @@ constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 // 8-wave workgroup (256 query rows) holds a CU's 8 waves, so each K/V tile
 // goes from L2 to LDS once per CU for 256 rows.  With two stages each, the stage of every
 // read is a compile-time constant in the two-iteration unrolled loop.
+//
+// 2-wave workgroups (64-row query blocks, the per-query-block lists) stream
+// 32-key tiles instead: each list entry (a block of up to 64 tokens) becomes
+// two tiles, and the 32 KB ring lets four such workgroups, i.e. two waves
+// per SIMD, share a CU (a 64 KB ring held them to one wave per SIMD).
 template <int D, int NW>
 struct Layout {
+  static constexpr int TK = NW == 2 ? 32 : kTileKeys;  // keys per tile
   static constexpr int ROWB = 2 * D;                    // bytes per K / V row
-  static constexpr int TILEB = kTileKeys * ROWB;        // bytes per K or V tile
+  static constexpr int TILEB = TK * ROWB;               // bytes per K or V tile
   static constexpr int KSTAGES = 2;
   static constexpr int VSTAGES = 2;
   static constexpr int LDSB = (KSTAGES + VSTAGES) * TILEB;
@@ -172,6 +178,11 @@ void attn_fwd_kernel(const AttnParams p) {
   constexpr int BM = NW * 32;
   constexpr int NST = D / 16;     // MFMA k-steps over d for S
   constexpr int NDT = D / 32;     // 32-row d tiles of O^T
+  constexpr int TK = L::TK;       // keys per tile
+  constexpr int KT = TK / 32;     // 32-key halves of a tile (S accumulators)
+  constexpr int NG = 2 * KT;      // 16-key P groups of a tile
+  constexpr int TPE = kTileKeys / TK;   // tiles per list entry (block mode)
+  static_assert(MODE == MODE_BLOCKS || TK == kTileKeys, "range mode streams 64-key tiles");
   // K and V stages as two LDS objects, so that the reads of each carry the
   // object they come from.
   __shared__ __attribute__((aligned(1024))) char kst[L::KSTAGES * L::TILEB];
@@ -301,7 +312,7 @@ void attn_fwd_kernel(const AttnParams p) {
     lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
     hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
     list0 = lo;
-    ntiles = hi - lo;
+    ntiles = (hi - lo) * TPE;
     kh = p.k + b * p.ks_b + h * p.ks_h;
     vh = p.v + b * p.ks_b + h * p.ks_h;
     kstride = p.ks_n;
@@ -309,18 +320,31 @@ void attn_fwd_kernel(const AttnParams p) {
 
   // tile t -> (element offset of its row 0, number of valid rows).  Called
   // for t = 0, 1, 2, ... in order; in block mode each call also fetches the
-  // next tile's block id, so that its latency overlaps one iteration.  In
-  // range mode tile t covers keys [(kt0 + t) 64, +64) of the key set; a tile
-  // past its end (possible only when the schedule's tile count exceeds the
-  // device-side span) has no valid rows.
+  // next list entry's block id, so that its latency overlaps one iteration
+  // (with 32-key tiles, entry t / 2 gives tile t its half t % 2; the second
+  // half of a short block has no valid rows).  In range mode tile t covers
+  // keys [(kt0 + t) 64, +64) of the key set; a tile past its end (possible
+  // only when the schedule's tile count exceeds the device-side span) has no
+  // valid rows.
   int id_next = (MODE == MODE_BLOCKS && ntiles > 0) ? ld_uniform(p.indices, list0) : 0;
+  int id_hold = 0;
   auto tile_src = [&](int t, int64_t& off, int& len) {
     if (MODE == MODE_BLOCKS) {
-      const int id = id_next;
-      if (t + 1 < ntiles) id_next = ld_uniform(p.indices, list0 + t + 1);
+      const int half = TPE == 2 ? (t & 1) : 0;
+      const int e = TPE == 2 ? (t >> 1) : t;
+      if (half == 0) {
+        id_hold = id_next;
+        if (e + 1 < ntiles / TPE) id_next = ld_uniform(p.indices, list0 + e + 1);
+      }
+      const int id = id_hold;
       int s0 = 0, l0 = 0;
       if (id >= 0 && id < p.nkb)
         block_span(id, p.Nkv, p.kv_block, p.kv_seg, p.kv_bps, s0, l0, p.kv_bps_magic);
+      if (TPE == 2) {
+        s0 += TK * half;
+        l0 -= TK * half;
+        l0 = l0 < 0 ? 0 : (l0 > TK ? TK : l0);
+      }
       off = (int64_t)s0 * kstride;
       len = l0;
     } else {
@@ -394,7 +418,7 @@ void attn_fwd_kernel(const AttnParams p) {
   // S^T = K Q^T for the two 32-key halves of the tile in K stage ks.
   auto qk = [&](int ks, f32x16_t (&sc)[2]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       sc[kt] = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
@@ -411,10 +435,10 @@ void attn_fwd_kernel(const AttnParams p) {
   // here.  Key of sc[kt][i] = 32kt + 8(i/4) + 4hg + i%4.
   auto prep = [&](f32x16_t (&sc)[2], int len_cur, float rawmax) {
     float mx = rawmax;
-    if (len_cur < kTileKeys) {
+    if (len_cur < TK) {
       mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kt + 8 * (i >> 2) + 4 * hg + (i & 3);
@@ -446,10 +470,10 @@ void attn_fwd_kernel(const AttnParams p) {
   // group 3's PV.
   constexpr int QPG = NST / 2;                      // K fragments per group
   constexpr int SEG = QPG > NDT ? QPG : NDT;        // segments per group
-  constexpr int NSEG = 4 * SEG + NDT;
+  constexpr int NSEG = NG * SEG + NDT;
   constexpr int EPS = 8 / SEG;                      // exp2 per segment
   constexpr int PD = 2;                             // operand read-ahead, segments
-  auto has_qk = [](int s_) { return s_ < 4 * SEG && (s_ % SEG) < QPG; };
+  auto has_qk = [](int s_) { return s_ < NG * SEG && (s_ % SEG) < QPG; };
   auto has_pv = [](int s_) { return s_ >= SEG && (s_ % SEG) < NDT; };
   auto kfrag = [&](int ks, int g, int i) {
     const int st = (g & 1) * QPG + i;
@@ -481,9 +505,12 @@ void attn_fwd_kernel(const AttnParams p) {
     nx[0] = f32x16_t{};
     nx[1] = f32x16_t{};
     float nm0 = -INFINITY, nm1 = -INFINITY;
+    // Row max of the next tile: with two halves, nx[0]'s during segments
+    // M0 .. M0 + 3 (after its last QK MFMA in group 1) and nx[1]'s in the NDT
+    // tail segments; with one half, nx[0]'s in the tail segments.
     constexpr int M0 = 2 * SEG + 1;                 // segments taking nx[0]'s max
-    constexpr int M1 = 4 * SEG;                     // segments taking nx[1]'s max
-    constexpr int V1 = 16 / NDT;                    // nx[1] values per tail segment
+    constexpr int M1 = NG * SEG;                    // tail segments: the last half's max
+    constexpr int V1 = 16 / NDT;                    // values per tail segment
     bf16x8_t pb = {};
     f32x8_t pf;
 #pragma unroll
@@ -491,7 +518,7 @@ void attn_fwd_kernel(const AttnParams p) {
       const int g = s_ / SEG, i = s_ % SEG;
       if (s_ + PD < NSEG) fetch(s_ + PD, ks, vs);
       // softmax VALU work of group g
-      if (g < 4) {
+      if (g < NG) {
         const int kt = g >> 1, u = g & 1;
 #pragma unroll
         for (int e = i * EPS; e < (i + 1) * EPS; ++e) {
@@ -499,24 +526,24 @@ void attn_fwd_kernel(const AttnParams p) {
           l += pf[e];   // float32 weights: the LSE must not carry bf16 rounding
         }
       }
-      if (s_ >= M0 && s_ < M0 + 4)
+      if (KT == 2 && s_ >= M0 && s_ < M0 + 4)
 #pragma unroll
         for (int e = 4 * (s_ - M0); e < 4 * (s_ - M0 + 1); ++e) nm0 = fmaxf(nm0, nx[0][e]);
       if (s_ >= M1)
 #pragma unroll
-        for (int e = V1 * (s_ - M1); e < V1 * (s_ - M1 + 1); ++e) nm1 = fmaxf(nm1, nx[1][e]);
+        for (int e = V1 * (s_ - M1); e < V1 * (s_ - M1 + 1); ++e) nm1 = fmaxf(nm1, nx[KT - 1][e]);
       const int slot = s_ % (PD + 1);
       if (has_pv(s_))
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[slot], pb, acc[i], 0, 0, 0);
       if (has_qk(s_))
         nx[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[slot], qreg[(g & 1) * QPG + i],
                                                             nx[g >> 1], 0, 0, 0);
-      if (g < 4 && i == SEG - 1) pb = __builtin_convertvector(pf, bf16x8_t);
+      if (g < NG && i == SEG - 1) pb = __builtin_convertvector(pf, bf16x8_t);
       __builtin_amdgcn_sched_barrier(0);
     }
     nmax = fmaxf(nm0, nm1);
   };
-  static_assert(2 * SEG + 1 + 4 <= NSEG && 16 % NDT == 0, "max segments must fit the body");
+  static_assert((KT == 1 || 2 * SEG + 1 + 4 <= NSEG) && 16 % NDT == 0, "max segments must fit the body");
 
   // Load pipeline.  K(t) is last read by the QK MFMAs of iteration t-1, so
   // K(t + KSTAGES) goes out at the start of iteration t; V(t) is read in
@@ -601,7 +628,8 @@ void attn_fwd_kernel(const AttnParams p) {
   };
   // Dual output (block mode): after the first `snap` tiles of the list the
   // state is also written to the snapshot outputs.
-  const int snap = (MODE == MODE_BLOCKS && p.snap >= 0) ? (p.snap < ntiles ? p.snap : ntiles) : -1;
+  const int snap = (MODE == MODE_BLOCKS && p.snap >= 0)
+                       ? (p.snap * TPE < ntiles ? p.snap * TPE : ntiles) : -1;
 
   // One iteration: the first operand reads of the fused body go out right
   // after the barrier, ahead of the load issue and the rescale.
@@ -658,7 +686,7 @@ void attn_fwd_kernel(const AttnParams p) {
     wait_vm(0);
     qk(0, sa);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, sa[kt][i]);
     // iteration 0 refills K stage 0, which every wave has just read
