@@ -294,6 +294,29 @@ int ca_block_score_topk(const float* q_mean, const float* k_mean,
                         int32_t* out_idx, float* out_score, void* stream);
 
 /*
+ * ca_block_score_topk that also writes the PBSA block lists (Sparse Forcing
+ * page, section 2 item 3) of the selection in the same launch, for the case
+ * where the lists are a fixed prefix range followed by the selected ids:
+ * CSR row r = (b*H + h)*NQB + qb holds W = prefix_count + K ids,
+ *   prefix_begin .. prefix_begin + prefix_count - 1, then
+ *   id_offset + out_idx[b,h,qb,0..K-1] (ascending).
+ * The result equals ca_build_kv_index with sink range = the prefix and this
+ * selection as its persistent ids (NQB = 1) or top-K ids (id_offset as
+ * topk_offset), without the separate launch.
+ *   out_idx  int32 [B, H, NQB, K] as ca_block_score_topk (required)
+ *   indptr   int32 [B*H*NQB + 1] (= r * W); indices int32 [B*H*NQB*W]
+ *   limits   as ca_block_score_topk; prefix_begin, prefix_count >= 0 and
+ *            prefix_begin + prefix_count <= id_offset + cand_begin (so every
+ *            row is sorted and free of duplicates), else CA_EINVAL
+ */
+int ca_block_score_topk_lists(const float* q_mean, const float* k_mean,
+                              int B, int H, int NQB, int NKB, int d,
+                              int cand_begin, int cand_count, int K,
+                              int prefix_begin, int prefix_count, int id_offset,
+                              int32_t* out_idx, int32_t* indptr, int32_t* indices,
+                              void* stream);
+
+/*
  * Persistent-memory update when the local window slides (Sparse Forcing
  * page, section 2 item 1, memory management: blocks evicted from the local
  * window are candidates, and the top C by coarse score are kept or updated as

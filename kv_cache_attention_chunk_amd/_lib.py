@@ -47,6 +47,8 @@ SIGNATURES = {
                           _i64p, _i64p, _i64p, _p]),
     "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),
     "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "ca_block_score_topk_lists": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                       _p, _p, _p, _p]),
     "ca_persistent_update": (_i, [_p, _p, _i, _i, _i, _i, _i32p, _i, _i, _i, _i, _p, _p, _p]),
     "ca_pack_ragged": (_i, [_p, _p, _i, _i, _i, _i, _i64p, _i, _i32p, _i32p, _i, _i32p, _p, _p,
                             _i64, _p, _p]),

@@ -357,6 +357,34 @@ def block_score_topk(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *, cand
     return (idx, sc) if return_scores else idx
 
 
+def block_score_topk_lists(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *,
+                           cand_begin: int = 0, cand_count: Optional[int] = None,
+                           prefix_begin: int = 0, prefix_count: int = 0, id_offset: int = 0):
+    """block_score_topk that also returns the PBSA block lists of the selection
+    (one launch): CSR row (b, h, qb) = prefix_begin .. prefix_begin +
+    prefix_count - 1, then id_offset + the K selected ids.  The prefix must lie
+    below every selected id + id_offset.  Returns (idx, indptr, indices)."""
+    for n, t in (("q_mean", q_mean), ("k_mean", k_mean)):
+        if t.dtype != torch.float32 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 GPU tensor [B, H, N, d]")
+    B, H, NQB, d = q_mean.shape
+    NKB = k_mean.shape[2]
+    if tuple(k_mean.shape) != (B, H, NKB, d):
+        raise ValueError("k_mean shape mismatch")
+    cc = NKB - cand_begin if cand_count is None else cand_count
+    rows = B * H * NQB
+    dev = q_mean.device
+    idx = torch.empty((B, H, NQB, K), dtype=torch.int32, device=dev)
+    indptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    indices = torch.empty(max(rows * (prefix_count + K), 1), dtype=torch.int32, device=dev)
+    st = lib().ca_block_score_topk_lists(q_mean.data_ptr(), k_mean.data_ptr(), B, H, NQB, NKB, d,
+                                         cand_begin, cc, K, prefix_begin, prefix_count, id_offset,
+                                         idx.data_ptr(), indptr.data_ptr(), indices.data_ptr(),
+                                         _stream())
+    check(st)
+    return idx, indptr, indices
+
+
 def persistent_update(q_mean: torch.Tensor, k_mean: torch.Tensor,
                       persistent: Optional[torch.Tensor], evict_begin: int, evict_count: int,
                       C: int, *, out: Optional[torch.Tensor] = None, return_scores: bool = False):
@@ -533,18 +561,30 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
             loc_base = 0
         elif K:
             km_loc = block_mean(k, block, kv_seg)
-    pers = block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count) if C else None
-    loc = (block_score_topk(qm, km_loc, K, cand_begin=loc_base, cand_count=local_count)
-           if K else None)
+    # Selection and block lists in one launch each when a list is a prefix
+    # range followed by the selected ids; otherwise a separate merge.
     nqb = qm.shape[2]
-    sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
-                                    None if pers is None else pers[:, :, 0, :].contiguous(),
-                                    None, 0, device=q.device)
+    if C and sink_begin + sink_count <= hist_begin:
+        pers, sh_ptr, sh_idx = block_score_topk_lists(cm, km, C, cand_begin=hist_begin,
+                                                      cand_count=hist_count,
+                                                      prefix_begin=sink_begin,
+                                                      prefix_count=sink_count)
+    else:
+        pers = (block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count)
+                if C else None)
+        sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
+                                        None if pers is None else pers[:, :, 0, :].contiguous(),
+                                        None, 0, device=q.device)
+    if K:
+        loc, lo_ptr, lo_idx = block_score_topk_lists(qm, km_loc, K, cand_begin=loc_base,
+                                                     cand_count=local_count,
+                                                     id_offset=local_begin - loc_base)
+    else:
+        loc = None
+        lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, None, 0, device=q.device)
     o1, l1 = chunk_attn_fwd(q, k, v, kv_indptr=sh_ptr, kv_indices=sh_idx, kv_block=block,
                             kv_seg=seg, q_block=Nq, q_seg=Nq, scale=scale,
                             out_dtype=torch.float32)
-    lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, loc, local_begin - loc_base,
-                                    device=q.device)
     o, l = chunk_attn_fwd(q, k, v, kv_indptr=lo_ptr, kv_indices=lo_idx, kv_block=block,
                           kv_seg=seg, q_block=block, q_seg=seg, scale=scale,
                           out_dtype=out_dtype, o_init=o1, lse_init=l1)

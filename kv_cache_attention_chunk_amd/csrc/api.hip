@@ -557,6 +557,31 @@ int ca_block_score_topk(const float* q_mean, const float* k_mean, int B, int H, 
                   "block_score_topk launch");
 }
 
+int ca_block_score_topk_lists(const float* q_mean, const float* k_mean, int B, int H, int NQB,
+                              int NKB, int d, int cand_begin, int cand_count, int K,
+                              int prefix_begin, int prefix_count, int id_offset,
+                              int32_t* out_idx, int32_t* indptr, int32_t* indices, void* stream) {
+  if (B < 0 || H < 0 || NQB < 0 || NKB < 0) return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 4 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 4, <= 512)", d);
+  if (!q_mean || !k_mean || !out_idx || !indptr || !indices) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(q_mean) || !aligned16(k_mean)) return fail(CA_EINVAL, "means must be 16-byte aligned");
+  if (cand_count < 1 || cand_count > 4096) return fail(CA_ERANGE, "cand_count %d outside 1..4096", cand_count);
+  if (cand_begin < 0 || cand_begin + cand_count > NKB) return fail(CA_ERANGE, "candidate range outside [0, NKB)");
+  if (K < 1 || K > cand_count) return fail(CA_ERANGE, "K=%d outside 1..cand_count", K);
+  if ((int64_t)B * H > 65535 || NQB > 0x7FFFFFFF) return fail(CA_ERANGE, "grid too large");
+  if (prefix_begin < 0 || prefix_count < 0) return fail(CA_EINVAL, "negative prefix");
+  if ((int64_t)id_offset + cand_begin < 0 || (int64_t)id_offset + cand_begin + cand_count > 0x7FFFFFFF)
+    return fail(CA_ERANGE, "id_offset out of range");
+  if ((int64_t)prefix_begin + prefix_count > (int64_t)id_offset + cand_begin)
+    return fail(CA_EINVAL, "prefix range must lie below every candidate id + id_offset");
+  if ((int64_t)B * H * NQB * (prefix_count + K) > 0x7FFFFFFF) return fail(CA_ERANGE, "too many entries");
+  if (int r = check_device()) return r;
+  return launched(launch_score_topk(q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
+                                    out_idx, nullptr, static_cast<hipStream_t>(stream), indptr,
+                                    indices, prefix_begin, prefix_count, id_offset),
+                  "block_score_topk_lists launch");
+}
+
 int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H, int NKB, int d,
                          const int32_t* persistent, int C_in, int evict_begin, int evict_count,
                          int C, int32_t* out, float* out_score, void* stream) {

@@ -106,9 +106,14 @@ int attention_slots(int d);
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
                              const int64_t* xs, int block, int seg, int bps, int nb,
                              float* out, float* out_total, hipStream_t stream);
+// With indptr non-null the kernel also writes each row's block list: the
+// prefix range [prefix_begin, prefix_begin + prefix_count) followed by
+// id_offset + the selected ids (W = prefix_count + K entries per row).
 hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int NQB,
                              int NKB, int d, int cand_begin, int cand_count, int K,
-                             int32_t* out_idx, float* out_score, hipStream_t stream);
+                             int32_t* out_idx, float* out_score, hipStream_t stream,
+                             int32_t* indptr = nullptr, int32_t* indices = nullptr,
+                             int prefix_begin = 0, int prefix_count = 0, int id_offset = 0);
 hipError_t launch_persistent_update(const float* qm, const float* km, int B, int H, int NKB,
                                    int d, const int32_t* pers, int C_in, int evict_begin,
                                    int evict_count, int C, int32_t* out, float* out_score,

@@ -98,7 +98,18 @@ __global__ __launch_bounds__(kMeanThreads) void total_mean_kernel(
 //     candidates with rank < K are written in index order, i.e. ascending
 //     block id.
 // Scores live in dynamic LDS, padded with -inf to a multiple of 4.
+// Optionally the kernel also writes each row's PBSA block list (CSR row
+// r = (b*H + h)*NQB + qb of W = prefix_count + K entries): the prefix range
+// [prefix_begin, prefix_begin + prefix_count) followed by id_offset + the
+// selected ids.  The caller guarantees the prefix lies below every selected
+// id, so the row is sorted and free of duplicates as written.
 // ---------------------------------------------------------------------------
+struct TopkLists {
+  int32_t* indptr;           // nullptr: no block lists
+  int32_t* indices;
+  int prefix_begin, prefix_count, id_offset, rows;
+};
+
 constexpr int kTopkMaxCand = 4096;
 constexpr int kTopkBatch = 16;
 
@@ -109,7 +120,8 @@ __host__ __device__ constexpr int topk_lds_bytes(int n, int threads) {
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int NQB, int NKB, int d,
-    int cand_begin, int n, int K, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+    int cand_begin, int n, int K, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
+    const TopkLists lists) {
   extern __shared__ __attribute__((aligned(16))) float topk_lds[];
   const int n4 = (n + 3) >> 2;
   float* ss = topk_lds;                                          // [4 n4] scores
@@ -202,6 +214,16 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
   // the K candidates of rank < K, compacted in index order
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t o = ((int64_t)bh * NQB + qb) * K;
+  const int W = lists.prefix_count + K;
+  const int64_t row = (int64_t)bh * NQB + qb;
+  if (lists.indptr) {
+    for (int j = tid; j < lists.prefix_count; j += THREADS)
+      lists.indices[row * W + j] = lists.prefix_begin + j;
+    if (tid == 0) {
+      lists.indptr[row] = (int32_t)(row * W);
+      if (row == lists.rows - 1) lists.indptr[lists.rows] = lists.rows * W;
+    }
+  }
   int carry = 0;
   for (int c0 = 0; c0 < n; c0 += THREADS) {
     const int i = c0 + tid;
@@ -220,6 +242,7 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
       if (pos < K) {
         out_idx[o + pos] = cand_begin + i;
         if (out_score) out_score[o + pos] = ss[i];
+        if (lists.indptr) lists.indices[row * W + lists.prefix_count + pos] = lists.id_offset + cand_begin + i;
       }
     }
     carry += tot;
@@ -542,16 +565,20 @@ hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d, cons
 
 hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int NQB, int NKB,
                              int d, int cand_begin, int cand_count, int K, int32_t* out_idx,
-                             float* out_score, hipStream_t stream) {
+                             float* out_score, hipStream_t stream, int32_t* indptr,
+                             int32_t* indices, int prefix_begin, int prefix_count, int id_offset) {
   if (B * H == 0 || NQB == 0) return hipSuccess;
+  const TopkLists lists{indptr, indices, prefix_begin, prefix_count, id_offset, B * H * NQB};
   // small candidate sets: 256-thread workgroups, several resident per CU
   const dim3 grid(NQB, B * H);
   if (cand_count <= 256)
     hipLaunchKernelGGL(score_topk_kernel<256>, grid, dim3(256), topk_lds_bytes(cand_count, 256),
-                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score);
+                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score,
+                       lists);
   else
     hipLaunchKernelGGL(score_topk_kernel<1024>, grid, dim3(1024), topk_lds_bytes(cand_count, 1024),
-                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score);
+                       stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score,
+                       lists);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -139,6 +139,15 @@ def test_merge_mean_topk_index_checks(L):
     assert t(cb=451) == CA_ERANGE
     assert t(cc=5000) == CA_ERANGE
     assert L.ca_build_kv_index(1, 2, 75, 0, 25, None, 32, FAKE, 10, 0, FAKE, FAKE, None) == CA_EINVAL
+    tl = lambda **kw: L.ca_block_score_topk_lists(FAKE, FAKE, 1, 2, 75, 525, 128, kw.get("cb", 25),
+                                                  425, 32, kw.get("pb", 0), kw.get("pc", 25),
+                                                  kw.get("off", 0), FAKE, kw.get("ip", FAKE),
+                                                  FAKE, None)
+    assert tl(ip=None) == CA_EINVAL
+    assert tl(pc=26) == CA_EINVAL                      # prefix reaches the first candidate id
+    assert tl(pc=-1) == CA_EINVAL
+    assert tl(off=-26) == CA_ERANGE
+    assert tl(pb=10, pc=10, off=-6) == CA_EINVAL       # prefix end 20 > first id -6 + 25
     u = lambda **kw: L.ca_persistent_update(FAKE, FAKE, 1, 12, 525, kw.get("d", 128), kw.get("p", FAKE),
                                             kw.get("cin", 32), kw.get("eb", 450), kw.get("ne", 75),
                                             kw.get("C", 32), kw.get("out", FAKE + 4096), None, None)

@@ -313,6 +313,31 @@ def test_build_kv_index_dedup_and_offset():
     np.testing.assert_array_equal(ix.cpu().numpy()[:len(ixr)], ixr)
 
 
+@pytest.mark.parametrize("cb,cc,K,pb,pc,off", [
+    (25, 425, 32, 0, 25, 0),        # shared list: sink prefix + persistent ids (1024 threads)
+    (0, 75, 10, 0, 0, 450),         # local list: window-relative ids + offset (256 threads)
+    (400, 100, 7, 10, 300, 0),      # prefix longer than the workgroup
+    (3, 4, 4, 0, 3, 0),             # K = candidate count
+])
+def test_topk_lists_match_separate_index_build(cb, cc, K, pb, pc, off):
+    """Selection and block lists in one launch equal the separate top-K
+    launch followed by the list merge (the oracle's build_kv_index)."""
+    say(f"topk lists cb={cb} cc={cc} K={K} prefix={pb}+{pc} off={off}")
+    rng = np.random.default_rng(cb + cc + K)
+    B, H, NQB = 2, 3, 37
+    qm = rng.standard_normal((B, H, NQB, 128)).astype(np.float32) / 8
+    km = rng.standard_normal((B, H, cb + cc + 5, 128)).astype(np.float32) / 8
+    qt, kt = torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda()
+    idx, ip, ix = ca.block_score_topk_lists(qt, kt, K, cand_begin=cb, cand_count=cc,
+                                            prefix_begin=pb, prefix_count=pc, id_offset=off)
+    ref_idx = ca.block_score_topk(qt, kt, K, cand_begin=cb, cand_count=cc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx.cpu().numpy())
+    ipr, ixr = orc.build_kv_index(B, H, NQB, pb, pc, None, idx.cpu().numpy(), off)
+    np.testing.assert_array_equal(ip.cpu().numpy(), ipr)
+    np.testing.assert_array_equal(ix.cpu().numpy(), ixr)
+
+
 @pytest.mark.parametrize("d", [24, 64, 128, 512])
 def test_block_mean_with_chunk_mean(d):
     """Block means and the mean over all tokens (the chunk-mean query), for
