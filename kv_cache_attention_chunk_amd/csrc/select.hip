@@ -91,11 +91,17 @@ __global__ __launch_bounds__(kMeanThreads) void total_mean_kernel(
 //     and the loads of a batch of candidates are all issued before any is
 //     used; otherwise each thread scores whole candidates sequentially.
 //     A NaN score ranks as -inf.
-//   * selection by rank: rank(i) = #{j : s_j > s_i} + #{j < i : s_j = s_i},
-//     the position in (score descending, block id ascending) order.  F
-//     threads share one candidate, each counting a slice of j four scores at
-//     a time; the second term is counted only when s_i has a tie.  The
-//     candidates with rank < K are written in index order, i.e. ascending
+//   * selection: the K candidates first in (score descending, block id
+//     ascending) order, i.e. rank(i) = #{j : s_j > s_i} + #{j < i : s_j =
+//     s_i} below K.  Up to kRankMaxCand candidates the ranks are counted
+//     directly: F threads share one candidate, each counting a slice of j
+//     four scores at a time; the second term is counted only when s_i has a
+//     tie.  Above that (the count grows as n^2), a radix select finds the
+//     K-th largest score T in four 8-bit digit passes over an order-
+//     preserving integer image of the scores, together with the number of
+//     T-valued candidates to take (need = K - #{s > T}); the selection is
+//     then {s > T} and the first `need` candidates with s = T, the same set.
+//     The selected candidates are written in index order, i.e. ascending
 //     block id.
 // Scores live in dynamic LDS, padded with -inf to a multiple of 4.
 // Optionally the kernel also writes each row's PBSA block list (CSR row
@@ -112,9 +118,79 @@ struct TopkLists {
 
 constexpr int kTopkMaxCand = 4096;
 constexpr int kTopkBatch = 16;
+constexpr int kRankMaxCand = 128;    // larger candidate sets use the radix select
 
 __host__ __device__ constexpr int topk_lds_bytes(int n, int threads) {
-  return 4 * (4 * ((n + 3) / 4)) + 4 * n + 4 * (threads / 64);
+  return 4 * (4 * ((n + 3) / 4)) + 4 * n + 8 * (threads / 64);
+}
+
+// Order-preserving image of a float score (no NaN) as an unsigned integer:
+// -0 is first mapped to +0 so that equal scores have equal images.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x == 0.f ? 0.f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_key_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// K-th largest of the n scores ss[0..n) (1 <= K <= n) by radix select, most
+// significant digit first: each pass histograms the digit of the candidates
+// that match the digits chosen so far, and wave 0 finds the digit whose bin
+// holds the K-th largest (bins scanned from the top).  Returns T and need =
+// its position among the T-valued candidates (1 <= need <= #{s = T}), so
+// #{s > T} = K - need.  hist: 256 ints; state: 2 ints (LDS).
+template <int THREADS>
+__device__ void kth_largest(const float* ss, int n, int K, int* hist, int* state, float& thr,
+                            int& need) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t prefix = 0, mask = 0;
+  int k = K;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += THREADS) hist[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += THREADS) {
+      const uint32_t u = order_key(ss[i]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 255 - 4l .. 252 - 4l (descending)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hist[255 - 4 * lane - e];
+        tot += c[e];
+      }
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      int cum = incl - tot;
+      if (cum < k && k <= incl) {       // exactly one lane
+        bool found = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (!found && cum + c[e] >= k) {
+            found = true;
+            state[0] = 255 - 4 * lane - e;
+            state[1] = k - cum;
+          }
+          cum += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)state[0] << shift;
+    mask |= 0xFFu << shift;
+    k = state[1];
+  }
+  thr = order_key_inv(prefix);
+  need = k;
 }
 
 template <int THREADS>
@@ -126,7 +202,9 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
   const int n4 = (n + 3) >> 2;
   float* ss = topk_lds;                                          // [4 n4] scores
   int* rk = reinterpret_cast<int*>(ss + 4 * n4);                 // [n] ranks
-  int* wcount = rk + n;                                          // [THREADS / 64]
+  int* wcount = rk + n;                                          // [2 THREADS / 64]
+  __shared__ int hist[256];
+  __shared__ int rstate[2];
   const int qb = blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
@@ -177,13 +255,19 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
   }
   __syncthreads();
 
+  // selection: the threshold score T and how many T-valued candidates to
+  // take, or the ranks themselves for small candidate sets
+  const bool radix = n > kRankMaxCand;
+  float thr = 0.f;
+  int need = 0;
+  if (radix) kth_largest<THREADS>(ss, n, K, hist, rstate, thr, need);
   // ranks (padding entries sit above every index, compare as -inf and so
   // never count)
   int F = 1;
   while (F < 64 && n * (2 * F) <= THREADS) F *= 2;
   const int chunk4 = (n4 + F - 1) / F;
   const f32x4_t* ss4 = reinterpret_cast<const f32x4_t*>(ss);
-  for (int base = 0; base < n; base += THREADS / F) {
+  for (int base = 0; base < (radix ? 0 : n); base += THREADS / F) {
     const int i = base + tid / F;
     const int part = tid & (F - 1);
     int gt = 0, eq = 0;
@@ -224,28 +308,47 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
       if (row == lists.rows - 1) lists.indptr[lists.rows] = lists.rows * W;
     }
   }
-  int carry = 0;
+  // position of a selected candidate = #{selected j < i} = #{j < i : s_j > T}
+  // + min(#{j < i : s_j = T}, need) (with ranks: #{j < i : rank_j < K})
+  int carry_gt = 0, carry_eq = 0;
+  const unsigned long long below = (1ull << lane) - 1;
   for (int c0 = 0; c0 < n; c0 += THREADS) {
     const int i = c0 + tid;
-    const bool sel = i < n && rk[i] < K;
-    const unsigned long long m = __ballot(sel);
-    if (lane == 0) wcount[wave] = __popcll(m);
-    __syncthreads();
-    int wpre = 0, tot = 0;
-    for (int w = 0; w < THREADS / 64; ++w) {
-      const int c = wcount[w];
-      wpre += w < wave ? c : 0;
-      tot += c;
+    bool gt = false, eq = false;
+    if (i < n) {
+      if (radix) {
+        gt = ss[i] > thr;
+        eq = ss[i] == thr;
+      } else {
+        gt = rk[i] < K;
+      }
     }
-    if (sel) {
-      const int pos = carry + wpre + __popcll(m & ((1ull << lane) - 1));
+    const unsigned long long mg = __ballot(gt), me = __ballot(eq);
+    if (lane == 0) {
+      wcount[wave] = __popcll(mg);
+      wcount[THREADS / 64 + wave] = __popcll(me);
+    }
+    __syncthreads();
+    int gpre = 0, gtot = 0, epre = 0, etot = 0;
+    for (int w = 0; w < THREADS / 64; ++w) {
+      const int cg = wcount[w], ce = wcount[THREADS / 64 + w];
+      gpre += w < wave ? cg : 0;
+      epre += w < wave ? ce : 0;
+      gtot += cg;
+      etot += ce;
+    }
+    const int before_eq = carry_eq + epre + __popcll(me & below);
+    if (gt || (eq && before_eq < need)) {
+      const int before_gt = carry_gt + gpre + __popcll(mg & below);
+      const int pos = before_gt + (before_eq < need ? before_eq : need);
       if (pos < K) {
         out_idx[o + pos] = cand_begin + i;
         if (out_score) out_score[o + pos] = ss[i];
         if (lists.indptr) lists.indices[row * W + lists.prefix_count + pos] = lists.id_offset + cand_begin + i;
       }
     }
-    carry += tot;
+    carry_gt += gtot;
+    carry_eq += etot;
     __syncthreads();
   }
 }

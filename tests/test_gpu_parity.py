@@ -280,6 +280,30 @@ def test_topk_planted_ties_and_full():
         np.testing.assert_array_equal(sc.cpu().numpy(), ref["score"])
 
 
+@pytest.mark.parametrize("n,K", [(129, 5), (200, 17), (425, 32), (2000, 100), (3000, 2999),
+                                 (4096, 1), (4096, 4096)])
+def test_topk_radix_select_planted_ties(n, K):
+    """Candidate sets above 128 take the radix select (256- and 1024-thread
+    workgroups): ids and scores exact against the oracle with many exact
+    ties (small-integer and half-integer scores), also K = 1 and K = n."""
+    say(f"topk radix n={n} K={K}")
+    d = 128
+    q = np.zeros((1, 2, 3, d), np.float32)
+    q[..., 0] = 1.0
+    q[0, :, 1, 1] = -0.5
+    q[0, :, 2, 0] = -1.0
+    rng = np.random.default_rng(n + K)
+    k = np.zeros((1, 2, n + 3, d), np.float32)
+    k[..., 0] = rng.integers(-20, 21, size=(1, 2, n + 3))
+    k[..., 1] = rng.integers(-4, 5, size=(1, 2, n + 3))
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda()
+    idx, sc = ca.block_score_topk(qt, kt, K, cand_begin=2, cand_count=n, return_scores=True)
+    torch.cuda.synchronize()
+    ref = orc.block_score_topk(q, k, 2, n, K)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(sc.cpu().numpy(), ref["score"])
+
+
 def test_topk_random_and_index_build():
     say("topk random + build_kv_index")
     rng = np.random.default_rng(1)
