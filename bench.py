@@ -137,6 +137,45 @@ def _time_ms(torch, fn, reps=10, warmup_s=0.2):
     return e0.elapsed_time(e1) / reps
 
 
+def _time_calls(torch, fn, reps=20, warmup_s=0.2):
+    """Per-call HIP-event times of fn() in ms (one event pair per call, on the
+    current stream), after about warmup_s seconds of untimed calls."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warmup_s:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(s)
+        fn(i)
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def measured_roofs(torch):
+    """Roofs measured on this GPU: a large bf16 GEMM (torch.matmul, 8192^3,
+    contiguous operands) and a 1 GiB device-to-device copy."""
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    ms_g = _time_ms(torch, lambda: torch.matmul(a, b, out=c), 20)
+    del a, b, c
+    n = 1 << 29                                  # 1 GiB of bf16
+    x = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    ms_c = _time_ms(torch, lambda: y.copy_(x), 20)
+    del x, y
+    return {"bf16_gemm_tflops": round(2.0 * 8192 ** 3 / (ms_g * 1e-3) / 1e12, 1),
+            "copy_GBs": round(2.0 * (1 << 30) / (ms_c * 1e-3) / 1e9, 1),
+            "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB read + 1 GiB written"}
+
+
 def _block_len(ids, block=64, seg=1560):
     """Tokens of frame-aligned block ids (25 blocks per 1560-token frame)."""
     bps = -(-seg // block)
@@ -200,6 +239,21 @@ def per_config(reps=10, wan=None):
     f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
     kvb = 2.0 * w.Nkv * w.H * w.d * 2
     out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps), f, kvb)
+    # per-call spread, warm (one K/V set, resident in the 256 MB Infinity
+    # Cache) and cold (three K/V copies in rotation: 603 MB, more than the
+    # Infinity Cache and L2 hold, so each call reads its K/V from HBM)
+    o_w = torch.empty_like(q)
+    l_w = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    warm = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_w, lse=l_w), 30)
+    sets = [(k, v), (k.clone(), v.clone()), (k.clone(), v.clone())]
+    cold = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(
+        q, sets[i % 3][0], sets[i % 3][1], scale=w.scale, out=o_w, lse=l_w), 30)
+    del sets
+    for name, t in (("warm", warm), ("cold", cold)):
+        out["wan_dense"][f"{name}_ms_median"] = round(float(np.median(t)), 4)
+        out["wan_dense"][f"{name}_ms_min"] = round(float(t.min()), 4)
+    out["wan_dense"]["cold_tflops_median"] = round(f / (float(np.median(cold)) * 1e-3) / 1e12, 1)
+    out["wan_dense"]["cold_kv_GBs_median"] = round(kvb / (float(np.median(cold)) * 1e-3) / 1e9, 1)
     out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
     # local (sink + chunk frames) and full attention from one pass over each head's list
     row = np.array(w.meta["local_blocks"] + w.meta["history_blocks"], np.int32)
@@ -530,6 +584,9 @@ def main():
     if args.only == "step" and not args.no_configs:
         t0 = time.perf_counter()
         out["configs"] = per_config(wan=w)
+        roofs = measured_roofs(torch)
+        out["measured_roofs"] = roofs
+        out["roofline"]["frac_of_measured_gemm"] = round(achieved / roofs["bf16_gemm_tflops"], 4)
         log(f"per-workload timings in {time.perf_counter() - t0:.1f} s")
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
