@@ -192,15 +192,17 @@ def _rec(ms, flops, kv_bytes, **extra):
     return r
 
 
-def per_config(reps=10, wan=None):
+def per_config(reps=10, wan=None, names=None):
     """Time every configured workload once on the GPU (inputs resident):
     tiny dense + merge, Wan dense + merge, block-sparse at three top-K ratios,
     ragged 12-head, mixed 40-head.  FLOPs are algorithmic (4 d per score of
     every key set attended); kv bytes are the distinct K/V bytes the call
-    must read."""
+    must read.  `names` restricts the run to those entries (for per-workload
+    counter collection); their inputs are still built."""
     import torch
     import kv_cache_attention_chunk_amd as ca
     from kv_cache_attention_chunk_amd import workloads as wl
+    want = lambda n: names is None or n in names
     dev = lambda t: torch.from_numpy(t.bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
     out = {}
@@ -229,47 +231,56 @@ def per_config(reps=10, wan=None):
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
     f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
     kvb = 2.0 * w.Nkv * w.H * w.d * 2
-    ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps)
-    ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv), reps)
-    out["tiny_dense"] = {"dense_us": round(ms_d * 1e3, 1), "local_history_merge_us": round(ms_m * 1e3, 1),
-                         "gflop": round(f / 1e9, 3)}
+    if want("tiny_dense"):
+        ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps)
+        ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv), reps)
+        out["tiny_dense"] = {"dense_us": round(ms_d * 1e3, 1),
+                             "local_history_merge_us": round(ms_m * 1e3, 1), "gflop": round(f / 1e9, 3)}
     # Wan-1.3B layer: dense and local/history merge
     w = wan or wl.wan_dense(seed=0)
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
     f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
     kvb = 2.0 * w.Nkv * w.H * w.d * 2
-    out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps), f, kvb)
+    if want("wan_dense"):
+        out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps),
+                                f, kvb)
     # per-call spread, warm (one K/V set, resident in the 256 MB Infinity
     # Cache) and cold (three K/V copies in rotation: 603 MB, more than the
     # Infinity Cache and L2 hold, so each call reads its K/V from HBM)
-    o_w = torch.empty_like(q)
-    l_w = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-    warm = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_w, lse=l_w), 30)
-    sets = [(k, v), (k.clone(), v.clone()), (k.clone(), v.clone())]
-    cold = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(
-        q, sets[i % 3][0], sets[i % 3][1], scale=w.scale, out=o_w, lse=l_w), 30)
-    del sets
-    for name, t in (("warm", warm), ("cold", cold)):
-        out["wan_dense"][f"{name}_ms_median"] = round(float(np.median(t)), 4)
-        out["wan_dense"][f"{name}_ms_min"] = round(float(t.min()), 4)
-    out["wan_dense"]["cold_tflops_median"] = round(f / (float(np.median(cold)) * 1e-3) / 1e12, 1)
-    out["wan_dense"]["cold_kv_GBs_median"] = round(kvb / (float(np.median(cold)) * 1e-3) / 1e9, 1)
-    out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
+    if want("wan_dense"):
+        o_w = torch.empty_like(q)
+        l_w = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+        warm = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_w, lse=l_w),
+                           30)
+        sets = [(k, v), (k.clone(), v.clone()), (k.clone(), v.clone())]
+        cold = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(
+            q, sets[i % 3][0], sets[i % 3][1], scale=w.scale, out=o_w, lse=l_w), 30)
+        del sets
+        for name, t in (("warm", warm), ("cold", cold)):
+            out["wan_dense"][f"{name}_ms_median"] = round(float(np.median(t)), 4)
+            out["wan_dense"][f"{name}_ms_min"] = round(float(t.min()), 4)
+        out["wan_dense"]["cold_tflops_median"] = round(f / (float(np.median(cold)) * 1e-3) / 1e12, 1)
+        out["wan_dense"]["cold_kv_GBs_median"] = round(kvb / (float(np.median(cold)) * 1e-3) / 1e9, 1)
+    if want("wan_merge_variant"):
+        out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
     # local (sink + chunk frames) and full attention from one pass over each head's list
     row = np.array(w.meta["local_blocks"] + w.meta["history_blocks"], np.int32)
     dip, dix = i32(np.arange(w.B * w.H + 1) * len(row)), i32(np.tile(row, w.B * w.H))
     n_loc = len(w.meta["local_blocks"])
     f_loc = 4.0 * w.d * w.Nq * w.B * w.H * float(_block_len(w.meta["local_blocks"]).sum())
-    out["wan_dual_output"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_dual_fwd(
-        q, k, v, dip, dix, n_loc, kv_block=64, kv_seg=1560, q_block=w.Nq, q_seg=w.Nq,
-        scale=w.scale, out_dtype=torch.float32), reps), f, kvb,
-        local_gflop_shared=round(f_loc / 1e9, 2))
+    if want("wan_dual_output"):
+        out["wan_dual_output"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_dual_fwd(
+            q, k, v, dip, dix, n_loc, kv_block=64, kv_seg=1560, q_block=w.Nq, q_seg=w.Nq,
+            scale=w.scale, out_dtype=torch.float32), reps), f, kvb,
+            local_gflop_shared=round(f_loc / 1e9, 2))
     # block-sparse path at the three top-K ratios (selection included)
     km = ca.block_mean(k, 64, 1560)
     nqb = ca.num_blocks(w.Nq, 64, 1560)
     qlen = np.tile(_block_len(np.arange(nqb)), w.B * w.H)
     for ratio in (0.25, 0.125, 0.0625):
         lay = wl.sparse_layout(w, ratio)
+        if not want(f"sparse_K{lay['K']}"):
+            continue
         fn = lambda: ca.block_sparse_fwd(
             q, k, v, sink_begin=0, sink_count=lay["sink_count"], hist_begin=lay["hist_begin"],
             hist_count=lay["hist_count"], C=lay["C"], local_begin=lay["local_begin"],
@@ -296,10 +307,11 @@ def per_config(reps=10, wan=None):
     _, cm = ca.block_mean(q, 64, 1560, with_total=True)
     pers = ca.block_score_topk(cm, km, lay["C"], cand_begin=lay["hist_begin"],
                                cand_count=lay["hist_count"])[:, :, 0, :].contiguous()
-    ms = _time_ms(torch, lambda: ca.persistent_update(cm, km, pers, lay["local_begin"],
-                                                      lay["local_count"], lay["C"]), reps)
-    out["persistent_update"] = {"us": round(ms * 1e3, 1), "candidates_per_head":
-                                lay["C"] + lay["local_count"], "C": lay["C"], "heads": w.H}
+    if want("persistent_update"):
+        ms = _time_ms(torch, lambda: ca.persistent_update(cm, km, pers, lay["local_begin"],
+                                                          lay["local_count"], lay["C"]), reps)
+        out["persistent_update"] = {"us": round(ms * 1e3, 1), "candidates_per_head":
+                                    lay["C"] + lay["local_count"], "C": lay["C"], "heads": w.H}
     del q, k, v, km
     # ragged per-head caches
     w = wl.ragged(seed=0)
@@ -307,32 +319,35 @@ def per_config(reps=10, wan=None):
     tot = int(w.cu_seqlens[-1])
     f = 4.0 * w.d * w.Nq * tot
     kvb = 2.0 * tot * w.d * 2
-    out["ragged"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_varlen_fwd(
-        q, kf, vf, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
-        sum_len=tot, lengths_frames=w.meta["n_frames"])
+    if want("ragged"):
+        out["ragged"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_varlen_fwd(
+            q, kf, vf, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
+            sum_len=tot, lengths_frames=w.meta["n_frames"])
     # packing those ragged caches from the dense per-head cache (HBM-bound:
     # every packed K/V row read once and written once)
     kd, vd = dev(w.k), dev(w.v)
     plan = ca.pack_plan([w.ragged_frames[bh] for bh in range(w.B * w.H)], kd.device)
-    ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, plan, 1560), reps)
-    moved = 2.0 * 2.0 * tot * w.d * 2
-    out["ragged_pack"] = {"us": round(ms * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
-                          "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
-                          "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if want("ragged_pack"):
+        ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, plan, 1560), reps)
+        moved = 2.0 * 2.0 * tot * w.d * 2
+        out["ragged_pack"] = {"us": round(ms * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
+                              "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del q, kf, vf, kd, vd
     # latent KV cache (d_c = 192, d_rope = 32): absorbed query, latent
     # attention, per-head up-projection
     m = wl.wan_mla(seed=0)
     mq, mwk, mwv = dev(m["q"]), dev(m["w_uk"]), dev(m["w_uv"])
     mkv = ca.cast_bf16_to_f16(dev(m["kv_lat"]))
-    ms_all = _time_ms(torch, lambda: ca.mla_chunk_attn(mq, mkv, mwk, mwv, scale=m["scale"]), reps)
-    rows = m["Nq"] * m["H"]
-    f_att = 2.0 * rows * m["Nkv"] * (224 + 192)
-    f_proj = 2.0 * rows * (96 * 192 + 192 * 128)
-    kvb = m["Nkv"] * 224 * 2.0
-    out["wan_mla"] = _rec(ms_all, f_att + f_proj, kvb, attention_gflop=round(f_att / 1e9, 1),
-                          projection_gflop=round(f_proj / 1e9, 1),
-                          kv_bytes_vs_dense=round(kvb / (2.0 * m["Nkv"] * m["H"] * 128 * 2), 4))
+    if want("wan_mla"):
+        ms_all = _time_ms(torch, lambda: ca.mla_chunk_attn(mq, mkv, mwk, mwv, scale=m["scale"]), reps)
+        rows = m["Nq"] * m["H"]
+        f_att = 2.0 * rows * m["Nkv"] * (224 + 192)
+        f_proj = 2.0 * rows * (96 * 192 + 192 * 128)
+        kvb = m["Nkv"] * 224 * 2.0
+        out["wan_mla"] = _rec(ms_all, f_att + f_proj, kvb, attention_gflop=round(f_att / 1e9, 1),
+                              projection_gflop=round(f_proj / 1e9, 1),
+                              kv_bytes_vs_dense=round(kvb / (2.0 * m["Nkv"] * m["H"] * 128 * 2), 4))
     del mq, mwk, mwv, mkv
     # mixed 40-head layer (dense / block lists / ragged per head)
     w = wl.mixed(seed=0)
@@ -371,11 +386,12 @@ def per_config(reps=10, wan=None):
     ix = i32(np.concatenate(lists))
     ip = i32(ip)
     kf, vf, cu = dev(w.k_flat), dev(w.v_flat), i32(w.cu_seqlens)
-    out["mixed_40h"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_mixed_fwd(
-        q, w.head_mode, k=k, v=v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
-        q_block=64, q_seg=1560, k_flat=kf, v_flat=vf, cu_seqlens=cu,
-        cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
-        heads_dense_sparse_ragged=[int((w.head_mode == m).sum()) for m in range(3)])
+    if want("mixed_40h"):
+        out["mixed_40h"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_mixed_fwd(
+            q, w.head_mode, k=k, v=v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
+            q_block=64, q_seg=1560, k_flat=kf, v_flat=vf, cu_seqlens=cu,
+            cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
+            heads_dense_sparse_ragged=[int((w.head_mode == m).sum()) for m in range(3)])
     return out
 
 
@@ -388,6 +404,8 @@ def main():
     ap.add_argument("--only", choices=["step", "dense", "copy", "configs"], default="step",
                     help="'dense' times the dense kernel alone (for counter runs); 'copy' "
                          "runs a plain 1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--config", default="",
+                    help="with --only configs: comma-separated entries to time (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "plain", "balanced"], default="auto",
                     help="dense launch: the library's own choice (default), one workgroup per "
@@ -433,7 +451,8 @@ def main():
                           "ms": ms, "GBps_read+write": 2 * n_bytes / (ms * 1e-3) / 1e9}))
         return
     if args.only == "configs":
-        print(json.dumps(per_config()), flush=True)
+        names = set(args.config.split(",")) if args.config else None
+        print(json.dumps(per_config(names=names)), flush=True)
         return
     t0 = time.perf_counter()
     w = wl.wan_dense(seed=0)
