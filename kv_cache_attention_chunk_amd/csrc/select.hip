@@ -18,7 +18,12 @@ constexpr int kMeanThreads = 256;
 __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
     const uint16_t* __restrict__ x, int N, int H, int d, int64_t sb, int64_t sn, int64_t sh,
     int block, int seg, int bps, int nb, float* __restrict__ out) {
-  __shared__ float red[kMeanThreads * 8];
+  // Partial sums, 8 floats per thread, as two 16-byte halves.  Threads with
+  // bit 2 set store their halves swapped, so the 16-byte stores of 8
+  // consecutive threads land in 8 different bank groups; a column read of
+  // 64 consecutive elements still covers 64 consecutive words.
+  __shared__ __attribute__((aligned(16))) float red[kMeanThreads * 8];
+  auto red_at = [](int row, int e) { return row * 8 + (e ^ (((row >> 2) & 1) << 2)); };
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - (bh / H) * H;
@@ -41,14 +46,17 @@ __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[tid * 8 + e] = accv[e];
+  {
+    const int sw = ((tid >> 2) & 1) << 2;
+    *reinterpret_cast<f32x4_t*>(red + tid * 8 + sw) = f32x4_t{accv[0], accv[1], accv[2], accv[3]};
+    *reinterpret_cast<f32x4_t*>(red + tid * 8 + (4 ^ sw)) = f32x4_t{accv[4], accv[5], accv[6], accv[7]};
+  }
   __syncthreads();
   // thread j < d sums element j over the row groups (fixed order)
   for (int j = tid; j < d; j += kMeanThreads) {
     const int cc = j / 8, e = j - (j / 8) * 8;
     float s = 0.f;
-    for (int g = 0; g < rpp; ++g) s += red[(g * tpr + cc) * 8 + e];
+    for (int g = 0; g < rpp; ++g) s += red[red_at(g * tpr + cc, e)];
     out[((int64_t)bh * nb + blk) * d + j] = len > 0 ? s / (float)len : 0.f;
   }
 }
