@@ -14,6 +14,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) float f32x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // Key-set modes of the attention kernel.  MODE_RANGE: each head attends to a

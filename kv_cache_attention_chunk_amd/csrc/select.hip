@@ -201,6 +201,61 @@ __device__ void kth_largest(const float* ss, int n, int K, int* hist, int* state
   need = k;
 }
 
+// Coarse scores ss[c] = <q, row(c)> for c in [0, n) (a NaN score as -inf),
+// and -inf in ss[n .. n_pad); n >= 1 whenever n_pad > 0.  For d/4 a power of two up to 64, d/4 lanes
+// share one candidate (a 16-byte slice each, then a butterfly sum) and the
+// loads of a batch of candidates are all issued before any is used;
+// otherwise each thread scores whole candidates sequentially.
+template <int THREADS, class Row>
+__device__ __forceinline__ void coarse_scores(const float* q, int d, int n, int n_pad, Row row,
+                                              float* ss) {
+  const int tid = threadIdx.x;
+  auto key = [](float x) { return x != x ? -INFINITY : x; };
+  const int lpc = d / 4;                       // lanes per candidate
+  if ((lpc & (lpc - 1)) == 0 && lpc <= 64) {
+    const int sub = tid & (lpc - 1);
+    const int slot = tid / lpc;
+    const int per_pass = THREADS / lpc;
+    const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(q + 4 * sub);
+    for (int c0 = 0; c0 < n_pad; c0 += kTopkBatch * per_pass) {
+      f32x4_t kv[kTopkBatch];
+      // rows past n load row n - 1 (no branch per load, so the batch's
+      // loads all go out together); their scores are replaced below
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int c = c0 + u * per_pass + slot;
+        kv[u] = *reinterpret_cast<const f32x4_t*>(row(c < n ? c : n - 1) + 4 * sub);
+      }
+      float part[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u)
+        part[u] = fmaf(qv[3], kv[u][3], fmaf(qv[2], kv[u][2], fmaf(qv[1], kv[u][1], qv[0] * kv[u][0])));
+      // butterfly over the lpc lanes of each candidate, the batch's exchanges
+      // issued together
+      for (int o = lpc >> 1; o > 0; o >>= 1) {
+#pragma unroll
+        for (int u = 0; u < kTopkBatch; ++u) part[u] += __shfl_xor(part[u], o);
+      }
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int c = c0 + u * per_pass + slot;
+        if (sub == 0 && c < n_pad) ss[c] = c < n ? key(part[u]) : -INFINITY;
+      }
+    }
+  } else {
+    for (int j = tid; j < n_pad; j += THREADS) {
+      float acc = -INFINITY;
+      if (j < n) {
+        const float* kr = row(j);
+        acc = 0.f;
+        for (int c = 0; c < d; ++c) acc = fmaf(q[c], kr[c], acc);
+        acc = key(acc);
+      }
+      ss[j] = acc;
+    }
+  }
+}
+
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int NQB, int NKB, int d,
@@ -218,49 +273,7 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
   const int tid = threadIdx.x;
   const float* q = qm + ((int64_t)bh * NQB + qb) * d;
   const float* kbase = km + ((int64_t)bh * NKB + cand_begin) * d;
-  auto key = [](float x) { return x != x ? -INFINITY : x; };
-  const int lpc = d / 4;                       // lanes per candidate
-  if ((lpc & (lpc - 1)) == 0 && lpc <= 64) {
-    const int sub = tid & (lpc - 1);
-    const int slot = tid / lpc;
-    const int per_pass = THREADS / lpc;
-    const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(q + 4 * sub);
-    for (int c0 = 0; c0 < 4 * n4; c0 += kTopkBatch * per_pass) {
-      f32x4_t kv[kTopkBatch];
-#pragma unroll
-      for (int u = 0; u < kTopkBatch; ++u) {
-        const int c = c0 + u * per_pass + slot;
-        kv[u] = c < n ? *reinterpret_cast<const f32x4_t*>(kbase + (int64_t)c * d + 4 * sub)
-                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      float part[kTopkBatch];
-#pragma unroll
-      for (int u = 0; u < kTopkBatch; ++u)
-        part[u] = fmaf(qv[3], kv[u][3], fmaf(qv[2], kv[u][2], fmaf(qv[1], kv[u][1], qv[0] * kv[u][0])));
-      // butterfly over the lpc lanes of each candidate, the batch's exchanges
-      // issued together
-      for (int o = lpc >> 1; o > 0; o >>= 1) {
-#pragma unroll
-        for (int u = 0; u < kTopkBatch; ++u) part[u] += __shfl_xor(part[u], o);
-      }
-#pragma unroll
-      for (int u = 0; u < kTopkBatch; ++u) {
-        const int c = c0 + u * per_pass + slot;
-        if (sub == 0 && c < 4 * n4) ss[c] = c < n ? key(part[u]) : -INFINITY;
-      }
-    }
-  } else {
-    for (int j = tid; j < 4 * n4; j += THREADS) {
-      float acc = -INFINITY;
-      if (j < n) {
-        const float* kr = kbase + (int64_t)j * d;
-        acc = 0.f;
-        for (int c = 0; c < d; ++c) acc = fmaf(q[c], kr[c], acc);
-        acc = key(acc);
-      }
-      ss[j] = acc;
-    }
-  }
+  coarse_scores<THREADS>(q, d, n, 4 * n4, [&](int c) { return kbase + (int64_t)c * d; }, ss);
   __syncthreads();
 
   // selection: the threshold score T and how many T-valued candidates to
@@ -581,9 +594,14 @@ __global__ __launch_bounds__(kIndexThreads) void build_index_kernel(
 //   * candidates in LDS: the evicted range, then the persistent ids that lie
 //     in [0, NKB) and outside the evicted range (a set union; persistent ids
 //     are distinct by contract);
-//   * float32 scores (a NaN score ranks as -inf);
+//   * float32 scores, d/4 lanes per candidate as in the top-K kernel (a NaN
+//     score ranks as -inf);
 //   * rank(i) = #{j : s_j > s_i} + #{j : s_j = s_i, id_j < id_i}, i.e. the
-//     position in (score descending, block id ascending) order;
+//     position in (score descending, block id ascending) order, counted
+//     directly up to kRankMaxCand candidates; above that, the radix select
+//     gives the C-th largest score T and the candidates are those above T
+//     plus the T-valued ones of lowest id (ties are counted among those
+//     only);
 //   * the rank < C candidates are written at their position in ascending id
 //     order; slots past the candidate count get id -1 and score -inf.
 // The persistent row is read into LDS before anything is written, so the
@@ -595,10 +613,14 @@ __global__ __launch_bounds__(kUpdThreads) void persistent_update_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int NKB, int d,
     const int32_t* pers, int C_in, int eb, int ne, int C, int32_t* out,
     float* __restrict__ out_score) {
-  __shared__ int ids[kTopkMaxCand];
-  __shared__ float sc[kTopkMaxCand];
-  __shared__ int rk[kTopkMaxCand];
+  // candidates padded to a multiple of 4 (score -inf, id INT_MAX, not kept),
+  // so that the comparison loops read 4 at a time
+  __shared__ __attribute__((aligned(16))) int ids[kTopkMaxCand];
+  __shared__ __attribute__((aligned(16))) float sc[kTopkMaxCand];
+  __shared__ __attribute__((aligned(16))) int rk[kTopkMaxCand];
   __shared__ int wcount[kUpdThreads / 64];
+  __shared__ int hist[256];
+  __shared__ int rstate[2];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < ne; i += kUpdThreads) ids[i] = eb + i;
@@ -620,36 +642,70 @@ __global__ __launch_bounds__(kUpdThreads) void persistent_update_kernel(
     n += tot;
     __syncthreads();
   }
+  const int n4 = (n + 3) >> 2;
+  for (int i = n + tid; i < 4 * n4; i += kUpdThreads) {
+    ids[i] = 0x7FFFFFFF;
+    rk[i] = C;
+  }
   // scores
   const float* q = qm + (int64_t)bh * d;
   const float* kb = km + (int64_t)bh * NKB * d;
-  for (int i = tid; i < n; i += kUpdThreads) {
-    const float* kr = kb + (int64_t)ids[i] * d;
-    float acc = 0.f;
-    for (int c = 0; c < d; c += 4) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + c);
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(kr + c);
-      acc = fmaf(a[3], x[3], fmaf(a[2], x[2], fmaf(a[1], x[1], fmaf(a[0], x[0], acc))));
-    }
-    sc[i] = acc != acc ? -INFINITY : acc;
-  }
+  coarse_scores<kUpdThreads>(q, d, n, 4 * n4, [&](int c) { return kb + (int64_t)ids[c] * d; }, sc);
   __syncthreads();
-  for (int i = tid; i < n; i += kUpdThreads) {
-    const float si = sc[i];
-    const int idi = ids[i];
-    int r = 0;
-    for (int j = 0; j < n; ++j) {
-      const float sj = sc[j];
-      r += (int)(sj > si) + (int)(sj == si && ids[j] < idi);
+  const f32x4_t* sc4 = reinterpret_cast<const f32x4_t*>(sc);
+  const i32x4_t* ids4 = reinterpret_cast<const i32x4_t*>(ids);
+  const i32x4_t* rk4 = reinterpret_cast<const i32x4_t*>(rk);
+  if (n > kRankMaxCand) {
+    // rk = 0 for a kept candidate, C otherwise
+    float thr;
+    int need;
+    kth_largest<kUpdThreads>(sc, n, C < n ? C : n, hist, rstate, thr, need);
+    for (int i = tid; i < n; i += kUpdThreads) {
+      const float si = sc[i];
+      int r = C;
+      if (si > thr) {
+        r = 0;
+      } else if (si == thr) {
+        const int idi = ids[i];
+        int t = 0;
+#pragma unroll 4
+        for (int j4 = 0; j4 < n4; ++j4) {
+          const f32x4_t s4 = sc4[j4];
+          const i32x4_t d4 = ids4[j4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t += (int)(s4[e] == thr) & (int)(d4[e] < idi);
+        }
+        r = t < need ? 0 : C;
+      }
+      rk[i] = r;
     }
-    rk[i] = r;
+  } else {
+    for (int i = tid; i < n; i += kUpdThreads) {
+      const float si = sc[i];
+      const int idi = ids[i];
+      int r = 0;
+#pragma unroll 4
+      for (int j4 = 0; j4 < n4; ++j4) {
+        const f32x4_t s4 = sc4[j4];
+        const i32x4_t d4 = ids4[j4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r += (int)(s4[e] > si) + ((int)(s4[e] == si) & (int)(d4[e] < idi));
+      }
+      rk[i] = r;
+    }
   }
   __syncthreads();
   for (int i = tid; i < n; i += kUpdThreads) {
     if (rk[i] >= C) continue;
     const int idi = ids[i];
     int pos = 0;
-    for (int j = 0; j < n; ++j) pos += (int)(rk[j] < C && ids[j] < idi);
+#pragma unroll 4
+    for (int j4 = 0; j4 < n4; ++j4) {
+      const i32x4_t r4 = rk4[j4];
+      const i32x4_t d4 = ids4[j4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pos += (int)(r4[e] < C) & (int)(d4[e] < idi);
+    }
     out[(int64_t)bh * C + pos] = idi;
     if (out_score) out_score[(int64_t)bh * C + pos] = sc[i];
   }

@@ -49,6 +49,31 @@ def test_persistent_update_random(d, C_in, C):
         np.testing.assert_allclose(sc.cpu().numpy(), ref["score"], rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("C_in,eb,ne,C", [(300, 1500, 1000, 200), (100, 2000, 100, 250),
+                                         (64, 0, 4000, 4096)])
+def test_persistent_update_large_planted_ties(C_in, eb, ne, C):
+    """More than 128 candidates (radix select) with many exact ties (small
+    integer scores), persistent ids below the evicted range so that id order
+    differs from candidate order; also C above the candidate count and the
+    4096-candidate limit.  Ids and scores exact."""
+    say(f"persistent update large C_in={C_in} evict={eb}+{ne} C={C}")
+    rng = np.random.default_rng(C_in + ne + C)
+    B, H, NB, d = 1, 3, 4096, 128
+    qm = np.zeros((B, H, 1, d), np.float32)
+    qm[..., 0] = 1.0
+    km = np.zeros((B, H, NB, d), np.float32)
+    km[..., 0] = rng.integers(-10, 11, size=(B, H, NB))
+    lo_ids = np.arange(0, eb) if eb > 0 else np.arange(eb + ne, NB)
+    pers = np.stack([np.sort(rng.choice(lo_ids, C_in, replace=False)) for _ in range(B * H)]
+                    ).reshape(B, H, C_in).astype(np.int32)
+    idx, sc = ca.persistent_update(torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda(),
+                                   i32(pers), eb, ne, C, return_scores=True)
+    torch.cuda.synchronize()
+    ref = orc.persistent_update(qm, km, pers, eb, ne, C)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(sc.cpu().numpy(), ref["score"])
+
+
 def test_persistent_update_in_place_and_padding():
     say("persistent update in place + padding")
     rng = np.random.default_rng(5)
