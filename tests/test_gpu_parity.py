@@ -516,6 +516,43 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
     assert_lse(l[:, :, rows], Lr, "wan sparse")
 
 
+@pytest.mark.parametrize("lay", [
+    # sink above the history range: the shared list is merged by a separate launch
+    dict(sink_begin=8, sink_count=4, hist_begin=0, hist_count=8, C=3, local_begin=12,
+         local_count=4, K=2),
+    # no persistent blocks
+    dict(sink_begin=0, sink_count=2, hist_begin=2, hist_count=10, C=0, local_begin=12,
+         local_count=4, K=2),
+    # no top-K blocks: the local pass resumes over empty lists
+    dict(sink_begin=0, sink_count=1, hist_begin=1, hist_count=11, C=4, local_begin=12,
+         local_count=4, K=0),
+])
+def test_block_sparse_layouts(lay):
+    """Layouts off the fused path (the block lists assembled by a separate
+    launch, or absent): selection and attention against the oracle."""
+    say(f"block-sparse layout {lay}")
+    w = wl.tiny_dense(seed=5)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    o, l, info = ca.block_sparse_fwd(q, k, v, block=64, seg=256, scale=w.scale, **lay)
+    torch.cuda.synchronize()
+    nqb = w.Nq // 64
+    sel = orc.sparse_selection(w.q.f32, w.k.f32, 64, 256, 64, 256,
+                               dict(lay, C=max(lay["C"], 1), K=max(lay["K"], 1)))
+    if lay["C"]:
+        assert compare_topk(info["persistent"], sel["persistent"]) == 0
+    if lay["K"]:
+        assert compare_topk(info["local"] + info["local_base"], sel["local"]) == 0
+    ip, ix = _union_csr(info, w.B * w.H, nqb)
+    pers = sel["persistent"]["idx"][:, :, 0, :] if lay["C"] else np.zeros((w.B, w.H, 0), np.int32)
+    loc = sel["local"]["idx"] if lay["K"] else np.zeros((w.B, w.H, nqb, 0), np.int32)
+    ipr, ixr = orc.build_kv_index(w.B, w.H, nqb, lay["sink_begin"], lay["sink_count"], pers, loc, 0)
+    for r in range(len(ip) - 1):
+        np.testing.assert_array_equal(np.sort(ix[ip[r]:ip[r + 1]]), ixr[ipr[r]:ipr[r + 1]])
+    Or, Lr = orc.chunk_attn_blocks(w.q.f32, w.k.f32, w.v.f32, ip, ix, 64, 256, 64, 256, w.scale)
+    assert_o(o, Or, True, "layout sparse")
+    assert_lse(l, Lr, "layout sparse")
+
+
 def test_wan_block_sparse_resident_key_means(wan, wan_dev):
     """With the history key-block means passed in as resident state, only the
     local window's means are recomputed (over that window alone); the
