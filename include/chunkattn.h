@@ -277,6 +277,18 @@ int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_st
                   int block_size, int seg_len, float* out, float* out_total, void* stream);
 
 /*
+ * ca_block_mean of two bf16 tensors of the same shape [B, N, H, d] and block
+ * tiling in one launch (Sparse Forcing page, section 2 item 2: the query
+ * blocks and the local-window key blocks are compressed for the same
+ * scoring step): out1 (and optionally out1_total) from x1, out2 from x2, each
+ * exactly as ca_block_mean would write them.  Strides are per tensor (host);
+ * limits and errors as ca_block_mean.
+ */
+int ca_block_mean_pair(const void* x1, const int64_t* x1_strides, float* out1, float* out1_total,
+                       const void* x2, const int64_t* x2_strides, float* out2,
+                       int B, int N, int H, int d, int block_size, int seg_len, void* stream);
+
+/*
  * Coarse block scores and top-K (Sparse Forcing page, section 2 items 1-2:
  * scoring on block representatives, top-C persistent blocks, top-K local
  * blocks).  score(qb, c) = <q_mean[b,h,qb,:], k_mean[b,h,c,:]> in float32 for

@@ -46,6 +46,7 @@ SIGNATURES = {
     "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
                           _i64p, _i64p, _i64p, _p]),
     "ca_block_mean": (_i, [_p, _i, _i, _i, _i, _i64p, _i, _i, _p, _p, _p]),
+    "ca_block_mean_pair": (_i, [_p, _i64p, _p, _p, _p, _i64p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "ca_block_score_topk_lists": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                        _p, _p, _p, _p]),

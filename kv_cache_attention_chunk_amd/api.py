@@ -337,6 +337,26 @@ def block_mean(x: torch.Tensor, block_size: int = 64, seg_len: Optional[int] = N
     return (out, tot) if with_total else out
 
 
+def block_mean_pair(x1: torch.Tensor, x2: torch.Tensor, block_size: int = 64,
+                    seg_len: Optional[int] = None, with_total: bool = False):
+    """block_mean of two tensors of the same shape and tiling in one launch;
+    returns (means of x1, means of x2), plus x1's mean over all tokens with
+    with_total."""
+    _bshd("x1", x1), _bshd("x2", x2)
+    if x1.shape != x2.shape:
+        raise ValueError("x1 and x2 must have the same shape")
+    B, N, H, d = x1.shape
+    seg = seg_len or max(N, 1)
+    nb = num_blocks(N, block_size, seg)
+    o1 = torch.empty((B, H, nb, d), dtype=torch.float32, device=x1.device)
+    o2 = torch.empty((B, H, nb, d), dtype=torch.float32, device=x1.device)
+    tot = torch.empty((B, H, 1, d), dtype=torch.float32, device=x1.device) if with_total else None
+    st = lib().ca_block_mean_pair(x1.data_ptr(), _st(x1), o1.data_ptr(), _ptr(tot), x2.data_ptr(),
+                                  _st(x2), o2.data_ptr(), B, N, H, d, block_size, seg, _stream())
+    check(st)
+    return (o1, o2, tot) if with_total else (o1, o2)
+
+
 def block_score_topk(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *, cand_begin: int = 0,
                      cand_count: Optional[int] = None, return_scores: bool = False):
     """Top-K candidate blocks per query block by representative dot product;
@@ -545,9 +565,8 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
     ranges = sorted([(sink_begin, sink_count), (hist_begin, hist_count), (local_begin, local_count)])
     if any(a[0] + a[1] > b[0] for a, b in zip(ranges, ranges[1:])):
         raise ValueError("sink, history and local block ranges must be disjoint")
-    qm, cm = block_mean(q, block, seg, with_total=True)
     bps = -(-kv_seg // block)
-    km_loc, loc_base = None, local_begin
+    km_loc, loc_base, qm = None, local_begin, None
     if k_mean is None:
         km = block_mean(k, block, kv_seg)
         km_loc = km
@@ -557,10 +576,17 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
             last = local_begin + local_count - 1
             t0 = (local_begin // bps) * kv_seg
             t1 = min(Nkv, (last // bps) * kv_seg + min(kv_seg, (last % bps + 1) * block))
-            km_loc = block_mean(k[:, t0:t1], block, kv_seg)
+            kw = k[:, t0:t1]
+            if kw.shape == q.shape:
+                # the window holds as many tokens as the chunk: one launch
+                qm, km_loc, cm = block_mean_pair(q, kw, block, seg, with_total=True)
+            else:
+                km_loc = block_mean(kw, block, kv_seg)
             loc_base = 0
         elif K:
             km_loc = block_mean(k, block, kv_seg)
+    if qm is None:
+        qm, cm = block_mean(q, block, seg, with_total=True)
     # Selection and block lists in one launch each when a list is a prefix
     # range followed by the selected ids; otherwise a separate merge.
     nqb = qm.shape[2]

@@ -540,6 +540,26 @@ int ca_block_mean(const void* x, int B, int N, int H, int d, const int64_t* x_st
                   "block_mean launch");
 }
 
+int ca_block_mean_pair(const void* x1, const int64_t* x1_strides, float* out1, float* out1_total,
+                       const void* x2, const int64_t* x2_strides, float* out2, int B, int N,
+                       int H, int d, int block_size, int seg_len, void* stream) {
+  if (B < 0 || N < 0 || H < 0) return fail(CA_EINVAL, "negative size");
+  if (d <= 0 || d % 8 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 8, <= 512)", d);
+  if (block_size < 1 || seg_len < 1) return fail(CA_EINVAL, "block_size and seg_len must be >= 1");
+  if (!x1 || !out1 || !x2 || !out2) return fail(CA_EINVAL, "NULL pointer");
+  if (!aligned16(x1) || !aligned16(x2)) return fail(CA_EINVAL, "x1 and x2 must be 16-byte aligned");
+  if (int r = check_strides("x1", x1_strides, 8)) return r;
+  if (int r = check_strides("x2", x2_strides, 8)) return r;
+  if ((int64_t)B * H > 65535) return fail(CA_ERANGE, "B*H above 65535");
+  const int nb = num_blocks(N, block_size, seg_len);
+  if (int r = check_device()) return r;
+  return launched(launch_block_mean(static_cast<const uint16_t*>(x1), B, N, H, d, x1_strides,
+                                    block_size, seg_len, (seg_len + block_size - 1) / block_size,
+                                    nb, out1, out1_total, static_cast<hipStream_t>(stream),
+                                    static_cast<const uint16_t*>(x2), x2_strides, out2),
+                  "block_mean_pair launch");
+}
+
 int ca_block_score_topk(const float* q_mean, const float* k_mean, int B, int H, int NQB, int NKB,
                         int d, int cand_begin, int cand_count, int K, int32_t* out_idx,
                         float* out_score, void* stream) {

@@ -104,9 +104,14 @@ hipError_t launch_split_merge(int d, bool out_f32, const AttnParams& p, hipStrea
 // Workgroups of the range-mode attention kernel resident on the whole device
 // at once (0 on failure).
 int attention_slots(int d);
+// With x2 non-null, the block means of a second tensor of the same shape
+// and tiling (strides xs2) go to out2 in the same launch; out_total is the
+// first tensor's.
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
                              const int64_t* xs, int block, int seg, int bps, int nb,
-                             float* out, float* out_total, hipStream_t stream);
+                             float* out, float* out_total, hipStream_t stream,
+                             const uint16_t* x2 = nullptr, const int64_t* xs2 = nullptr,
+                             float* out2 = nullptr);
 // With indptr non-null the kernel also writes each row's block list: the
 // prefix range [prefix_begin, prefix_begin + prefix_count) followed by
 // id_offset + the selected ids (W = prefix_count + K entries per row).

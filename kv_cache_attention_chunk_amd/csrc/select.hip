@@ -15,9 +15,25 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kMeanThreads = 256;
 
+// One or two tensors of the same shape and tiling (blockIdx.z picks one):
+// the query and the key block means of the block-sparse path in one launch.
+struct MeanSrc {
+  const uint16_t* x;
+  int64_t sb, sn, sh;
+  float* out;
+};
+struct MeanSrcs {
+  MeanSrc s[2];
+};
+
 __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
-    const uint16_t* __restrict__ x, int N, int H, int d, int64_t sb, int64_t sn, int64_t sh,
-    int block, int seg, int bps, int nb, float* __restrict__ out) {
+    const MeanSrcs srcs, int N, int H, int d, int block, int seg, int bps, int nb) {
+  const bool second = blockIdx.z != 0;
+  const uint16_t* __restrict__ x = second ? srcs.s[1].x : srcs.s[0].x;
+  const int64_t sb = second ? srcs.s[1].sb : srcs.s[0].sb;
+  const int64_t sn = second ? srcs.s[1].sn : srcs.s[0].sn;
+  const int64_t sh = second ? srcs.s[1].sh : srcs.s[0].sh;
+  float* __restrict__ out = second ? srcs.s[1].out : srcs.s[0].out;
   // Partial sums, 8 floats per thread, as two 16-byte halves.  Threads with
   // bit 2 set store their halves swapped, so the 16-byte stores of 8
   // consecutive threads land in 8 different bank groups; a column read of
@@ -719,11 +735,15 @@ __global__ __launch_bounds__(kUpdThreads) void persistent_update_kernel(
 
 hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d, const int64_t* xs,
                              int block, int seg, int bps, int nb, float* out, float* out_total,
-                             hipStream_t stream) {
+                             hipStream_t stream, const uint16_t* x2, const int64_t* xs2,
+                             float* out2) {
   if (B * H == 0) return hipSuccess;
+  MeanSrcs srcs{};
+  srcs.s[0] = MeanSrc{x, xs[0], xs[1], xs[2], out};
+  if (x2) srcs.s[1] = MeanSrc{x2, xs2[0], xs2[1], xs2[2], out2};
   if (nb > 0)
-    hipLaunchKernelGGL(block_mean_kernel, dim3(nb, B * H), dim3(kMeanThreads), 0, stream, x, N,
-                       H, d, xs[0], xs[1], xs[2], block, seg, bps, nb, out);
+    hipLaunchKernelGGL(block_mean_kernel, dim3(nb, B * H, x2 ? 2 : 1), dim3(kMeanThreads), 0,
+                       stream, srcs, N, H, d, block, seg, bps, nb);
   if (out_total)
     hipLaunchKernelGGL(total_mean_kernel, dim3(B * H), dim3(kMeanThreads), 0, stream, out, N,
                        block, seg, bps, nb, d, out_total);

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -132,6 +132,13 @@ def test_merge_mean_topk_index_checks(L):
     assert m(o=FAKE, odt=0) == CA_EINVAL                      # aliases o1 with another dtype
     assert L.ca_block_mean(FAKE, 1, 100, 2, 12, s, 64, 100, FAKE, None, None) == CA_EUNSUPPORTED
     assert L.ca_block_mean(FAKE, 1, 100, 2, 64, s, 0, 100, FAKE, None, None) == CA_EINVAL
+    bp = lambda **kw: L.ca_block_mean_pair(FAKE, s, FAKE + 4096, None, kw.get("x2", FAKE + 8192), s,
+                                           kw.get("o2", FAKE + 16384), 1, 100, 2, kw.get("d", 64),
+                                           64, 100, None)
+    assert bp(d=12) == CA_EUNSUPPORTED
+    assert bp(x2=None) == CA_EINVAL
+    assert bp(o2=None) == CA_EINVAL
+    assert bp(x2=FAKE + 8) == CA_EINVAL                 # misaligned
     t = lambda **kw: L.ca_block_score_topk(FAKE, FAKE, 1, 2, 75, 525, 128, kw.get("cb", 450),
                                            kw.get("cc", 75), kw.get("K", 10), FAKE, None, None)
     assert t(K=0) == CA_ERANGE

@@ -362,6 +362,25 @@ def test_topk_lists_match_separate_index_build(cb, cc, K, pb, pc, off):
     np.testing.assert_array_equal(ix.cpu().numpy(), ixr)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_mean_pair_equals_two_calls(d):
+    """Two tensors in one launch (the second a window of a longer cache, so
+    with its own strides): each output bit for bit as its own ca_block_mean
+    call, and against the oracle."""
+    say(f"block_mean pair d={d}")
+    X = _gen(61, 1, 1560 * 2 + 100, 3, d, 2.0)
+    Y = _gen(62, 1, 1560 * 5, 3, d, 1.0)
+    x, y = to_dev(X), to_dev(Y)
+    yw = y[:, 1560 * 2:1560 * 2 + x.shape[1]]
+    m1, m2, tot = ca.block_mean_pair(x, yw, 64, 1560, with_total=True)
+    r1, rt = ca.block_mean(x, 64, 1560, with_total=True)
+    r2 = ca.block_mean(yw, 64, 1560)
+    torch.cuda.synchronize()
+    assert torch.equal(m1, r1) and torch.equal(m2, r2) and torch.equal(tot, rt)
+    np.testing.assert_allclose(m2.cpu().numpy(), orc.block_mean(Y.f32[:, 1560 * 2:1560 * 2 + X.f32.shape[1]],
+                                                                64, 1560), rtol=0, atol=2e-6)
+
+
 @pytest.mark.parametrize("d", [24, 64, 128, 512])
 def test_block_mean_with_chunk_mean(d):
     """Block means and the mean over all tokens (the chunk-mean query), for
