@@ -78,30 +78,43 @@ __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
 }
 
 // Mean over all N tokens of each (b, h) from its block means: sum over blocks
-// of len_j * mean_j divided by N.  One workgroup per (b, h).  With G =
-// 256 / d thread groups (at least 1), group g sums blocks g, g + G, ... in
-// float32 (independent loads, so many are in flight), then the G partial
-// sums of each column are added in group order.
-__global__ __launch_bounds__(kMeanThreads) void total_mean_kernel(
+// of len_j * mean_j divided by N.  One workgroup of 1024 threads per (b, h).
+// With G = 1024 / d thread groups, group g sums blocks g, g + G, ... in
+// float32 (independent loads, so many are in flight; the block's frame and
+// position are stepped along instead of divided out per block), then the G
+// partial sums of each column are added in group order.
+constexpr int kTotThreads = 1024;
+
+__global__ __launch_bounds__(kTotThreads) void total_mean_kernel(
     const float* __restrict__ means, int N, int block, int seg, int bps, int nb, int d,
     float* __restrict__ out) {
-  __shared__ float red[512];
+  __shared__ float red[kTotThreads];
   const int bh = blockIdx.x;
-  const int G = d <= kMeanThreads ? kMeanThreads / d : 1;
+  const int G = kTotThreads / d;
   const float* m = means + (int64_t)bh * nb * d;
-  for (int slot = threadIdx.x; slot < G * d; slot += kMeanThreads) {
+  const int slot = threadIdx.x;
+  if (slot < G * d) {
     const int g = slot / d, j = slot - (slot / d) * d;
+    int fs = g / bps, fj = g - (g / bps) * bps;       // frame and position of block g
     float s = 0.f;
-#pragma unroll 8
+#pragma unroll 4
     for (int blk = g; blk < nb; blk += G) {
-      int start, len;
-      block_span(blk, N, block, seg, bps, start, len);
+      int seg_len = N - fs * seg;
+      seg_len = seg_len < seg ? seg_len : seg;
+      int len = seg_len - fj * block;
+      len = len < block ? len : block;
+      len = len < 0 ? 0 : len;
       s = fmaf((float)len, m[(int64_t)blk * d + j], s);
+      fj += G;
+      while (fj >= bps) {
+        fj -= bps;
+        ++fs;
+      }
     }
     red[slot] = s;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < d; j += kMeanThreads) {
+  for (int j = threadIdx.x; j < d; j += kTotThreads) {
     float t = 0.f;
     for (int g = 0; g < G; ++g) t += red[g * d + j];
     out[(int64_t)bh * d + j] = N > 0 ? t / (float)N : 0.f;
@@ -745,7 +758,7 @@ hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d, cons
     hipLaunchKernelGGL(block_mean_kernel, dim3(nb, B * H, x2 ? 2 : 1), dim3(kMeanThreads), 0,
                        stream, srcs, N, H, d, block, seg, bps, nb);
   if (out_total)
-    hipLaunchKernelGGL(total_mean_kernel, dim3(B * H), dim3(kMeanThreads), 0, stream, out, N,
+    hipLaunchKernelGGL(total_mean_kernel, dim3(B * H), dim3(kTotThreads), 0, stream, out, N,
                        block, seg, bps, nb, d, out_total);
   return hipGetLastError();
 }
