@@ -329,6 +329,32 @@ int ca_block_score_topk_lists(const float* q_mean, const float* k_mean,
                               void* stream);
 
 /*
+ * Several independent selections (each as ca_block_score_topk, or as
+ * ca_block_score_topk_lists when indptr is non-NULL) in one launch.  The
+ * persistent top-C against the chunk-mean query and the local top-K per
+ * query block (Sparse Forcing page, section 2 items 1-3) depend only on the
+ * block means, so the persistent selection's few workgroups can run beside
+ * the local selection's many.  Each job's outputs equal the separate call's.
+ *   jobs     host array of n_jobs descriptors, 1 <= n_jobs <= 4; each job has
+ *            the arguments and limits of the single call (out_score may be
+ *            NULL; indptr NULL = no block lists, else indices, prefix_begin,
+ *            prefix_count and id_offset as in ca_block_score_topk_lists)
+ */
+typedef struct ca_topk_job {
+  const float* q_mean;
+  const float* k_mean;
+  int B, H, NQB, NKB, d;
+  int cand_begin, cand_count, K;
+  int prefix_begin, prefix_count, id_offset;
+  int32_t* out_idx;
+  float* out_score;
+  int32_t* indptr;
+  int32_t* indices;
+} ca_topk_job;
+
+int ca_block_score_topk_batch(const ca_topk_job* jobs, int n_jobs, void* stream);
+
+/*
  * Persistent-memory update when the local window slides (Sparse Forcing
  * page, section 2 item 1, memory management: blocks evicted from the local
  * window are candidates, and the top C by coarse score are kept or updated as

@@ -7,7 +7,7 @@ scoring with top-K, and PBSA block-list assembly.  Importing this package does
 not load the library; the first call does, and fails if it is not built.
 """
 from .api import (  # noqa: F401
-    block_mean, block_mean_pair, block_score_topk, block_score_topk_lists, block_sparse_fwd, build_kv_index, cast_bf16_to_f16,
+    block_mean, block_mean_pair, block_score_topk, block_score_topk_batch, block_score_topk_lists, block_sparse_fwd, build_kv_index, cast_bf16_to_f16,
     chunk_attn_dual_fwd,
     chunk_attn_fwd,
     chunk_attn_mixed_fwd, chunk_attn_varlen_fwd, lse_merge, mla_chunk_attn, num_blocks, pack_plan,
@@ -18,7 +18,7 @@ from .api import (  # noqa: F401
 
 __all__ = [
     "chunk_attn_fwd", "chunk_attn_dual_fwd", "chunk_attn_varlen_fwd", "chunk_attn_mixed_fwd", "lse_merge",
-    "block_mean", "block_mean_pair", "block_score_topk", "block_score_topk_lists", "build_kv_index", "block_sparse_fwd", "num_blocks",
+    "block_mean", "block_mean_pair", "block_score_topk", "block_score_topk_batch", "block_score_topk_lists", "build_kv_index", "block_sparse_fwd", "num_blocks",
     "pack_plan", "pack_ragged", "persistent_update", "workspace_bytes", "mla_chunk_attn",
     "cast_bf16_to_f16",
 ]

@@ -50,6 +50,7 @@ SIGNATURES = {
     "ca_block_score_topk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "ca_block_score_topk_lists": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                        _p, _p, _p, _p]),
+    "ca_block_score_topk_batch": (_i, [_p, _i, _p]),
     "ca_persistent_update": (_i, [_p, _p, _i, _i, _i, _i, _i32p, _i, _i, _i, _i, _p, _p, _p]),
     "ca_pack_ragged": (_i, [_p, _p, _i, _i, _i, _i, _i64p, _i, _i32p, _i32p, _i, _i32p, _p, _p,
                             _i64, _p, _p]),
@@ -61,6 +62,18 @@ SIGNATURES = {
 }
 
 _LIB = None
+
+
+class TopkJob(ctypes.Structure):
+    """ctypes mirror of ca_topk_job (include/chunkattn.h)."""
+    _fields_ = [("q_mean", ctypes.c_void_p), ("k_mean", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("NQB", ctypes.c_int),
+                ("NKB", ctypes.c_int), ("d", ctypes.c_int),
+                ("cand_begin", ctypes.c_int), ("cand_count", ctypes.c_int), ("K", ctypes.c_int),
+                ("prefix_begin", ctypes.c_int), ("prefix_count", ctypes.c_int),
+                ("id_offset", ctypes.c_int),
+                ("out_idx", ctypes.c_void_p), ("out_score", ctypes.c_void_p),
+                ("indptr", ctypes.c_void_p), ("indices", ctypes.c_void_p)]
 
 
 def header_functions():

@@ -6,6 +6,7 @@ step of the computation runs in the HIP kernels of libchunkattn.so.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Tuple
 
@@ -405,6 +406,42 @@ def block_score_topk_lists(q_mean: torch.Tensor, k_mean: torch.Tensor, K: int, *
     return idx, indptr, indices
 
 
+def block_score_topk_batch(jobs):
+    """Up to four independent selections in one launch.  Each job is a dict
+    with q_mean, k_mean, K and optionally cand_begin, cand_count and, for
+    block lists, prefix_begin, prefix_count, id_offset and lists=True.
+    Returns one result per job: idx, or (idx, indptr, indices) with lists."""
+    from ._lib import TopkJob
+    if not 1 <= len(jobs) <= 4:
+        raise ValueError("1 to 4 jobs")
+    arr = (TopkJob * len(jobs))()
+    res, keep = [], []
+    for n, jb in enumerate(jobs):
+        qm, km, K = jb["q_mean"], jb["k_mean"], jb["K"]
+        for name, t in (("q_mean", qm), ("k_mean", km)):
+            if t.dtype != torch.float32 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 GPU tensor [B, H, N, d]")
+        B, H, NQB, d = qm.shape
+        NKB = km.shape[2]
+        if tuple(km.shape) != (B, H, NKB, d):
+            raise ValueError("k_mean shape mismatch")
+        cb = jb.get("cand_begin", 0)
+        cc = jb.get("cand_count", NKB - cb)
+        idx = torch.empty((B, H, NQB, K), dtype=torch.int32, device=qm.device)
+        ip = ix = None
+        pb, pc, off = jb.get("prefix_begin", 0), jb.get("prefix_count", 0), jb.get("id_offset", 0)
+        if jb.get("lists"):
+            rows = B * H * NQB
+            ip = torch.empty(rows + 1, dtype=torch.int32, device=qm.device)
+            ix = torch.empty(max(rows * (pc + K), 1), dtype=torch.int32, device=qm.device)
+        arr[n] = TopkJob(qm.data_ptr(), km.data_ptr(), B, H, NQB, NKB, d, cb, cc, K, pb, pc, off,
+                         idx.data_ptr(), None, _ptr(ip), _ptr(ix))
+        res.append((idx, ip, ix) if ip is not None else idx)
+        keep += [qm, km]
+    check(lib().ca_block_score_topk_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream()))
+    return res
+
+
 def persistent_update(q_mean: torch.Tensor, k_mean: torch.Tensor,
                       persistent: Optional[torch.Tensor], evict_begin: int, evict_count: int,
                       C: int, *, out: Optional[torch.Tensor] = None, return_scores: bool = False):
@@ -590,7 +627,15 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
     # Selection and block lists in one launch each when a list is a prefix
     # range followed by the selected ids; otherwise a separate merge.
     nqb = qm.shape[2]
-    if C and sink_begin + sink_count <= hist_begin:
+    loc = None
+    if C and K and sink_begin + sink_count <= hist_begin:
+        # both selections and their block lists in one launch
+        (pers, sh_ptr, sh_idx), (loc, lo_ptr, lo_idx) = block_score_topk_batch([
+            dict(q_mean=cm, k_mean=km, K=C, cand_begin=hist_begin, cand_count=hist_count,
+                 prefix_begin=sink_begin, prefix_count=sink_count, lists=True),
+            dict(q_mean=qm, k_mean=km_loc, K=K, cand_begin=loc_base, cand_count=local_count,
+                 id_offset=local_begin - loc_base, lists=True)])
+    elif C and sink_begin + sink_count <= hist_begin:
         pers, sh_ptr, sh_idx = block_score_topk_lists(cm, km, C, cand_begin=hist_begin,
                                                       cand_count=hist_count,
                                                       prefix_begin=sink_begin,
@@ -601,12 +646,11 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
         sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
                                         None if pers is None else pers[:, :, 0, :].contiguous(),
                                         None, 0, device=q.device)
-    if K:
+    if K and loc is None:
         loc, lo_ptr, lo_idx = block_score_topk_lists(qm, km_loc, K, cand_begin=loc_base,
                                                      cand_count=local_count,
                                                      id_offset=local_begin - loc_base)
-    else:
-        loc = None
+    elif not K:
         lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, None, 0, device=q.device)
     o1, l1 = chunk_attn_fwd(q, k, v, kv_indptr=sh_ptr, kv_indices=sh_idx, kv_block=block,
                             kv_seg=seg, q_block=Nq, q_seg=Nq, scale=scale,

@@ -602,6 +602,40 @@ int ca_block_score_topk_lists(const float* q_mean, const float* k_mean, int B, i
                   "block_score_topk_lists launch");
 }
 
+int ca_block_score_topk_batch(const ca_topk_job* jobs, int n_jobs, void* stream) {
+  if (n_jobs < 1 || n_jobs > 4) return fail(CA_ERANGE, "n_jobs %d outside 1..4", n_jobs);
+  if (!jobs) return fail(CA_EINVAL, "jobs is NULL");
+  TopkJobDesc desc[4];
+  int64_t wgs = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const ca_topk_job& a = jobs[i];
+    if (a.B < 0 || a.H < 0 || a.NQB < 0 || a.NKB < 0) return fail(CA_EINVAL, "job %d: negative size", i);
+    if (a.d <= 0 || a.d % 4 || a.d > 512) return fail(CA_EUNSUPPORTED, "job %d: head dim %d (multiple of 4, <= 512)", i, a.d);
+    if (!a.q_mean || !a.k_mean || !a.out_idx) return fail(CA_EINVAL, "job %d: NULL pointer", i);
+    if (!aligned16(a.q_mean) || !aligned16(a.k_mean)) return fail(CA_EINVAL, "job %d: means must be 16-byte aligned", i);
+    if (a.cand_count < 1 || a.cand_count > 4096) return fail(CA_ERANGE, "job %d: cand_count %d outside 1..4096", i, a.cand_count);
+    if (a.cand_begin < 0 || a.cand_begin + a.cand_count > a.NKB) return fail(CA_ERANGE, "job %d: candidate range outside [0, NKB)", i);
+    if (a.K < 1 || a.K > a.cand_count) return fail(CA_ERANGE, "job %d: K=%d outside 1..cand_count", i, a.K);
+    if (a.indptr) {
+      if (!a.indices) return fail(CA_EINVAL, "job %d: indices is NULL", i);
+      if (a.prefix_begin < 0 || a.prefix_count < 0) return fail(CA_EINVAL, "job %d: negative prefix", i);
+      if ((int64_t)a.id_offset + a.cand_begin < 0 || (int64_t)a.id_offset + a.cand_begin + a.cand_count > 0x7FFFFFFF)
+        return fail(CA_ERANGE, "job %d: id_offset out of range", i);
+      if ((int64_t)a.prefix_begin + a.prefix_count > (int64_t)a.id_offset + a.cand_begin)
+        return fail(CA_EINVAL, "job %d: prefix range must lie below every candidate id + id_offset", i);
+      if ((int64_t)a.B * a.H * a.NQB * (a.prefix_count + a.K) > 0x7FFFFFFF) return fail(CA_ERANGE, "job %d: too many entries", i);
+    }
+    wgs += (int64_t)a.B * a.H * a.NQB;
+    desc[i] = TopkJobDesc{a.q_mean, a.k_mean, a.B, a.H, a.NQB, a.NKB, a.d, a.cand_begin,
+                          a.cand_count, a.K, a.prefix_begin, a.prefix_count, a.id_offset,
+                          a.out_idx, a.out_score, a.indptr, a.indices};
+  }
+  if (wgs > 0x7FFFFFFF) return fail(CA_ERANGE, "too many selection rows");
+  if (int r = check_device()) return r;
+  return launched(launch_score_topk_batch(desc, n_jobs, static_cast<hipStream_t>(stream)),
+                  "block_score_topk_batch launch");
+}
+
 int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H, int NKB, int d,
                          const int32_t* persistent, int C_in, int evict_begin, int evict_count,
                          int C, int32_t* out, float* out_score, void* stream) {

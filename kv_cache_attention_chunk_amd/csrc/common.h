@@ -112,6 +112,19 @@ hipError_t launch_block_mean(const uint16_t* x, int B, int N, int H, int d,
                              float* out, float* out_total, hipStream_t stream,
                              const uint16_t* x2 = nullptr, const int64_t* xs2 = nullptr,
                              float* out2 = nullptr);
+// One selection of a batched launch (fields as launch_score_topk's).
+struct TopkJobDesc {
+  const float* qm;
+  const float* km;
+  int B, H, NQB, NKB, d, cand_begin, cand_count, K;
+  int prefix_begin, prefix_count, id_offset;
+  int32_t* out_idx;
+  float* out_score;
+  int32_t* indptr;
+  int32_t* indices;
+};
+// Up to 4 independent selections in one launch of 256-thread workgroups.
+hipError_t launch_score_topk_batch(const TopkJobDesc* jobs, int n_jobs, hipStream_t stream);
 // With indptr non-null the kernel also writes each row's block list: the
 // prefix range [prefix_begin, prefix_begin + prefix_count) followed by
 // id_offset + the selected ids (W = prefix_count + K entries per row).

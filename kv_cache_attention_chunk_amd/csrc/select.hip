@@ -153,6 +153,21 @@ struct TopkLists {
   int prefix_begin, prefix_count, id_offset, rows;
 };
 
+struct TopkJob {
+  const float* qm;
+  const float* km;
+  int NQB, NKB, d, cand_begin, n, K, wg_begin;
+  int32_t* out_idx;
+  float* out_score;
+  TopkLists lists;
+};
+constexpr int kTopkMaxJobs = 4;
+constexpr int kTopkBatchThreads = 256;
+struct TopkJobs {
+  TopkJob j[kTopkMaxJobs];
+  int n_jobs;
+};
+
 constexpr int kTopkMaxCand = 4096;
 constexpr int kTopkBatch = 16;
 constexpr int kRankMaxCand = 128;    // larger candidate sets use the radix select
@@ -285,20 +300,19 @@ __device__ __forceinline__ void coarse_scores(const float* q, int d, int n, int 
   }
 }
 
+// One selection row (b*H + h = bh, query block qb) on a whole workgroup;
+// topk_lds is the dynamic LDS (topk_lds_bytes(n, THREADS)), hist and rstate
+// static LDS.
 template <int THREADS>
-__global__ __launch_bounds__(THREADS) void score_topk_kernel(
-    const float* __restrict__ qm, const float* __restrict__ km, int NQB, int NKB, int d,
-    int cand_begin, int n, int K, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
-    const TopkLists lists) {
-  extern __shared__ __attribute__((aligned(16))) float topk_lds[];
+__device__ void topk_row(const float* __restrict__ qm, const float* __restrict__ km, int NQB,
+                         int NKB, int d, int cand_begin, int n, int K,
+                         int32_t* __restrict__ out_idx, float* __restrict__ out_score,
+                         const TopkLists& lists, int qb, int bh, float* topk_lds, int* hist,
+                         int* rstate) {
   const int n4 = (n + 3) >> 2;
   float* ss = topk_lds;                                          // [4 n4] scores
   int* rk = reinterpret_cast<int*>(ss + 4 * n4);                 // [n] ranks
   int* wcount = rk + n;                                          // [2 THREADS / 64]
-  __shared__ int hist[256];
-  __shared__ int rstate[2];
-  const int qb = blockIdx.x;
-  const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const float* q = qm + ((int64_t)bh * NQB + qb) * d;
   const float* kbase = km + ((int64_t)bh * NKB + cand_begin) * d;
@@ -401,6 +415,35 @@ __global__ __launch_bounds__(THREADS) void score_topk_kernel(
     carry_eq += etot;
     __syncthreads();
   }
+}
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void score_topk_kernel(
+    const float* __restrict__ qm, const float* __restrict__ km, int NQB, int NKB, int d,
+    int cand_begin, int n, int K, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
+    const TopkLists lists) {
+  extern __shared__ __attribute__((aligned(16))) float topk_lds[];
+  __shared__ int hist[256];
+  __shared__ int rstate[2];
+  topk_row<THREADS>(qm, km, NQB, NKB, d, cand_begin, n, K, out_idx, out_score, lists, blockIdx.x,
+                    blockIdx.y, topk_lds, hist, rstate);
+}
+
+// Several independent selections in one launch (the persistent top-C and
+// the local top-K of the block-sparse path run side by side): workgroups
+// [wg_begin_j, wg_begin_j + BH_j * NQB_j) serve job j.
+__global__ __launch_bounds__(kTopkBatchThreads) void score_topk_batch_kernel(const TopkJobs jobs) {
+  extern __shared__ __attribute__((aligned(16))) float topk_lds[];
+  __shared__ int hist[256];
+  __shared__ int rstate[2];
+  int j = 0;
+  while (j + 1 < jobs.n_jobs && (int)blockIdx.x >= jobs.j[j + 1].wg_begin) ++j;
+  const TopkJob& jb = jobs.j[j];
+  const int local = (int)blockIdx.x - jb.wg_begin;
+  const int bh = local / jb.NQB;
+  const int qb = local - bh * jb.NQB;
+  topk_row<kTopkBatchThreads>(jb.qm, jb.km, jb.NQB, jb.NKB, jb.d, jb.cand_begin, jb.n, jb.K,
+                              jb.out_idx, jb.out_score, jb.lists, qb, bh, topk_lds, hist, rstate);
 }
 
 // ---------------------------------------------------------------------------
@@ -779,6 +822,25 @@ hipError_t launch_score_topk(const float* qm, const float* km, int B, int H, int
     hipLaunchKernelGGL(score_topk_kernel<1024>, grid, dim3(1024), topk_lds_bytes(cand_count, 1024),
                        stream, qm, km, NQB, NKB, d, cand_begin, cand_count, K, out_idx, out_score,
                        lists);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk_batch(const TopkJobDesc* jobs, int n_jobs, hipStream_t stream) {
+  TopkJobs tj{};
+  int wgs = 0, n_max = 1;
+  for (int i = 0; i < n_jobs; ++i) {
+    const TopkJobDesc& a = jobs[i];
+    const int rows = a.B * a.H * a.NQB;
+    tj.j[i] = TopkJob{a.qm, a.km, a.NQB, a.NKB, a.d, a.cand_begin, a.cand_count, a.K, wgs,
+                      a.out_idx, a.out_score,
+                      TopkLists{a.indptr, a.indices, a.prefix_begin, a.prefix_count, a.id_offset, rows}};
+    wgs += rows;
+    n_max = a.cand_count > n_max ? a.cand_count : n_max;
+  }
+  tj.n_jobs = n_jobs;
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(score_topk_batch_kernel, dim3(wgs), dim3(kTopkBatchThreads),
+                     topk_lds_bytes(n_max, kTopkBatchThreads), stream, tj);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -139,6 +139,19 @@ def test_merge_mean_topk_index_checks(L):
     assert bp(x2=None) == CA_EINVAL
     assert bp(o2=None) == CA_EINVAL
     assert bp(x2=FAKE + 8) == CA_EINVAL                 # misaligned
+    job = lambda **kw: _lib.TopkJob(FAKE, FAKE, 1, 2, kw.get("nqb", 75), 525, 128, kw.get("cb", 450),
+                                    75, kw.get("K", 10), kw.get("pb", 0), kw.get("pc", 0),
+                                    kw.get("off", 0), FAKE, None, kw.get("ip", None),
+                                    kw.get("ix", None))
+    def batch(*jobs):
+        arr = (_lib.TopkJob * len(jobs))(*jobs)
+        return L.ca_block_score_topk_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), None)
+    assert L.ca_block_score_topk_batch(None, 1, None) == CA_EINVAL
+    assert batch(*[job()] * 5) == CA_ERANGE             # more than 4 jobs
+    assert batch(job(), job(K=0)) == CA_ERANGE          # second job checked too
+    assert batch(job(cb=451)) == CA_ERANGE
+    assert batch(job(ip=FAKE)) == CA_EINVAL             # lists without indices
+    assert batch(job(ip=FAKE, ix=FAKE, pc=451)) == CA_EINVAL   # prefix reaches the candidates
     t = lambda **kw: L.ca_block_score_topk(FAKE, FAKE, 1, 2, 75, 525, 128, kw.get("cb", 450),
                                            kw.get("cc", 75), kw.get("K", 10), FAKE, None, None)
     assert t(K=0) == CA_ERANGE

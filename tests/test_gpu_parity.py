@@ -362,6 +362,37 @@ def test_topk_lists_match_separate_index_build(cb, cc, K, pb, pc, off):
     np.testing.assert_array_equal(ix.cpu().numpy(), ixr)
 
 
+def test_topk_batch_equals_separate_calls():
+    """Selections of different shapes in one launch (the block-sparse path's
+    persistent and local pair, a plain top-K, a 4096-candidate radix case):
+    ids and block lists bit for bit as the separate calls, ids against the
+    oracle."""
+    say("topk batch")
+    rng = np.random.default_rng(3)
+    t = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32) / 8).cuda()
+    cm, km = t(1, 12, 1, 128), t(1, 12, 525, 128)
+    qm, kl = t(1, 12, 75, 128), t(1, 12, 75, 128)
+    q3, k3 = t(2, 3, 7, 64), t(2, 3, 300, 64)
+    q4, k4 = t(1, 2, 2, 128), t(1, 2, 4100, 128)
+    jobs = [dict(q_mean=cm, k_mean=km, K=32, cand_begin=25, cand_count=425, prefix_begin=0,
+                 prefix_count=25, lists=True),
+            dict(q_mean=qm, k_mean=kl, K=10, cand_begin=0, cand_count=75, id_offset=450, lists=True),
+            dict(q_mean=q3, k_mean=k3, K=17, cand_begin=20, cand_count=250),
+            dict(q_mean=q4, k_mean=k4, K=300, cand_begin=4, cand_count=4096)]
+    (p1, ip1, ix1), (p2, ip2, ix2), p3, p4 = ca.block_score_topk_batch(jobs)
+    s1 = ca.block_score_topk_lists(cm, km, 32, cand_begin=25, cand_count=425, prefix_begin=0, prefix_count=25)
+    s2 = ca.block_score_topk_lists(qm, kl, 10, cand_begin=0, cand_count=75, id_offset=450)
+    s3 = ca.block_score_topk(q3, k3, 17, cand_begin=20, cand_count=250)
+    s4 = ca.block_score_topk(q4, k4, 300, cand_begin=4, cand_count=4096)
+    torch.cuda.synchronize()
+    for a, b in [(p1, s1[0]), (ip1, s1[1]), (ix1, s1[2]), (p2, s2[0]), (ip2, s2[1]), (ix2, s2[2]),
+                 (p3, s3), (p4, s4)]:
+        assert torch.equal(a, b)
+    for idx, (qq, kk, cb, cc, K) in [(p1, (cm, km, 25, 425, 32)), (p3, (q3, k3, 20, 250, 17)),
+                                     (p4, (q4, k4, 4, 4096, 300))]:
+        compare_topk(idx, orc.block_score_topk(qq.cpu().numpy(), kk.cpu().numpy(), cb, cc, K))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_block_mean_pair_equals_two_calls(d):
     """Two tensors in one launch (the second a window of a longer cache, so
