@@ -123,7 +123,7 @@ struct TopkJobDesc {
   int32_t* indptr;
   int32_t* indices;
 };
-// Up to 4 independent selections in one launch of 256-thread workgroups.
+// Up to 4 independent selections in one launch of 512-thread workgroups.
 hipError_t launch_score_topk_batch(const TopkJobDesc* jobs, int n_jobs, hipStream_t stream);
 // With indptr non-null the kernel also writes each row's block list: the
 // prefix range [prefix_begin, prefix_begin + prefix_count) followed by

@@ -162,7 +162,7 @@ struct TopkJob {
   TopkLists lists;
 };
 constexpr int kTopkMaxJobs = 4;
-constexpr int kTopkBatchThreads = 256;
+constexpr int kTopkBatchThreads = 512;
 struct TopkJobs {
   TopkJob j[kTopkMaxJobs];
   int n_jobs;
