@@ -560,17 +560,40 @@ int ca_block_mean_pair(const void* x1, const int64_t* x1_strides, float* out1, f
                   "block_mean_pair launch");
 }
 
+// Argument checks shared by the selection calls (one job of the batched
+// call, or the single calls' arguments); `who` prefixes the message.
+static int check_topk_job(const ca_topk_job& a, const char* who) {
+  if (a.B < 0 || a.H < 0 || a.NQB < 0 || a.NKB < 0) return fail(CA_EINVAL, "%s: negative size", who);
+  if (a.d <= 0 || a.d % 4 || a.d > 512)
+    return fail(CA_EUNSUPPORTED, "%s: head dim %d (multiple of 4, <= 512)", who, a.d);
+  if (!a.q_mean || !a.k_mean || !a.out_idx) return fail(CA_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(a.q_mean) || !aligned16(a.k_mean))
+    return fail(CA_EINVAL, "%s: means must be 16-byte aligned", who);
+  if (a.cand_count < 1 || a.cand_count > 4096)
+    return fail(CA_ERANGE, "%s: cand_count %d outside 1..4096", who, a.cand_count);
+  if (a.cand_begin < 0 || a.cand_begin + a.cand_count > a.NKB)
+    return fail(CA_ERANGE, "%s: candidate range outside [0, NKB)", who);
+  if (a.K < 1 || a.K > a.cand_count) return fail(CA_ERANGE, "%s: K=%d outside 1..cand_count", who, a.K);
+  if (!a.indptr) return 0;
+  if (!a.indices) return fail(CA_EINVAL, "%s: indices is NULL", who);
+  if (a.prefix_begin < 0 || a.prefix_count < 0) return fail(CA_EINVAL, "%s: negative prefix", who);
+  if ((int64_t)a.id_offset + a.cand_begin < 0 ||
+      (int64_t)a.id_offset + a.cand_begin + a.cand_count > 0x7FFFFFFF)
+    return fail(CA_ERANGE, "%s: id_offset out of range", who);
+  if ((int64_t)a.prefix_begin + a.prefix_count > (int64_t)a.id_offset + a.cand_begin)
+    return fail(CA_EINVAL, "%s: prefix range must lie below every candidate id + id_offset", who);
+  if ((int64_t)a.B * a.H * a.NQB * (a.prefix_count + a.K) > 0x7FFFFFFF)
+    return fail(CA_ERANGE, "%s: too many entries", who);
+  return 0;
+}
+
 int ca_block_score_topk(const float* q_mean, const float* k_mean, int B, int H, int NQB, int NKB,
                         int d, int cand_begin, int cand_count, int K, int32_t* out_idx,
                         float* out_score, void* stream) {
-  if (B < 0 || H < 0 || NQB < 0 || NKB < 0) return fail(CA_EINVAL, "negative size");
-  if (d <= 0 || d % 4 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 4, <= 512)", d);
-  if (!q_mean || !k_mean || !out_idx) return fail(CA_EINVAL, "NULL pointer");
-  if (!aligned16(q_mean) || !aligned16(k_mean)) return fail(CA_EINVAL, "means must be 16-byte aligned");
-  if (cand_count < 1 || cand_count > 4096) return fail(CA_ERANGE, "cand_count %d outside 1..4096", cand_count);
-  if (cand_begin < 0 || cand_begin + cand_count > NKB) return fail(CA_ERANGE, "candidate range outside [0, NKB)");
-  if (K < 1 || K > cand_count) return fail(CA_ERANGE, "K=%d outside 1..cand_count", K);
-  if ((int64_t)B * H > 65535 || NQB > 0x7FFFFFFF) return fail(CA_ERANGE, "grid too large");
+  const ca_topk_job a{q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
+                      0, 0, 0, out_idx, out_score, nullptr, nullptr};
+  if (int r = check_topk_job(a, "block_score_topk")) return r;
+  if ((int64_t)B * H > 65535) return fail(CA_ERANGE, "grid too large");
   if (int r = check_device()) return r;
   return launched(launch_score_topk(q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
                                     out_idx, out_score, static_cast<hipStream_t>(stream)),
@@ -581,20 +604,11 @@ int ca_block_score_topk_lists(const float* q_mean, const float* k_mean, int B, i
                               int NKB, int d, int cand_begin, int cand_count, int K,
                               int prefix_begin, int prefix_count, int id_offset,
                               int32_t* out_idx, int32_t* indptr, int32_t* indices, void* stream) {
-  if (B < 0 || H < 0 || NQB < 0 || NKB < 0) return fail(CA_EINVAL, "negative size");
-  if (d <= 0 || d % 4 || d > 512) return fail(CA_EUNSUPPORTED, "head dim %d (multiple of 4, <= 512)", d);
-  if (!q_mean || !k_mean || !out_idx || !indptr || !indices) return fail(CA_EINVAL, "NULL pointer");
-  if (!aligned16(q_mean) || !aligned16(k_mean)) return fail(CA_EINVAL, "means must be 16-byte aligned");
-  if (cand_count < 1 || cand_count > 4096) return fail(CA_ERANGE, "cand_count %d outside 1..4096", cand_count);
-  if (cand_begin < 0 || cand_begin + cand_count > NKB) return fail(CA_ERANGE, "candidate range outside [0, NKB)");
-  if (K < 1 || K > cand_count) return fail(CA_ERANGE, "K=%d outside 1..cand_count", K);
-  if ((int64_t)B * H > 65535 || NQB > 0x7FFFFFFF) return fail(CA_ERANGE, "grid too large");
-  if (prefix_begin < 0 || prefix_count < 0) return fail(CA_EINVAL, "negative prefix");
-  if ((int64_t)id_offset + cand_begin < 0 || (int64_t)id_offset + cand_begin + cand_count > 0x7FFFFFFF)
-    return fail(CA_ERANGE, "id_offset out of range");
-  if ((int64_t)prefix_begin + prefix_count > (int64_t)id_offset + cand_begin)
-    return fail(CA_EINVAL, "prefix range must lie below every candidate id + id_offset");
-  if ((int64_t)B * H * NQB * (prefix_count + K) > 0x7FFFFFFF) return fail(CA_ERANGE, "too many entries");
+  if (!indptr) return fail(CA_EINVAL, "block_score_topk_lists: indptr is NULL");
+  const ca_topk_job a{q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
+                      prefix_begin, prefix_count, id_offset, out_idx, nullptr, indptr, indices};
+  if (int r = check_topk_job(a, "block_score_topk_lists")) return r;
+  if ((int64_t)B * H > 65535) return fail(CA_ERANGE, "grid too large");
   if (int r = check_device()) return r;
   return launched(launch_score_topk(q_mean, k_mean, B, H, NQB, NKB, d, cand_begin, cand_count, K,
                                     out_idx, nullptr, static_cast<hipStream_t>(stream), indptr,
@@ -609,22 +623,9 @@ int ca_block_score_topk_batch(const ca_topk_job* jobs, int n_jobs, void* stream)
   int64_t wgs = 0;
   for (int i = 0; i < n_jobs; ++i) {
     const ca_topk_job& a = jobs[i];
-    if (a.B < 0 || a.H < 0 || a.NQB < 0 || a.NKB < 0) return fail(CA_EINVAL, "job %d: negative size", i);
-    if (a.d <= 0 || a.d % 4 || a.d > 512) return fail(CA_EUNSUPPORTED, "job %d: head dim %d (multiple of 4, <= 512)", i, a.d);
-    if (!a.q_mean || !a.k_mean || !a.out_idx) return fail(CA_EINVAL, "job %d: NULL pointer", i);
-    if (!aligned16(a.q_mean) || !aligned16(a.k_mean)) return fail(CA_EINVAL, "job %d: means must be 16-byte aligned", i);
-    if (a.cand_count < 1 || a.cand_count > 4096) return fail(CA_ERANGE, "job %d: cand_count %d outside 1..4096", i, a.cand_count);
-    if (a.cand_begin < 0 || a.cand_begin + a.cand_count > a.NKB) return fail(CA_ERANGE, "job %d: candidate range outside [0, NKB)", i);
-    if (a.K < 1 || a.K > a.cand_count) return fail(CA_ERANGE, "job %d: K=%d outside 1..cand_count", i, a.K);
-    if (a.indptr) {
-      if (!a.indices) return fail(CA_EINVAL, "job %d: indices is NULL", i);
-      if (a.prefix_begin < 0 || a.prefix_count < 0) return fail(CA_EINVAL, "job %d: negative prefix", i);
-      if ((int64_t)a.id_offset + a.cand_begin < 0 || (int64_t)a.id_offset + a.cand_begin + a.cand_count > 0x7FFFFFFF)
-        return fail(CA_ERANGE, "job %d: id_offset out of range", i);
-      if ((int64_t)a.prefix_begin + a.prefix_count > (int64_t)a.id_offset + a.cand_begin)
-        return fail(CA_EINVAL, "job %d: prefix range must lie below every candidate id + id_offset", i);
-      if ((int64_t)a.B * a.H * a.NQB * (a.prefix_count + a.K) > 0x7FFFFFFF) return fail(CA_ERANGE, "job %d: too many entries", i);
-    }
+    char who[16];
+    snprintf(who, sizeof who, "job %d", i);
+    if (int r = check_topk_job(a, who)) return r;
     wgs += (int64_t)a.B * a.H * a.NQB;
     desc[i] = TopkJobDesc{a.q_mean, a.k_mean, a.B, a.H, a.NQB, a.NKB, a.d, a.cand_begin,
                           a.cand_count, a.K, a.prefix_begin, a.prefix_count, a.id_offset,
