@@ -117,9 +117,17 @@ def cpu_baseline(w):
                       f"float64 numpy oracle, {dt:.1f} s"}
 
 
-def _time_ms(torch, fn, reps=10, warmup_s=0.2):
+class _Timing(float):
+    """Average time per call in ms, carrying the median and the minimum of
+    single-launch timings (None when not taken)."""
+    median = None
+    minimum = None
+
+
+def _time_ms(torch, fn, reps=10, warmup_s=0.2, spread=True):
     """Average HIP-event time of fn() on the current stream, in ms, after
-    about warmup_s seconds of untimed calls (clocks settle under load)."""
+    about warmup_s seconds of untimed calls (clocks settle under load); with
+    spread, also the median and minimum over 20 calls timed one by one."""
     fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -134,7 +142,11 @@ def _time_ms(torch, fn, reps=10, warmup_s=0.2):
         fn()
     e1.record(s)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    t = _Timing(e0.elapsed_time(e1) / reps)
+    if spread:
+        calls = _time_calls(torch, lambda i=0: fn(), 20, 0.0)
+        t.median, t.minimum = float(np.median(calls)), float(calls.min())
+    return t
 
 
 def _time_calls(torch, fn, reps=20, warmup_s=0.2):
@@ -164,12 +176,12 @@ def measured_roofs(torch):
     a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
-    ms_g = _time_ms(torch, lambda: torch.matmul(a, b, out=c), 20)
+    ms_g = _time_ms(torch, lambda: torch.matmul(a, b, out=c), 20, spread=False)
     del a, b, c
     n = 1 << 29                                  # 1 GiB of bf16
     x = torch.empty(n, device="cuda", dtype=torch.bfloat16)
     y = torch.empty_like(x)
-    ms_c = _time_ms(torch, lambda: y.copy_(x), 20)
+    ms_c = _time_ms(torch, lambda: y.copy_(x), 20, spread=False)
     del x, y
     return {"bf16_gemm_tflops": round(2.0 * 8192 ** 3 / (ms_g * 1e-3) / 1e12, 1),
             "copy_GBs": round(2.0 * (1 << 30) / (ms_c * 1e-3) / 1e9, 1),
@@ -188,6 +200,9 @@ def _rec(ms, flops, kv_bytes, **extra):
          "kv_GBs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
          "kv_frac_hbm": round(kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
          "gflop": round(flops / 1e9, 2), "kv_MB": round(kv_bytes / 1e6, 2)}
+    if getattr(ms, "median", None) is not None:
+        r["ms_median"] = round(ms.median, 4)
+        r["ms_min"] = round(ms.minimum, 4)
     r.update(extra)
     return r
 
@@ -310,7 +325,8 @@ def per_config(reps=10, wan=None, names=None):
     if want("persistent_update"):
         ms = _time_ms(torch, lambda: ca.persistent_update(cm, km, pers, lay["local_begin"],
                                                           lay["local_count"], lay["C"]), reps)
-        out["persistent_update"] = {"us": round(ms * 1e3, 1), "candidates_per_head":
+        out["persistent_update"] = {"us": round(ms * 1e3, 1), "us_median": round(ms.median * 1e3, 1),
+                                    "us_min": round(ms.minimum * 1e3, 1), "candidates_per_head":
                                     lay["C"] + lay["local_count"], "C": lay["C"], "heads": w.H}
     del q, k, v, km
     # ragged per-head caches
@@ -330,7 +346,8 @@ def per_config(reps=10, wan=None, names=None):
     if want("ragged_pack"):
         ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, plan, 1560), reps)
         moved = 2.0 * 2.0 * tot * w.d * 2
-        out["ragged_pack"] = {"us": round(ms * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
+        out["ragged_pack"] = {"us": round(ms * 1e3, 1), "us_median": round(ms.median * 1e3, 1),
+                              "us_min": round(ms.minimum * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
                               "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del q, kf, vf, kd, vd
