@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CA_ABI_VERSION 2
+#define CA_ABI_VERSION 3
 
 enum ca_status {
   CA_OK = 0,
@@ -399,9 +399,20 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
  *          element strides q_strides (host, multiples of 8), values contiguous
  *   w_uk   bf16 [H, 96, 192] (W^K_h: latent -> content key), contiguous
  *   q_lat  fp16 [B, Nq, H, 224] contiguous output (exact bf16 products,
- *          float32 accumulation, one rounding to fp16)
+ *          float32 accumulation, one rounding to fp16; values beyond fp16's
+ *          range saturate to +-65504)
+ *   q_lat_lo  optional (NULL allowed) bf16 [B, Nq, H, 192] contiguous output:
+ *          the rounding residual x - fp16(x) of each absorbed content value
  * ca_mla_attn_fwd
  *   q_lat  fp16 [B, Nq, H, 224] contiguous (from ca_mla_absorb_q)
+ *   q_lat_lo  optional (NULL allowed) residual from ca_mla_absorb_q.  Given,
+ *          the LSE gets the first-order correction of the query's fp16
+ *          rounding: LSE += scale * (q_lat_lo . o_lat) (the softmax-weighted
+ *          mean latent row is o_lat on the content part, and the position
+ *          part of the query is exact in fp16), leaving float32-grade LSE
+ *          error instead of 2^-12 relative error on every score.  o_lat is
+ *          not corrected (its error from the rounding is first order in the
+ *          score error times the spread of the values, well inside the O bar)
  *   kv_lat fp16 latent rows [c ; k^R] (224 values): row t of batch entry b at
  *          kv_lat + b kv_batch_stride + t kv_row_stride (elements; the row
  *          stride a multiple of 8 and >= 224); a bf16 cache converts with
@@ -416,13 +427,19 @@ int ca_persistent_update(const float* q_mean, const float* k_mean, int B, int H,
  *          as a sum of two bf16 parts (relative residual 2^-17)
  * All pointers of the three calls are 16-byte aligned (else CA_EINVAL).
  * ca_cast_bf16_to_f16: y[i] = fp16 round-to-nearest-even of bf16 x[i], n a
- *   multiple of 8, both 16-byte aligned.
+ *   multiple of 8, both 16-byte aligned.  Exact for |x| in fp16's normal
+ *   range [2^-14, 65504]; smaller magnitudes round to fp16's subnormal grid
+ *   (absolute error <= 2^-25); larger finite magnitudes saturate to +-65504
+ *   (no infinities, which would turn whole rows of scores into NaN); +-inf
+ *   maps to +-65504 and NaN stays NaN.  A cache holding values beyond 65504
+ *   is therefore not represented exactly and its attention is not exact.
  */
 int ca_mla_absorb_q(const void* q, int B, int Nq, int H, int d_nope, int d_rope, int d_c,
-                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* stream);
-int ca_mla_attn_fwd(const void* q_lat, const void* kv_lat, int B, int Nq, int H, int Nkv, int d_c,
-                    int d_rope, int64_t kv_batch_stride, int64_t kv_row_stride, float scale,
-                    float* o_lat, float* lse, void* stream);
+                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* q_lat_lo,
+                    void* stream);
+int ca_mla_attn_fwd(const void* q_lat, const void* q_lat_lo, const void* kv_lat, int B, int Nq,
+                    int H, int Nkv, int d_c, int d_rope, int64_t kv_batch_stride,
+                    int64_t kv_row_stride, float scale, float* o_lat, float* lse, void* stream);
 int ca_mla_up_proj(const float* o_lat, const void* w_uv, int B, int Nq, int H, int d_c, int d_v,
                    void* o, int o_dtype, const int64_t* o_strides, void* stream);
 int ca_cast_bf16_to_f16(const void* x, void* y, int64_t n, void* stream);

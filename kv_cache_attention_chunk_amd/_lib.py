@@ -12,7 +12,7 @@ import re
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libchunkattn.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "chunkattn.h")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
 CA_BF16, CA_F32 = 0, 1
 CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
@@ -54,8 +54,8 @@ SIGNATURES = {
     "ca_persistent_update": (_i, [_p, _p, _i, _i, _i, _i, _i32p, _i, _i, _i, _i, _p, _p, _p]),
     "ca_pack_ragged": (_i, [_p, _p, _i, _i, _i, _i, _i64p, _i, _i32p, _i32p, _i, _i32p, _p, _p,
                             _i64, _p, _p]),
-    "ca_mla_absorb_q": (_i, [_p, _i, _i, _i, _i, _i, _i, _i64p, _p, _p, _p]),
-    "ca_mla_attn_fwd": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _f, _p, _p, _p]),
+    "ca_mla_absorb_q": (_i, [_p, _i, _i, _i, _i, _i, _i, _i64p, _p, _p, _p, _p]),
+    "ca_mla_attn_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _f, _p, _p, _p]),
     "ca_mla_up_proj": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _i, _i64p, _p]),
     "ca_cast_bf16_to_f16": (_i, [_p, _p, _i64, _p]),
     "ca_build_kv_index": (_i, [_i, _i, _i, _i, _i, _i32p, _i, _i32p, _i, _i, _p, _p, _p]),

@@ -185,10 +185,15 @@ def chunk_attn_dual_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         kv_indptr: torch.Tensor, kv_indices: torch.Tensor, local_count: int, *,
                         kv_block: int = 64, kv_seg: Optional[int] = None, q_block: int = 64,
                         q_seg: Optional[int] = None, scale: Optional[float] = None,
-                        out_dtype=torch.bfloat16):
+                        out_dtype=None, out_local: Optional[torch.Tensor] = None,
+                        lse_local: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """One pass over each CSR row giving attention over the row's first
     local_count blocks (the local branch: sink + current frames) and over
-    the whole row (full attention).  Returns (o_local, lse_local, o, lse)."""
+    the whole row (full attention).  Returns (o_local, lse_local, o, lse);
+    outputs given as out_local / lse_local / out / lse are written in place.
+    The output dtype is out_dtype, else out's dtype, else bf16."""
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q), _bshd("k", k), _bshd("v", v)
     B, Nq, H, d = q.shape
     Nkv = k.shape[1]
@@ -196,10 +201,10 @@ def chunk_attn_dual_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("k, v must be [B, Nkv, H, d] matching q, with equal strides")
     _i32("kv_indptr", kv_indptr), _i32("kv_indices", kv_indices)
     _check_indptr(kv_indptr, B * H, Nq, q_block, q_seg)
-    ol = _out(B, Nq, H, d, out_dtype, q.device, None)
-    ll = _lse_out(B, H, Nq, q.device, None)
-    o = _out(B, Nq, H, d, out_dtype, q.device, None)
-    l = _lse_out(B, H, Nq, q.device, None)
+    ol = _out(B, Nq, H, d, out_dtype, q.device, out_local)
+    ll = _lse_out(B, H, Nq, q.device, lse_local)
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib().ca_chunk_attn_dual_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d, _st(q), _st(k),
@@ -493,12 +498,15 @@ def pack_plan(frames, device) -> dict:
             "ptr": torch.from_numpy(ptr).to(device), "src": torch.from_numpy(src_np).to(device)}
 
 
-def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
+def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int, *,
+                out_k: Optional[torch.Tensor] = None, out_v: Optional[torch.Tensor] = None,
+                out_cu: Optional[torch.Tensor] = None):
     """Flatten per-head frame selections of a dense cache k, v [B, N, H, d]
     into k_flat, v_flat [sum of frames * frame_tokens, d] + cu_seqlens.
     `frames` is a list per head (see pack_plan) or a plan from pack_plan.
     Merged frames are the float32 average rounded to bf16.  Returns (k_flat,
-    v_flat, cu_seqlens, cu_seqlens_host)."""
+    v_flat, cu_seqlens, cu_seqlens_host); out_k / out_v (contiguous bf16
+    [rows, d]) and out_cu (int32 [B*H + 1]) are written in place when given."""
     _bshd("k", k), _bshd("v", v)
     B, N, H, d = k.shape
     if k.shape != v.shape or k.stride() != v.stride():
@@ -507,9 +515,21 @@ def pack_ragged(k: torch.Tensor, v: torch.Tensor, frames, frame_tokens: int):
     if plan["heads"] != B * H:
         raise ValueError("frames must list B*H heads")
     F = plan["frames"]
-    kf = torch.empty((F * frame_tokens, d), dtype=torch.bfloat16, device=k.device)
-    vf = torch.empty_like(kf)
-    cu = torch.empty(B * H + 1, dtype=torch.int32, device=k.device)
+
+    def flat_out(name, t):
+        if t is None:
+            return torch.empty((F * frame_tokens, d), dtype=torch.bfloat16, device=k.device)
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or \
+                tuple(t.shape) != (F * frame_tokens, d):
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor [{F * frame_tokens}, {d}]")
+        return t
+    kf, vf = flat_out("out_k", out_k), flat_out("out_v", out_v)
+    if out_cu is None:
+        cu = torch.empty(B * H + 1, dtype=torch.int32, device=k.device)
+    else:
+        cu = _i32("out_cu", out_cu)
+        if cu.numel() != B * H + 1:
+            raise ValueError("out_cu must have B*H + 1 entries")
     st = lib().ca_pack_ragged(k.data_ptr(), v.data_ptr(), B, N, H, d, _st(k), frame_tokens,
                               plan["ptr"].data_ptr(), plan["ptr_host"].ctypes.data, F,
                               plan["src"].data_ptr(), kf.data_ptr(), vf.data_ptr(), d,
@@ -528,12 +548,18 @@ def cast_bf16_to_f16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
 
 
 def mla_chunk_attn(q: torch.Tensor, kv_lat: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
-                   *, scale: Optional[float] = None, out_dtype=torch.bfloat16):
+                   *, scale: Optional[float] = None, out_dtype=torch.bfloat16,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   o_lat: Optional[torch.Tensor] = None):
     """Chunk attention over a latent KV cache (d_c = 192, d_rope = 32):
     q bf16 [B, Nq, H, 128] (content 96 + position 32), kv_lat fp16
     [B, N, 224] (rows [c ; k^R]), w_uk bf16 [H, 96, 192], w_uv bf16
-    [H, 128, 192].  Absorbs W^K into the queries, attends every (query, head)
-    row to the latent rows, projects with W^V.  Returns (o, lse, o_lat)."""
+    [H, 128, 192].  Absorbs W^K into the queries (fp16, with the rounding
+    residual kept for the LSE's first-order correction), attends every
+    (query, head) row to the latent rows, projects with W^V.  Returns
+    (o, lse, o_lat);
+    outputs given as out / lse / o_lat (float32 [B, Nq, H, 192],
+    contiguous) are written in place."""
     _bshd("q", q)
     B, Nq, H, dq = q.shape
     if kv_lat.dtype != torch.float16 or kv_lat.dim() != 3 or kv_lat.shape[0] != B or \
@@ -545,14 +571,20 @@ def mla_chunk_attn(q: torch.Tensor, kv_lat: torch.Tensor, w_uk: torch.Tensor, w_
     N = kv_lat.shape[1]
     sc = 1.0 / math.sqrt(dq) if scale is None else float(scale)
     q_lat = torch.empty((B, Nq, H, 224), dtype=torch.float16, device=q.device)
+    q_lo = torch.empty((B, Nq, H, 192), dtype=torch.bfloat16, device=q.device)
     check(lib().ca_mla_absorb_q(q.data_ptr(), B, Nq, H, 96, dq - 96, 192, _st(q), w_uk.data_ptr(),
-                                q_lat.data_ptr(), _stream()))
-    o_lat = torch.empty((B, Nq, H, 192), dtype=torch.float32, device=q.device)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    check(lib().ca_mla_attn_fwd(q_lat.data_ptr(), kv_lat.data_ptr(), B, Nq, H, N, 192, 32,
+                                q_lat.data_ptr(), q_lo.data_ptr(), _stream()))
+    if o_lat is None:
+        o_lat = torch.empty((B, Nq, H, 192), dtype=torch.float32, device=q.device)
+    elif o_lat.dtype != torch.float32 or tuple(o_lat.shape) != (B, Nq, H, 192) or \
+            not o_lat.is_contiguous() or not o_lat.is_cuda:
+        raise ValueError("o_lat must be a contiguous float32 GPU tensor [B, Nq, H, 192]")
+    lse = _lse_out(B, H, Nq, q.device, lse)
+    check(lib().ca_mla_attn_fwd(q_lat.data_ptr(), q_lo.data_ptr(), kv_lat.data_ptr(), B, Nq, H, N,
+                                192, 32,
                                 kv_lat.stride(0) if N else 0, kv_lat.stride(1) if N else 224, sc,
                                 o_lat.data_ptr(), lse.data_ptr(), _stream()))
-    o = torch.empty((B, Nq, H, 128), dtype=out_dtype, device=q.device)
+    o = _out(B, Nq, H, 128, out_dtype, q.device, out)
     check(lib().ca_mla_up_proj(o_lat.data_ptr(), w_uv.data_ptr(), B, Nq, H, 192, 128, o.data_ptr(),
                                _DT[out_dtype], _st(o), _stream()))
     return o, lse, o_lat
@@ -579,7 +611,8 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
                      sink_count: int, hist_begin: int, hist_count: int, C: int,
                      local_begin: int, local_count: int, K: int, block: int = 64,
                      seg: Optional[int] = None, k_mean: Optional[torch.Tensor] = None,
-                     scale: Optional[float] = None, out_dtype=torch.bfloat16):
+                     scale: Optional[float] = None, out_dtype=torch.bfloat16,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """The block-sparse path in the Sparse Forcing order: block means of Q and
     K (and the chunk-mean query), persistent blocks = top-C history blocks
     against the chunk-mean query, top-K local-window blocks per query block,
@@ -657,7 +690,8 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_
                             out_dtype=torch.float32)
     o, l = chunk_attn_fwd(q, k, v, kv_indptr=lo_ptr, kv_indices=lo_idx, kv_block=block,
                           kv_seg=seg, q_block=block, q_seg=seg, scale=scale,
-                          out_dtype=out_dtype, o_init=o1, lse_init=l1)
+                          out_dtype=out.dtype if out is not None else out_dtype, out=out,
+                          lse=lse, o_init=o1, lse_init=l1)
     return o, l, {"q_mean": qm, "k_mean": km, "k_mean_local": km_loc, "chunk_mean": cm,
                   "persistent": pers, "local": loc, "local_base": local_begin - loc_base,
                   "shared_indptr": sh_ptr, "shared_indices": sh_idx,

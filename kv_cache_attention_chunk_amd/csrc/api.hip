@@ -705,27 +705,31 @@ int check_mla_dims(int d_nope, int d_rope, int d_c, int d_v) {
 }  // namespace
 
 int ca_mla_absorb_q(const void* q, int B, int Nq, int H, int d_nope, int d_rope, int d_c,
-                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* stream) {
+                    const int64_t* q_strides, const void* w_uk, void* q_lat, void* q_lat_lo,
+                    void* stream) {
   if (B < 0 || Nq < 0 || H < 0) return fail(CA_EINVAL, "negative size");
   if (int r = check_mla_dims(d_nope, d_rope, d_c, kMlaVal)) return r;
   if (!q || !w_uk || !q_lat) return fail(CA_EINVAL, "NULL pointer");
-  if (!aligned16(q) || !aligned16(w_uk) || !aligned16(q_lat)) return fail(CA_EINVAL, "q, w_uk, q_lat must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(w_uk) || !aligned16(q_lat) || !aligned16(q_lat_lo))
+    return fail(CA_EINVAL, "q, w_uk, q_lat, q_lat_lo must be 16-byte aligned");
   if (int r = check_strides("q", q_strides, 8)) return r;
   if ((int64_t)B * Nq * H > 0x7FFFFFFF / 256) return fail(CA_ERANGE, "too many rows");
   if (int r = check_device()) return r;
   return launched(launch_mla_absorb(static_cast<const uint16_t*>(q), B, Nq, H, q_strides,
                                     static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_lat),
+                                    static_cast<uint16_t*>(q_lat_lo),
                                     static_cast<hipStream_t>(stream)),
                   "mla absorb launch");
 }
 
-int ca_mla_attn_fwd(const void* q_lat, const void* kv_lat, int B, int Nq, int H, int Nkv, int d_c,
-                    int d_rope, int64_t kv_batch_stride, int64_t kv_row_stride, float scale,
-                    float* o_lat, float* lse, void* stream) {
+int ca_mla_attn_fwd(const void* q_lat, const void* q_lat_lo, const void* kv_lat, int B, int Nq,
+                    int H, int Nkv, int d_c, int d_rope, int64_t kv_batch_stride,
+                    int64_t kv_row_stride, float scale, float* o_lat, float* lse, void* stream) {
   if (B < 0 || Nq < 0 || H < 0 || Nkv < 0) return fail(CA_EINVAL, "negative size");
   if (int r = check_mla_dims(kMlaNope, d_rope, d_c, kMlaVal)) return r;
   if (!q_lat || !o_lat || !lse || (Nkv > 0 && !kv_lat)) return fail(CA_EINVAL, "NULL pointer");
-  if (!aligned16(q_lat) || !aligned16(kv_lat) || !aligned16(o_lat)) return fail(CA_EINVAL, "q_lat, kv_lat, o_lat must be 16-byte aligned");
+  if (!aligned16(q_lat) || !aligned16(kv_lat) || !aligned16(o_lat) || !aligned16(q_lat_lo))
+    return fail(CA_EINVAL, "q_lat, q_lat_lo, kv_lat, o_lat must be 16-byte aligned");
   if (kv_row_stride < d_c + d_rope || kv_row_stride % 8 || kv_row_stride > (1 << 22))
     return fail(CA_EINVAL, "kv_row_stride must be a multiple of 8 in [d_c + d_rope, 2^22]");
   if (kv_batch_stride < 0 || kv_batch_stride % 8) return fail(CA_EINVAL, "kv_batch_stride must be a non-negative multiple of 8");
@@ -733,7 +737,9 @@ int ca_mla_attn_fwd(const void* q_lat, const void* kv_lat, int B, int Nq, int H,
   if ((int64_t)Nq * H > 0x7FFFFFFF / 2 || (int64_t)B * ((int64_t)Nq * H + 127) / 128 > 0x7FFFFFFF)
     return fail(CA_ERANGE, "too many rows");
   if (int r = check_device()) return r;
-  return launched(launch_mla_attn(static_cast<const uint16_t*>(q_lat), static_cast<const uint16_t*>(kv_lat),
+  return launched(launch_mla_attn(static_cast<const uint16_t*>(q_lat),
+                                  static_cast<const uint16_t*>(q_lat_lo),
+                                  static_cast<const uint16_t*>(kv_lat),
                                   kv_batch_stride, kv_row_stride, B, Nq, H, Nkv, scale, o_lat, lse,
                                   static_cast<hipStream_t>(stream)),
                   "mla attention launch");

@@ -142,10 +142,11 @@ hipError_t launch_pack_ragged(const uint16_t* k, const uint16_t* v, int B, int N
                               int total_frames, const int32_t* src, uint16_t* kf, uint16_t* vf,
                               int64_t fs, int32_t* cu, hipStream_t stream);
 hipError_t launch_mla_absorb(const uint16_t* q, int B, int Nq, int H, const int64_t* qs,
-                             const uint16_t* w_uk, uint16_t* q_lat, hipStream_t stream);
-hipError_t launch_mla_attn(const uint16_t* q_lat, const uint16_t* kv, int64_t kv_bs, int64_t kv_rs,
-                           int B, int Nq, int H, int Nkv, float scale, float* o_lat, float* lse,
-                           hipStream_t stream);
+                             const uint16_t* w_uk, uint16_t* q_lat, uint16_t* q_lat_lo,
+                             hipStream_t stream);
+hipError_t launch_mla_attn(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* kv,
+                           int64_t kv_bs, int64_t kv_rs, int B, int Nq, int H, int Nkv,
+                           float scale, float* o_lat, float* lse, hipStream_t stream);
 hipError_t launch_mla_up(const float* o_lat, int B, int Nq, int H, const uint16_t* w_uv,
                          void* o, bool o_f32, const int64_t* os, hipStream_t stream);
 hipError_t launch_cast_bf16_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);

@@ -66,6 +66,7 @@ __device__ __forceinline__ lds_void_t* mla_dma_dst(char* p) {
 
 struct MlaParams {
   const uint16_t* q;       // fp16 [B, Nq, H, 224] contiguous (absorbed query ; q^R)
+  const uint16_t* q_lo;    // optional bf16 [B, Nq, H, 192]: absorbed query - fp16(absorbed query)
   const uint16_t* kv;      // fp16 latent rows, 224 values each
   int64_t kv_bs, kv_rs;    // batch and row strides of kv, elements
   float* o;                // float32 [B, Nq, H, 192] contiguous
@@ -74,6 +75,7 @@ struct MlaParams {
   int rows_per_b;          // Nq * H
   int wg_per_b;
   float scale_log2;
+  float scale;
 };
 
 // Half-tiles of 32 latent rows flow through a ring of four LDS stages
@@ -289,8 +291,18 @@ void mla_attn_kernel(const MlaParams p) {
 
   const float lt = mla_half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // First-order correction of the LSE for the fp16 rounding of the absorbed
+  // query: with q = fp16(q) + dq, ln sum_t exp(scale (q . kv_t)) =
+  // LSE(fp16(q)) + scale dq . kbar + O(dq^2), kbar = sum_t w_t kv_t the
+  // softmax-weighted mean latent row.  dq is zero on the position part (a
+  // bf16 q^R is exact in fp16), and on the content part kbar is the latent
+  // output o~ itself, so the term is a dot product of dq with this row's
+  // outputs: the LSE then carries float32-grade error, not 2^-12 relative
+  // error on every score.
+  float corr = 0.f;
   if (qvalid) {
     float* ob = p.o + rglob * kMlaDC;
+    const uint16_t* lo = p.q_lo ? p.q_lo + rglob * kMlaDC : nullptr;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -300,15 +312,33 @@ void mla_attn_kernel(const MlaParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * r + e] * inv;
         *reinterpret_cast<f32x4_t*>(ob + d0) = v4;
+        if (lo) {
+          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(lo + d0);
+          corr = fmaf(__uint_as_float(x[0] << 16), v4[0], corr);
+          corr = fmaf(__uint_as_float(x[0] & 0xFFFF0000u), v4[1], corr);
+          corr = fmaf(__uint_as_float(x[1] << 16), v4[2], corr);
+          corr = fmaf(__uint_as_float(x[1] & 0xFFFF0000u), v4[3], corr);
+        }
       }
-    if (hg == 0) {
-      const int n = rloc / p.H, h = rloc - (rloc / p.H) * p.H;
-      p.lse[((int64_t)b * p.H + h) * p.Nq + n] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
-    }
+  }
+  corr = mla_half_sum(corr);
+  if (qvalid && hg == 0) {
+    const int n = rloc / p.H, h = rloc - (rloc / p.H) * p.H;
+    p.lse[((int64_t)b * p.H + h) * p.Nq + n] =
+        lt > 0.f ? fmaf(p.scale, corr, (m + log2f(lt)) * kLn2f) : -INFINITY;
   }
 }
 
-// bf16 -> fp16, round to nearest even; 8 values per thread
+// float32 -> fp16 operand value: finite values beyond fp16's largest finite
+// value (65504) saturate to +-65504 instead of becoming infinities (which
+// would turn whole rows of scores into NaN); NaN stays NaN.  The conversion
+// itself rounds to nearest even.
+constexpr float kF16Max = 65504.f;
+__device__ __forceinline__ float f16_saturate(float x) {
+  return fabsf(x) > kF16Max ? copysignf(kF16Max, x) : x;
+}
+
+// bf16 -> fp16, round to nearest even, saturating; 8 values per thread
 __global__ __launch_bounds__(256) void cast_bf16_f16_kernel(const uint16_t* __restrict__ x,
                                                             uint16_t* __restrict__ y, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -317,8 +347,8 @@ __global__ __launch_bounds__(256) void cast_bf16_f16_kernel(const uint16_t* __re
   f32x8_t f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __uint_as_float(v[e] << 16);
-    f[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+    f[2 * e] = f16_saturate(__uint_as_float(v[e] << 16));
+    f[2 * e + 1] = f16_saturate(__uint_as_float(v[e] & 0xFFFF0000u));
   }
   reinterpret_cast<u32x4_t*>(y)[i] = __builtin_bit_cast(u32x4_t, __builtin_convertvector(f, f16x8_t));
 }
@@ -355,6 +385,8 @@ struct ProjParams {
   void* out;
   int64_t os_r, os_h;
   int rows, H, tail;
+  uint16_t* lo;              // fp16 output only, optional: bf16(x - fp16(x)) of each output
+  int64_t ls_r, ls_h;        // its row and head strides (elements)
 };
 
 template <int K, int N, bool W_IN_MAJOR, int TIN, int TOUT>
@@ -442,12 +474,22 @@ __global__ __launch_bounds__(kProjWaves * 64) void head_proj_kernel(const ProjPa
     for (int g = 0; g < 4; ++g) {
       const int j0 = 32 * jb + 8 * g + 4 * hg;
       const f32x4_t v = {acc[jb][4 * g], acc[jb][4 * g + 1], acc[jb][4 * g + 2], acc[jb][4 * g + 3]};
-      if (TOUT == 1)
+      if (TOUT == 1) {
         *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.out) + obase + j0) = v;
-      else if (TOUT == 2)
-        *reinterpret_cast<f16x4_t*>(reinterpret_cast<_Float16*>(p.out) + obase + j0) =
-            __builtin_convertvector(v, f16x4_t);
-      else
+      } else if (TOUT == 2) {
+        f32x4_t vs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vs[e] = f16_saturate(v[e]);
+        const f16x4_t h4 = __builtin_convertvector(vs, f16x4_t);
+        *reinterpret_cast<f16x4_t*>(reinterpret_cast<_Float16*>(p.out) + obase + j0) = h4;
+        if (p.lo) {
+          // the rounding residual, exact in float32, kept to bf16 precision
+          const f32x4_t res = v - __builtin_convertvector(h4, f32x4_t);
+          *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(p.lo) +
+                                       (int64_t)r * p.ls_r + (int64_t)h * p.ls_h + j0) =
+              __builtin_convertvector(res, bf16x4_t);
+        }
+      } else
         *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(p.out) + obase + j0) =
             __builtin_convertvector(v, bf16x4_t);
     }
@@ -461,7 +503,10 @@ __global__ __launch_bounds__(kProjWaves * 64) void head_proj_kernel(const ProjPa
       const int64_t o = obase + N + 16 * hg + 8 * c;
       if (TOUT == 2) {
         typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_o;
-        *reinterpret_cast<f16x8_o*>(reinterpret_cast<_Float16*>(p.out) + o) = __builtin_convertvector(f, f16x8_o);
+        f32x8_t fs;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fs[e] = f16_saturate(f[e]);
+        *reinterpret_cast<f16x8_o*>(reinterpret_cast<_Float16*>(p.out) + o) = __builtin_convertvector(fs, f16x8_o);
       } else if (TOUT == 1) {
         *reinterpret_cast<f32x8_t*>(reinterpret_cast<float*>(p.out) + o) = f;
       } else {
@@ -477,7 +522,8 @@ __global__ __launch_bounds__(kProjWaves * 64) void head_proj_kernel(const ProjPa
 // (fp16), from bf16 q [B, Nq, H, 128] with element strides (qs_b, qs_n, qs_h)
 // and bf16 W^K [H, 96, 192].
 hipError_t launch_mla_absorb(const uint16_t* q, int B, int Nq, int H, const int64_t* qs,
-                             const uint16_t* w_uk, uint16_t* q_lat, hipStream_t stream) {
+                             const uint16_t* w_uk, uint16_t* q_lat, uint16_t* q_lat_lo,
+                             hipStream_t stream) {
   for (int b = 0; b < B; ++b) {
     ProjParams p{};
     p.in = q + b * qs[0];
@@ -486,6 +532,8 @@ hipError_t launch_mla_absorb(const uint16_t* q, int B, int Nq, int H, const int6
     p.out = q_lat + (int64_t)b * Nq * H * kMlaDK;
     p.os_r = (int64_t)H * kMlaDK; p.os_h = kMlaDK;
     p.rows = Nq; p.H = H; p.tail = kMlaDR;
+    p.lo = q_lat_lo ? q_lat_lo + (int64_t)b * Nq * H * kMlaDC : nullptr;
+    p.ls_r = (int64_t)H * kMlaDC; p.ls_h = kMlaDC;
     const dim3 grid((Nq + kProjRows - 1) / kProjRows, H);
     if (Nq > 0 && H > 0)
       hipLaunchKernelGGL((head_proj_kernel<96, kMlaDC, true, 0, 2>), grid, dim3(kProjWaves * 64), 0,
@@ -528,11 +576,12 @@ hipError_t launch_cast_bf16_f16(const uint16_t* x, uint16_t* y, int64_t n, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_mla_attn(const uint16_t* q_lat, const uint16_t* kv, int64_t kv_bs, int64_t kv_rs,
-                           int B, int Nq, int H, int Nkv, float scale, float* o_lat, float* lse,
-                           hipStream_t stream) {
+hipError_t launch_mla_attn(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* kv,
+                           int64_t kv_bs, int64_t kv_rs, int B, int Nq, int H, int Nkv,
+                           float scale, float* o_lat, float* lse, hipStream_t stream) {
   MlaParams p{};
-  p.q = q_lat; p.kv = kv; p.kv_bs = kv_bs; p.kv_rs = kv_rs;
+  p.q = q_lat; p.q_lo = q_lat_lo; p.kv = kv; p.kv_bs = kv_bs; p.kv_rs = kv_rs;
+  p.scale = scale;
   p.o = o_lat; p.lse = lse;
   p.B = B; p.Nq = Nq; p.H = H; p.Nkv = Nkv;
   p.rows_per_b = Nq * H;

@@ -714,6 +714,10 @@ __global__ __launch_bounds__(kUpdThreads) void persistent_update_kernel(
     n += tot;
     __syncthreads();
   }
+  // The evicted-range fill above is read by other waves below; with no
+  // persistent ids (C_in = 0) the compaction loop, whose barriers would
+  // otherwise order it, does not run.
+  __syncthreads();
   const int n4 = (n + 3) >> 2;
   for (int i = n + tid; i < 4 * n4; i += kUpdThreads) {
     ids[i] = 0x7FFFFFFF;

@@ -33,10 +33,28 @@ attention, merge and block means are computed in float64.  Where a floating
 point value decides an integer (the top-K block ids) the decision is taken on
 float32 scores, the precision the GPU kernels compute them in.
 
-Parity status: every function below is pinned by tests that do not re-run its
-own formula (brute-force loops, closed forms, library routines it does not
-call, cross-mode identities, planted orderings).  No function is parity
-unpinned.
+Parity status: each function below is pinned by tests that do not re-run its
+own formula, and planted-mistake tests show the pins catch plausible slips:
+  attention, chunk_attn_dense/_blocks/_varlen  brute-force fsum loops, closed
+      forms, scipy logsumexp/softmax, all blocks = dense, ragged = gathered
+      frames = block lists (tests/test_oracle_pins.py)
+  lse_merge, lse_merge_bshd    merge of disjoint branches = attention over
+      their union, special cases (tests/test_oracle_pins.py)
+  block_spans, block_mean      frame-aligned tiling by hand, ramp and constant
+      closed forms, fsum brute force (tests/test_oracle_pins.py)
+  chunk_mean_query             ramp with per-(batch, head, channel) offsets,
+      planted block lengths, fsum brute force
+      (tests/test_oracle_selection_pins.py)
+  block_score_topk, persistent_update   planted orders and ties, Python sort
+      on fsum scores (tests/test_oracle_pins.py)
+  build_kv_index               the set definition (tests/test_oracle_pins.py)
+  sparse_selection             planted inputs with hand-derived ids, and the
+      whole selection recomputed from raw tokens (fsum, Python sort)
+      (tests/test_oracle_selection_pins.py)
+  pack_ragged                  gathered frames, hand-rounded merges
+  mla_chunk_attn               brute-force loops, reduction to plain
+      attention, the absorbed form (tests/test_oracle_pins.py)
+No function is left parity unpinned.
 """
 from __future__ import annotations
 
@@ -319,8 +337,11 @@ def block_score_topk(q_mean, k_mean, cand_begin: int, cand_count: int, K: int,
 
     Returns idx [B, H, NQB, K] int32, score [B, H, NQB, K] float32 (in idx
     order), gap [B, H, NQB] = score of K-th best minus (K+1)-th best (inf if
-    K == cand_count), and near_tie [B, H, NQB] = number of candidates whose
-    score is within tie_eps of the K-th best (the K-th itself included)."""
+    K == cand_count), near_tie [B, H, NQB] = number of candidates whose
+    score is within tie_eps of the K-th best (the K-th itself included),
+    kth [B, H, NQB] = the K-th best score, and every candidate's id and
+    score: cand [B, H, NQB, cand_count] int64, cand_score (same shape,
+    float32), so that a selection differing at near-ties can be checked."""
     qm = np.asarray(q_mean, dtype=np.float32).astype(np.float64)
     km = np.asarray(k_mean, dtype=np.float32).astype(np.float64)
     B, H, NQB, d = qm.shape
@@ -331,21 +352,27 @@ def block_score_topk(q_mean, k_mean, cand_begin: int, cand_count: int, K: int,
     sc = np.zeros((B, H, NQB, K), dtype=np.float32)
     gap = np.full((B, H, NQB), np.inf)
     near = np.zeros((B, H, NQB), dtype=np.int64)
+    kth_all = np.zeros((B, H, NQB))
+    cand_score = np.zeros((B, H, NQB, cand_count), dtype=np.float32)
     for b in range(B):
         for h in range(H):
             kc = km[b, h, cand]
             for qb in range(NQB):
                 s = (kc @ qm[b, h, qb]).astype(np.float32)
+                cand_score[b, h, qb] = s
                 order = np.lexsort((cand, -s.astype(np.float64)))
                 top = order[:K]
                 asc = top[np.argsort(cand[top])]
                 idx[b, h, qb] = cand[asc]
                 sc[b, h, qb] = s[asc]
                 kth = float(s[order[K - 1]])
+                kth_all[b, h, qb] = kth
                 if K < cand_count:
                     gap[b, h, qb] = kth - float(s[order[K]])
                 near[b, h, qb] = int(np.sum(np.abs(s.astype(np.float64) - kth) < tie_eps))
-    return {"idx": idx, "score": sc, "gap": gap, "near_tie": near}
+    return {"idx": idx, "score": sc, "gap": gap, "near_tie": near, "kth": kth_all,
+            "cand": np.broadcast_to(cand, (B, H, NQB, cand_count)).copy(),
+            "cand_score": cand_score}
 
 
 def persistent_update(q_mean, k_mean, persistent, evict_begin: int, evict_count: int, C: int,
@@ -361,8 +388,10 @@ def persistent_update(q_mean, k_mean, persistent, evict_begin: int, evict_count:
     or outside [0, NB), is not a second candidate.  Scores, ordering and tie
     rule as in block_score_topk (float32 scores, higher first, lower id first
     on equal scores); the kept ids are returned ascending, padded with -1 (and
-    score -inf) when fewer than C candidates exist.  Also returns gap and
-    near_tie as block_score_topk does."""
+    score -inf) when fewer than C candidates exist.  Also returns gap,
+    near_tie and kth as block_score_topk does, and the candidates with their
+    scores (cand [B, H, n_max] int64 padded with -1, cand_score padded with
+    -inf)."""
     qm = np.asarray(q_mean, dtype=np.float32).astype(np.float64)
     km = np.asarray(k_mean, dtype=np.float32).astype(np.float64)
     pers = np.asarray(persistent, dtype=np.int64)
@@ -373,12 +402,15 @@ def persistent_update(q_mean, k_mean, persistent, evict_begin: int, evict_count:
     sc = np.full((B, H, C), -np.inf, dtype=np.float32)
     gap = np.full((B, H), np.inf)
     near = np.zeros((B, H), dtype=np.int64)
+    kth_all = np.full((B, H), -np.inf)
+    cands = []
     for b in range(B):
         for h in range(H):
             cand = sorted(ev | {int(x) for x in pers[b, h] if 0 <= x < NB})
             cand = np.array(cand, dtype=np.int64)
             s = np.array([np.float32(np.dot(qm[b, h, 0], km[b, h, c])) for c in cand],
                          dtype=np.float32)
+            cands.append((cand, s))
             order = np.lexsort((cand, -s.astype(np.float64)))
             k = min(C, len(cand))
             top = order[:k]
@@ -387,10 +419,18 @@ def persistent_update(q_mean, k_mean, persistent, evict_begin: int, evict_count:
             sc[b, h, :k] = s[asc]
             if k:
                 kth = float(s[order[k - 1]])
+                kth_all[b, h] = kth
                 if k < len(cand):
                     gap[b, h] = kth - float(s[order[k]])
                 near[b, h] = int(np.sum(np.abs(s.astype(np.float64) - kth) < tie_eps))
-    return {"idx": idx, "score": sc, "gap": gap, "near_tie": near}
+    n_max = max([len(c) for c, _ in cands] + [0])
+    cand_ids = np.full((B, H, n_max), -1, dtype=np.int64)
+    cand_sc = np.full((B, H, n_max), -np.inf, dtype=np.float32)
+    for i, (c, s) in enumerate(cands):
+        cand_ids[i // H, i % H, :len(c)] = c
+        cand_sc[i // H, i % H, :len(c)] = s
+    return {"idx": idx, "score": sc, "gap": gap, "near_tie": near, "kth": kth_all,
+            "cand": cand_ids, "cand_score": cand_sc}
 
 
 def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,

@@ -18,49 +18,137 @@ def i32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
 
 
+def half_ulp_bf16(x):
+    """Half a bf16 ulp at |x| (8-bit significand): 2^(floor(log2 |x|) - 8)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
 def o_bound(ref, out_bf16: bool):
-    """Allowed |O_gpu - O_ref|: 1e-2, plus the bf16 rounding of the stored
-    output where half a bf16 ulp alone exceeds the budget (|O| >= 4)."""
+    """Allowed |O_gpu - O_ref|.  The O bar is 1e-2 on the computed (float32)
+    output; a bf16 output then also carries its own rounding, half a bf16 ulp,
+    which reaches 2^-8 = 0.0039 below |O| = 2, 0.0078 in [2, 4) and more above.
+    Below |O| = 2 the 1e-2 bar holds outright (P's bf16 rounding and the
+    output's half-ulp together stay below it); from |O| = 2 on the bound is
+    1e-2 plus the output's half-ulp.  Float32 outputs meet 1e-2 everywhere."""
     ref = np.abs(ref)
     b = np.full(ref.shape, O_TOL)
     if out_bf16:
-        b = np.where(ref >= 4.0, O_TOL + ref * 2.0 ** -8, b)
+        b = np.where(ref >= 2.0, O_TOL + half_ulp_bf16(ref), b)
     return b
 
 
+PARITY_LOG = []     # (what, max|dO|, max|dLSE|, relaxed-bound elements, max|O_ref|)
+
+
 def assert_o(o_gpu, o_ref, out_bf16=True, what=""):
-    og = o_gpu.float().cpu().numpy().astype(np.float64)
+    og = o_gpu.float().cpu().numpy().astype(np.float64) if hasattr(o_gpu, "cpu") else \
+        np.asarray(o_gpu, np.float64)
     assert og.shape == o_ref.shape, (og.shape, o_ref.shape)
-    assert np.all(np.isfinite(og)), f"{what}: non-finite O"
+    assert np.all(np.isfinite(og)), f"{what}: non-finite O (an unwritten NaN sentinel?)"
     err = np.abs(og - o_ref)
     bound = o_bound(o_ref, out_bf16)
     bad = err > bound
     assert not bad.any(), f"{what}: {bad.sum()} O elements off, max err {err.max():.3g}"
-    return float(err.max())
+    relaxed = int(np.sum(err > O_TOL))
+    if relaxed:
+        print(f"[relaxed-bound] {what}: {relaxed} bf16 O elements above 1e-2 "
+              f"(within 1e-2 + half-ulp), max |O_ref| {np.abs(o_ref).max():.3g}", flush=True)
+    PARITY_LOG.append((what, float(err.max()) if err.size else 0.0, None, relaxed,
+                       float(np.abs(o_ref).max()) if o_ref.size else 0.0))
+    return float(err.max()) if err.size else 0.0
 
 
-def assert_lse(l_gpu, l_ref, what=""):
-    lg = l_gpu.cpu().numpy().astype(np.float64)
+def assert_lse(l_gpu, l_ref, what="", tol=None):
+    """|LSE_gpu - LSE_ref| <= 1e-3 (or `tol`, an array or scalar), and the
+    same -inf pattern (empty key sets)."""
+    lg = l_gpu.cpu().numpy().astype(np.float64) if hasattr(l_gpu, "cpu") else \
+        np.asarray(l_gpu, np.float64)
     assert lg.shape == l_ref.shape, (lg.shape, l_ref.shape)
+    assert not np.isnan(lg).any(), f"{what}: NaN LSE (an unwritten sentinel?)"
     ninf_ref = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(lg), ninf_ref), f"{what}: -inf pattern differs"
     fin = ~ninf_ref
     err = np.abs(lg[fin] - l_ref[fin]) if fin.any() else np.zeros(1)
-    assert err.max() <= LSE_TOL, f"{what}: LSE max err {err.max():.3g}"
+    bound = LSE_TOL if tol is None else np.broadcast_to(tol, l_ref.shape)[fin]
+    assert np.all(err <= bound), f"{what}: LSE max err {err.max():.3g}"
+    if PARITY_LOG and PARITY_LOG[-1][0] == what and PARITY_LOG[-1][2] is None:
+        PARITY_LOG[-1] = PARITY_LOG[-1][:2] + (float(err.max()),) + PARITY_LOG[-1][3:]
     return float(err.max())
 
 
-def compare_topk(idx_gpu, ref, tie_eps=TIE_EPS):
-    """Ids must match exactly except for (b, h, qb) rows whose K-th/(K+1)-th
-    score gap is below tie_eps; those may differ only among the near-tied
-    candidates.  Returns the number of rows that differed (all at ties)."""
-    ig = idx_gpu.cpu().numpy()
+def nan_out(B, N, H, d, dtype=torch.bfloat16):
+    """An output buffer filled with NaN: every element the kernels are meant
+    to write must have been overwritten when the call returns."""
+    return torch.full((B, N, H, d), float("nan"), dtype=dtype, device="cuda")
+
+
+def nan_lse(B, H, N):
+    return torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def assert_written(what, *ts):
+    """No NaN sentinel survived anywhere in the given outputs."""
+    for i, t in enumerate(ts):
+        n = int(torch.isnan(t.float()).sum())
+        assert n == 0, f"{what}: {n} elements of output {i} were never written"
+
+
+def wave_rows(Nq, q_block=None, q_seg=None, seed=0):
+    """Query rows that place a checked row in every 32-row wave slice of
+    every workgroup: one random row in each 32-row slice of the 256-row
+    query tiles (dense and ragged workgroups: 8 waves x 32 rows) and, with a
+    query-block tiling (q_block, q_seg), one in each 32-row slice of every
+    query block (block-list workgroups), plus the first and the last row."""
+    from oracle import chunk_attention as oc
+    rng = np.random.default_rng(seed)
+    rows = {0, Nq - 1}
+    for s in range(0, Nq, 32):
+        rows.add(int(rng.integers(s, min(s + 32, Nq))))
+    if q_block:
+        for s, l in oc.block_spans(Nq, q_block, q_seg or Nq).tolist():
+            for o in range(0, l, 32):
+                rows.add(int(rng.integers(s + o, s + min(o + 32, l))))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def compare_topk(idx_gpu, ref, tie_eps=TIE_EPS, what="", report=None):
+    """Selected ids against the oracle's.  A row must match exactly unless its
+    K-th/(K+1)-th score gap is below tie_eps.  On such a near-tie row the GPU
+    set must still hold every oracle candidate scoring above sigma_K + tie_eps,
+    and each id it holds must score at least sigma_K - tie_eps (so ids may
+    differ only inside the tie band); every such row is printed.  Ids must
+    be ascending and unique (a -1 tail pads short candidate sets).  Returns
+    the number of rows that differed; with `report` (a dict) also counts the
+    near-tie rows and the differing rows into it."""
+    ig = idx_gpu.cpu().numpy() if hasattr(idx_gpu, "cpu") else np.asarray(idx_gpu)
     ir = ref["idx"]
-    assert ig.shape == ir.shape
+    assert ig.shape == ir.shape, (ig.shape, ir.shape)
     diff = np.any(ig != ir, axis=-1)
+    near_rows = ref["gap"] < tie_eps
     for pos in zip(*np.nonzero(diff)):
-        assert ref["gap"][pos] < tie_eps, f"top-K mismatch at {pos} with gap {ref['gap'][pos]}"
+        assert ref["gap"][pos] < tie_eps, f"{what} top-K mismatch at {pos} with gap {ref['gap'][pos]}"
+        cand = ref["cand"][pos]
+        sc = ref["cand_score"][pos].astype(np.float64)
+        kth = float(ref["kth"][pos])
+        score_of = {int(c): float(x) for c, x in zip(cand, sc) if c >= 0}
+        got = [int(x) for x in ig[pos] if x >= 0]
+        assert len(got) == int(np.sum(ir[pos] >= 0)), f"{what} row {pos}: wrong count"
+        must = {c for c, x in score_of.items() if x > kth + tie_eps}
+        assert must <= set(got), f"{what} row {pos}: misses ids above the tie band"
+        for c in got:
+            assert c in score_of, f"{what} row {pos}: id {c} is not a candidate"
+            assert score_of[c] >= kth - tie_eps, f"{what} row {pos}: id {c} below the tie band"
+        print(f"[near-tie] {what} row {pos}: gap {ref['gap'][pos]:.3g}, gpu {got}, "
+              f"oracle {ir[pos].tolist()}", flush=True)
     for pos in np.ndindex(ig.shape[:-1]):
         row = ig[pos]
-        assert np.all(np.diff(row) > 0), f"ids not ascending/unique at {pos}"
+        valid = row[row >= 0]
+        assert np.all(np.diff(valid) > 0), f"{what} ids not ascending/unique at {pos}"
+        assert np.all(row[len(valid):] == -1), f"{what} padding not at the tail at {pos}"
+    if report is not None:
+        report["near_tie_rows"] = report.get("near_tie_rows", 0) + int(near_rows.sum())
+        report["rows_differing_at_ties"] = report.get("rows_differing_at_ties", 0) + int(diff.sum())
+        report["rows"] = report.get("rows", 0) + int(np.prod(ig.shape[:-1]))
     return int(diff.sum())

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ca_abi_version() == 2
+    assert L.ca_abi_version() == 3
     for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"range"),
                        (4, b"device"), (5, b"HIP")]:
         assert word in L.ca_status_str(code)

@@ -18,7 +18,7 @@ import torch
 import kv_cache_attention_chunk_amd as ca
 import oracle as orc
 from kv_cache_attention_chunk_amd import workloads as wl
-from helpers import assert_lse, assert_o, i32, to_dev
+from helpers import assert_lse, assert_o, assert_written, i32, nan_lse, nan_out, to_dev, wave_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -137,10 +137,12 @@ def test_balanced_forced_on_the_wan_layer():
     w = wl.wan_dense(seed=0)
     q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
     ws = _nan_ws(w.d)
-    o, l = ca.chunk_attn_fwd(q, k, v, scale=w.scale, balanced="always", workspace=ws)
+    o, l = nan_out(1, w.Nq, w.H, w.d), nan_lse(1, w.H, w.Nq)
+    ca.chunk_attn_fwd(q, k, v, scale=w.scale, balanced="always", workspace=ws, out=o, lse=l)
     torch.cuda.synchronize()
     assert _touched(ws), "balanced schedule not taken"
-    rows = np.r_[0:40, 2300:2330, 4600:4680]
+    assert_written("wan balanced", o, l)
+    rows = wave_rows(w.Nq, seed=7)
     Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale, rows=rows)
     assert_o(o[:, rows], Or, True, "wan balanced")
     assert_lse(l[:, :, rows], Lr, "wan balanced")

@@ -13,7 +13,7 @@ import torch
 import kv_cache_attention_chunk_amd as ca
 import oracle as orc
 from kv_cache_attention_chunk_amd import workloads as wl
-from helpers import assert_lse, assert_o, i32, to_dev
+from helpers import assert_lse, assert_o, assert_written, i32, nan_lse, nan_out, to_dev, wave_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,14 @@ def test_dual_wan_local_and_full(wan=None):
     row = np.array(local + hist, np.int32)
     ip = np.arange(w.H + 1, dtype=np.int32) * len(row)
     ix = np.tile(row, w.H)
-    ol, ll, o, l = ca.chunk_attn_dual_fwd(q, k, v, i32(ip), i32(ix), len(local), kv_block=64,
-                                          kv_seg=1560, q_block=w.Nq, q_seg=w.Nq, scale=w.scale,
-                                          out_dtype=torch.float32)
+    ol, o = (nan_out(1, w.Nq, w.H, w.d, torch.float32) for _ in range(2))
+    ll, l = nan_lse(1, w.H, w.Nq), nan_lse(1, w.H, w.Nq)
+    ca.chunk_attn_dual_fwd(q, k, v, i32(ip), i32(ix), len(local), kv_block=64, kv_seg=1560,
+                           q_block=w.Nq, q_seg=w.Nq, scale=w.scale, out_local=ol, lse_local=ll,
+                           out=o, lse=l)
     torch.cuda.synchronize()
-    rows = np.r_[0:32, 2000:2016, 4650:4680]
+    assert_written("wan dual", ol, ll, o, l)
+    rows = wave_rows(w.Nq, seed=5)
     tok = orc.block_tokens(orc.block_spans(w.Nkv, 64, 1560), local)
     Orl, Lrl = orc.chunk_attn_dense(w.q.f32[:, rows], w.k.f32[:, tok], w.v.f32[:, tok], w.scale)
     Or, Lr = orc.chunk_attn_dense(w.q.f32, w.k.f32, w.v.f32, w.scale, rows=rows)

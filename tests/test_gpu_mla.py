@@ -12,7 +12,7 @@ import torch
 import kv_cache_attention_chunk_amd as ca
 import oracle as orc
 from kv_cache_attention_chunk_amd import workloads as wl
-from helpers import assert_lse, assert_o, to_dev
+from helpers import assert_lse, assert_o, assert_written, nan_lse, nan_out, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +31,9 @@ def _run(q, kv, wk, wv, scale, out_dtype=torch.bfloat16):
     return ca.mla_chunk_attn(to_dev(q), kv16, to_dev(wk), to_dev(wv), scale=scale, out_dtype=out_dtype)
 
 
-def _ref(q, kv, wk, wv, scale, rows=None):
-    return orc.mla_chunk_attn(q.f32, kv.f32[..., :192], kv.f32[..., 192:], wk.f32, wv.f32, scale, rows=rows)
+def _ref(q, kv, wk, wv, scale, rows=None, heads=None):
+    return orc.mla_chunk_attn(q.f32, kv.f32[..., :192], kv.f32[..., 192:], wk.f32, wv.f32, scale,
+                              rows=rows, heads=heads)
 
 
 def test_cast_bf16_to_f16_rounds_to_nearest_even():
@@ -44,6 +45,21 @@ def test_cast_bf16_to_f16_rounds_to_nearest_even():
     torch.cuda.synchronize()
     ref = xb.f32.astype(np.float16)              # IEEE round to nearest even
     assert np.array_equal(y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+def test_cast_bf16_to_f16_saturates_beyond_fp16_range():
+    say("bf16 -> fp16 cast: saturation and NaN")
+    x = np.array([65504.0, 65536.0, -70000.0, 3.0e38, -3.0e38, np.inf, -np.inf, np.nan,
+                  1.0e-6, -2.0e-8, 0.0, -0.0, 1.5, 65280.0, -65280.0, 6.0e-5], np.float32)
+    xb = wl.Bf16Tensor.from_f32(x)
+    y = ca.cast_bf16_to_f16(to_dev(xb)).cpu().numpy()
+    torch.cuda.synchronize()
+    xr = xb.f32
+    ref = np.clip(xr, -65504.0, 65504.0).astype(np.float16)   # NaN stays NaN
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(y[fin].view(np.uint16), ref[fin].view(np.uint16))
+    assert np.all(np.isfinite(y[fin]))
 
 
 @pytest.mark.parametrize("B,Nq,H,N,out_dtype", [
@@ -77,9 +93,25 @@ def test_mla_empty_cache():
 def test_mla_wan_shape():
     say("mla wan shape: 12 heads x 4680 queries vs 32760 latent rows")
     w = wl.wan_mla(seed=0)
-    o, l, _ = _run(w["q"], w["kv_lat"], w["w_uk"], w["w_uv"], w["scale"])
+    B, Nq, H = 1, w["q"].shape[1], w["q"].shape[2]
+    o, l = nan_out(B, Nq, H, 128), nan_lse(B, H, Nq)
+    o_lat = torch.full((B, Nq, H, 192), float("nan"), dtype=torch.float32, device="cuda")
+    kv16 = ca.cast_bf16_to_f16(to_dev(w["kv_lat"]))
+    ca.mla_chunk_attn(to_dev(w["q"]), kv16, to_dev(w["w_uk"]), to_dev(w["w_uv"]),
+                      scale=w["scale"], out=o, lse=l, o_lat=o_lat)
     torch.cuda.synchronize()
-    rows = np.r_[0:24, 2331:2341, 4660:4680]
-    Or, Lr = _ref(w["q"], w["kv_lat"], w["w_uk"], w["w_uv"], w["scale"], rows=rows)
-    assert_o(o[:, rows], Or, True, "mla wan")
-    assert_lse(l[:, :, rows], Lr, "mla wan")
+    assert_written("mla wan", o, l, o_lat)
+    # a (query, head) row of every 32-row wave slice: kernel rows are the
+    # flattened (query, head) pairs n * H + h
+    rng = np.random.default_rng(6)
+    flat = [int(rng.integers(s, min(s + 32, Nq * H))) for s in range(0, Nq * H, 32)]
+    by_head = {}
+    for r in flat:
+        by_head.setdefault(r % H, []).append(r // H)
+    og, lg = o.float().cpu().numpy(), l.cpu().numpy()
+    for h, rows in sorted(by_head.items()):
+        rows = np.array(sorted(set(rows)))
+        Or, Lr = _ref(w["q"], w["kv_lat"], w["w_uk"], w["w_uv"], w["scale"], rows=rows,
+                      heads=[h])
+        assert_o(og[:, rows, h:h + 1], Or, True, f"mla wan head {h}")
+        assert_lse(lg[:, h:h + 1, rows], Lr, f"mla wan head {h}")

@@ -3,8 +3,10 @@ inputs (O max-abs 1e-2, LSE max-abs 1e-3, block ids exact except near-ties).
 
 Small cases span several 64-key tiles, ragged query/key tails, 24-token tail
 blocks, empty key sets, d = 64 and 128 and strided head-subset views; the
-workload-sized cases run the library exactly as the benchmark does and are
-checked on sampled query rows that the oracle computes one by one.
+workload-sized cases run the library exactly as the benchmark does, start
+from NaN-filled outputs that every element must overwrite, and are checked on
+the whole layer (dense) or on a row of every 32-row wave slice of every
+workgroup, for every head.
 """
 import math
 import sys
@@ -16,7 +18,8 @@ import torch
 import kv_cache_attention_chunk_amd as ca
 from kv_cache_attention_chunk_amd import workloads as wl
 import oracle as orc
-from helpers import assert_lse, assert_o, compare_topk, i32, to_dev
+from helpers import (assert_lse, assert_o, assert_written, compare_topk, i32, nan_lse,
+                     nan_out, to_dev, wave_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -473,11 +476,11 @@ def test_build_kv_index_unstaged_large():
 
 
 # ---------------------------------------------------------------------------
-# workload-sized cases, exactly as the benchmark runs them, on sampled rows
+# workload-sized cases, exactly as the benchmark runs them.  Outputs start as
+# NaN sentinels, which every element must have overwritten; the whole dense
+# layer is compared with the oracle, the other modes on a row in every 32-row
+# wave slice of every workgroup, for every head.
 # ---------------------------------------------------------------------------
-WAN_ROWS = np.r_[0:32, 120:136, 2000:2008, 4600:4616, 4664:4680]
-
-
 @pytest.fixture(scope="module")
 def wan():
     return wl.wan_dense(seed=0)
@@ -488,36 +491,49 @@ def wan_dev(wan):
     return to_dev(wan.q), to_dev(wan.k), to_dev(wan.v)
 
 
-@pytest.mark.parametrize("policy", ["auto", "never"])
-def test_wan_dense_full_size(wan, wan_dev, policy):
+@pytest.fixture(scope="module")
+def wan_dense_ref(wan):
+    say("oracle: the whole wan dense layer (12 heads x 4680 rows x 32760 keys)")
+    return orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale)
+
+
+@pytest.mark.parametrize("policy", ["auto", "never", "always"])
+def test_wan_dense_full_size(wan, wan_dev, wan_dense_ref, policy):
     # auto: the schedule bench.py times; never: the plain grid, one workgroup
-    # per (head, 256-query tile)
-    say(f"wan dense 12x4680x32760 d128, split policy {policy}")
+    # per (head, 256-query tile); always: the balanced schedule
+    say(f"wan dense 12x4680x32760 d128, split policy {policy}, whole layer")
     q, k, v = wan_dev
-    o, l = ca.chunk_attn_fwd(q, k, v, scale=wan.scale, balanced=policy)
+    o, l = nan_out(1, wan.Nq, wan.H, wan.d), nan_lse(1, wan.H, wan.Nq)
+    ca.chunk_attn_fwd(q, k, v, scale=wan.scale, balanced=policy, out=o, lse=l)
     torch.cuda.synchronize()
-    Or, Lr = orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale, rows=WAN_ROWS)
-    assert_o(o[:, WAN_ROWS], Or, True, "wan dense")
-    assert_lse(l[:, :, WAN_ROWS], Lr, "wan dense")
-    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+    assert_written("wan dense", o, l)
+    Or, Lr = wan_dense_ref
+    assert_o(o, Or, True, f"wan dense {policy}")
+    assert_lse(l, Lr, f"wan dense {policy}")
 
 
-def test_wan_local_history_merge_full_size(wan, wan_dev):
-    say("wan local/history merge")
+def test_wan_local_history_merge_full_size(wan, wan_dev, wan_dense_ref):
+    say("wan local/history merge, whole layer")
     q, k, v = wan_dev
     outs = []
     for key in ("local_blocks", "history_blocks"):
         blocks = np.array(wan.meta[key], np.int32)
         ip = np.arange(wan.H + 1, dtype=np.int32) * len(blocks)
         ix = np.tile(blocks, wan.H)
-        outs.append(ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(ip), kv_indices=i32(ix), kv_block=64,
-                                      kv_seg=1560, q_block=wan.Nq, q_seg=wan.Nq, scale=wan.scale,
-                                      out_dtype=torch.float32))
-    om, lm = ca.lse_merge(outs[0][0], outs[0][1], outs[1][0], outs[1][1], out_dtype=torch.bfloat16)
+        ob = nan_out(1, wan.Nq, wan.H, wan.d, torch.float32)
+        lb = nan_lse(1, wan.H, wan.Nq)
+        ca.chunk_attn_fwd(q, k, v, kv_indptr=i32(ip), kv_indices=i32(ix), kv_block=64,
+                          kv_seg=1560, q_block=wan.Nq, q_seg=wan.Nq, scale=wan.scale,
+                          out=ob, lse=lb)
+        outs.append((ob, lb))
+    om, lm = nan_out(1, wan.Nq, wan.H, wan.d), nan_lse(1, wan.H, wan.Nq)
+    ca.lse_merge(outs[0][0], outs[0][1], outs[1][0], outs[1][1], out=om, out_lse=lm)
     torch.cuda.synchronize()
-    Or, Lr = orc.chunk_attn_dense(wan.q.f32, wan.k.f32, wan.v.f32, wan.scale, rows=WAN_ROWS)
-    assert_o(om[:, WAN_ROWS], Or, True, "wan merge")
-    assert_lse(lm[:, :, WAN_ROWS], Lr, "wan merge")
+    assert_written("wan merge branches", outs[0][0], outs[0][1], outs[1][0], outs[1][1])
+    assert_written("wan merge", om, lm)
+    Or, Lr = wan_dense_ref
+    assert_o(om, Or, True, "wan merge")
+    assert_lse(lm, Lr, "wan merge")
 
 
 def _union_csr(info, H, nqb):
@@ -539,18 +555,20 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
     say(f"wan block-sparse ratio={ratio}")
     q, k, v = wan_dev
     lay = wl.sparse_layout(wan, ratio)
-    o, l, info = ca.block_sparse_fwd(q, k, v, sink_begin=0, sink_count=lay["sink_count"],
+    o, l = nan_out(1, wan.Nq, wan.H, wan.d), nan_lse(1, wan.H, wan.Nq)
+    _, _, info = ca.block_sparse_fwd(q, k, v, sink_begin=0, sink_count=lay["sink_count"],
                                      hist_begin=lay["hist_begin"], hist_count=lay["hist_count"],
                                      C=lay["C"], local_begin=lay["local_begin"],
                                      local_count=lay["local_count"], K=lay["K"], block=64,
-                                     seg=1560, scale=wan.scale)
+                                     seg=1560, scale=wan.scale, out=o, lse=l)
     torch.cuda.synchronize()
+    assert_written("wan sparse", o, l)
     sel = orc.sparse_selection(wan.q.f32, wan.k.f32, 64, 1560, 64, 1560, lay)
     np.testing.assert_allclose(info["q_mean"].cpu().numpy(), sel["q_mean"], rtol=0, atol=5e-6)
     np.testing.assert_allclose(info["k_mean"].cpu().numpy(), sel["k_mean"], rtol=0, atol=5e-6)
     np.testing.assert_allclose(info["chunk_mean"].cpu().numpy(), sel["chunk_mean"], rtol=0, atol=5e-6)
-    ties = (compare_topk(info["persistent"], sel["persistent"])
-            + compare_topk(info["local"] + info["local_base"], sel["local"]))
+    ties = (compare_topk(info["persistent"], sel["persistent"], what="persistent")
+            + compare_topk(info["local"] + info["local_base"], sel["local"], what="local"))
     say(f"top-K rows differing at near-ties: {ties}")
     ip, ix = _union_csr(info, wan.H, 75)
     if ties == 0:
@@ -558,12 +576,13 @@ def test_wan_block_sparse_pipeline(wan, wan_dev, ratio):
         for r in range(len(ip) - 1):
             np.testing.assert_array_equal(np.sort(ix[ip[r]:ip[r + 1]]),
                                           sel["indices"][sel["indptr"][r]:sel["indptr"][r + 1]])
-    # attention over the selected lists (as built on the GPU, checked above)
-    rows = np.r_[0:64, 1536:1560, 4616:4680]
+    # attention over the selected lists (as built on the GPU, checked above),
+    # on a row of every 32-row wave slice of every query block and tile
+    rows = wave_rows(wan.Nq, 64, 1560, seed=int(ratio * 1000))
     Or, Lr = orc.chunk_attn_blocks(wan.q.f32, wan.k.f32, wan.v.f32, ip, ix, 64, 1560, 64, 1560,
                                    wan.scale, rows=rows)
-    assert_o(o[:, rows], Or, True, "wan sparse")
-    assert_lse(l[:, :, rows], Lr, "wan sparse")
+    assert_o(o[:, rows], Or, True, f"wan sparse {ratio}")
+    assert_lse(l[:, :, rows], Lr, f"wan sparse {ratio}")
 
 
 @pytest.mark.parametrize("lay", [
@@ -669,10 +688,12 @@ def test_resume_from_empty_branch_and_into_empty_set():
 def test_ragged_full_size():
     say("ragged 12 heads, cu_seqlens")
     w = wl.ragged(seed=0)
-    o, l = ca.chunk_attn_varlen_fwd(to_dev(w.q), to_dev(w.k_flat), to_dev(w.v_flat), i32(w.cu_seqlens),
-                                    cu_seqlens_host=w.cu_seqlens, scale=w.scale)
+    o, l = nan_out(1, w.Nq, w.H, w.d), nan_lse(1, w.H, w.Nq)
+    ca.chunk_attn_varlen_fwd(to_dev(w.q), to_dev(w.k_flat), to_dev(w.v_flat), i32(w.cu_seqlens),
+                             cu_seqlens_host=w.cu_seqlens, scale=w.scale, out=o, lse=l)
     torch.cuda.synchronize()
-    rows = np.r_[0:40, 4640:4680]
+    assert_written("ragged", o, l)
+    rows = wave_rows(w.Nq, seed=3)
     Or, Lr = orc.chunk_attn_varlen(w.q.f32, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens, w.scale, rows=rows)
     assert_o(o[:, rows], Or, True, "ragged")
     assert_lse(l[:, :, rows], Lr, "ragged")
@@ -706,13 +727,15 @@ def test_mixed_40_heads_full_size():
     ip = np.zeros(len(lists) + 1, np.int32)
     ip[1:] = np.cumsum([len(x) for x in lists])
     ix = np.concatenate(lists).astype(np.int32)
-    o, l = ca.chunk_attn_mixed_fwd(q, w.head_mode, k=k, v=v, kv_indptr=i32(ip), kv_indices=i32(ix),
-                                   kv_block=64, kv_seg=1560, q_block=64, q_seg=1560,
-                                   k_flat=to_dev(w.k_flat), v_flat=to_dev(w.v_flat),
-                                   cu_seqlens=i32(w.cu_seqlens), cu_seqlens_host=w.cu_seqlens,
-                                   scale=w.scale)
+    o, l = nan_out(1, w.Nq, w.H, w.d), nan_lse(1, w.H, w.Nq)
+    ca.chunk_attn_mixed_fwd(q, w.head_mode, k=k, v=v, kv_indptr=i32(ip), kv_indices=i32(ix),
+                            kv_block=64, kv_seg=1560, q_block=64, q_seg=1560,
+                            k_flat=to_dev(w.k_flat), v_flat=to_dev(w.v_flat),
+                            cu_seqlens=i32(w.cu_seqlens), cu_seqlens_host=w.cu_seqlens,
+                            scale=w.scale, out=o, lse=l)
     torch.cuda.synchronize()
-    rows = np.r_[0:16, 1540:1560, 4664:4680]
+    assert_written("mixed", o, l)
+    rows = wave_rows(w.Nq, 64, 1560, seed=4)
     og, lg = o[:, rows].float().cpu().numpy(), l[:, :, rows].cpu().numpy()
     for mode in range(3):
         hs = [h for h in range(w.H) if w.head_mode[h] == mode]

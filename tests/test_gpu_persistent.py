@@ -121,3 +121,35 @@ def test_persistent_update_wan_eviction():
     say(f"updated rows differing at near-ties: {ties}")
     n_evicted = int(((new.cpu().numpy() >= lay["local_begin"])).sum())
     say(f"evicted blocks entering the persistent set: {n_evicted} of {w.H * lay['C']}")
+
+
+@pytest.mark.parametrize("ne,integer_scores", [(1000, False), (1000, True), (100, False),
+                                               (37, True)])
+def test_persistent_update_without_persistent_set(ne, integer_scores):
+    """C_in = 0 (the first eviction: persistent = None), so the candidates are
+    the evicted range alone: 12 heads, d = 128, up to 1000 evicted blocks
+    (radix select above 128 candidates).  With small-integer scores full of
+    exact ties the ids and scores must equal the oracle's exactly; with random
+    scores exactly except at near-ties."""
+    say(f"persistent update C_in=0 ne={ne} integer={integer_scores}")
+    rng = np.random.default_rng(ne + 7 * integer_scores)
+    B, H, NB, d, C, eb = 1, 12, 1200, 128, 32, 150
+    if integer_scores:
+        qm = np.zeros((B, H, 1, d), np.float32)
+        qm[..., 3] = 1.0
+        km = np.zeros((B, H, NB, d), np.float32)
+        km[..., 3] = rng.integers(-6, 7, size=(B, H, NB))
+    else:
+        qm, km = _f32(rng, B, H, 1, d), _f32(rng, B, H, NB, d)
+    idx, sc = ca.persistent_update(torch.from_numpy(qm).cuda(), torch.from_numpy(km).cuda(),
+                                   None, eb, ne, C, return_scores=True)
+    torch.cuda.synchronize()
+    ref = orc.persistent_update(qm, km, np.zeros((B, H, 0), np.int32), eb, ne, C)
+    if integer_scores:
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+        np.testing.assert_array_equal(sc.cpu().numpy(), ref["score"])
+    else:
+        ties = compare_topk(idx, ref)
+        say(f"rows differing at near-ties: {ties}")
+        if ties == 0:
+            np.testing.assert_allclose(sc.cpu().numpy(), ref["score"], rtol=1e-5, atol=1e-5)
