@@ -146,6 +146,106 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * PBSA in one pass (Sparse Forcing page, section 2 item 3: dense attention
+ * over the persistent blocks, sparse attention over the top-K blocks of the
+ * local window chosen per query block).  The key set of query block qb of
+ * head (b, h) is the union of two block lists:
+ *   shared_indptr,   CSR row b*H + h (B*H + 1 entries): blocks every query
+ *   shared_indices   block of the head attends to (the sink frame and the
+ *                    persistent blocks)
+ *   local_indptr,    CSR row (b*H + h)*NQB + qb (B*H*NQB + 1 entries,
+ *   local_indices    NQB = ca_num_blocks(Nq, q_block, q_seg)): the query
+ *                    block's own blocks (its top-K window blocks)
+ * Ids refer to the KV tiling (kv_block, kv_seg), must be distinct within a
+ * row, and a block must not appear in both lists of a row (it would count
+ * twice); order is free.  Ids outside the tiling contribute no keys.
+ *   *_nnz        entries of the indices arrays; row spans are clamped to them
+ *   q_block      1..64 (each query block is served by 64 rows of a workgroup)
+ * One launch: each workgroup keeps four query blocks' softmax state in
+ * registers over the shared list and then their local lists, with no
+ * intermediate output.  Other arguments as in ca_chunk_attn_fwd; an empty
+ * key set gives O = 0, LSE = -inf.
+ */
+int ca_chunk_attn_pbsa_fwd(const void* q, const void* k, const void* v,
+                           int B, int H, int Nq, int Nkv, int d,
+                           const int64_t* q_strides, const int64_t* kv_strides,
+                           const int64_t* o_strides,
+                           const int32_t* shared_indptr, const int32_t* shared_indices,
+                           int shared_nnz, const int32_t* local_indptr,
+                           const int32_t* local_indices, int local_nnz,
+                           int kv_block, int kv_seg, int q_block, int q_seg, float scale,
+                           void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * The block-sparse path in one call (Sparse Forcing page, section 2): block
+ * representatives (item 2: the mean of each block's tokens), persistent
+ * memory = the C history blocks with the highest coarse score against the
+ * chunk-mean query (item 1), the K local-window blocks with the highest
+ * coarse score per query block (item 2), and PBSA over the union of the
+ * sink blocks, the persistent blocks and the query block's top-K blocks
+ * (item 3, one ca_chunk_attn_pbsa_fwd launch).  Coarse scores, ties and id
+ * order as in ca_block_score_topk.
+ *
+ *   q, k, v, strides, scale, o, o_dtype, lse   as in ca_chunk_attn_fwd
+ *   block, seg   one frame-aligned tiling for both axes (block 1..64): query
+ *                block qb and KV block ids as ca_num_blocks counts them
+ *   sink_begin, sink_count   KV blocks every query block attends to
+ *   hist_begin, hist_count   candidates of the persistent selection
+ *   local_begin, local_count candidates of the top-K selection (the local
+ *                            window, at most 4096; so is the history)
+ *                The three ranges lie in [0, NKB) and must be disjoint.
+ *   C, K         0 <= C <= hist_count, 0 <= K <= local_count
+ *   k_mean       optional float32 [B, H, NKB, d]: key-block means kept as
+ *                resident state from earlier steps (only the history
+ *                entries are read; the local window holds the current chunk,
+ *                so its means are recomputed from k).  NULL: every key
+ *                block's mean is computed.
+ *   workspace    caller-owned device memory of at least the size
+ *                ca_block_sparse_workspace returns, 256-byte aligned; it
+ *                holds the intermediates at the offsets that call reports
+ *                (they can be read back after the call).  Calls sharing a
+ *                workspace must be ordered on one stream.
+ * Launches: one block-mean launch (two or three when the local window is
+ * not the chunk's own size or not frame-aligned), one selection launch
+ * (both selections and their block lists; a separate list merge when the
+ * sink range lies above the history or C = 0), one attention launch.
+ */
+typedef struct ca_block_sparse_ws {
+  size_t bytes;            /* workspace size */
+  size_t q_mean;           /* float32 [B, H, NQB, d] query-block means */
+  size_t k_mean;           /* float32 [B, H, NKB, d] every key block's mean (k_mean_in_ws) */
+  size_t k_mean_local;     /* float32 [B, H, local_count, d] the window's means (window_means) */
+  size_t chunk_mean;       /* float32 [B, H, d] mean of all Nq queries per head (C > 0) */
+  size_t persistent;       /* int32 [B, H, C] persistent ids, ascending */
+  size_t local;            /* int32 [B, H, NQB, K] top-K ids - local_id_base, ascending */
+  size_t shared_indptr;    /* int32 [B*H + 1] ... */
+  size_t shared_indices;   /* ... CSR per head: sink + persistent ids */
+  size_t local_indptr;     /* int32 [B*H*NQB + 1] ... */
+  size_t local_indices;    /* ... CSR per query block: its top-K ids */
+  int window_means;        /* 1: the local window's means are computed over the window alone */
+  int window_token0;       /* its first token */
+  int window_tokens;       /* its token count */
+  int local_id_base;       /* absolute KV block id = local id + local_id_base */
+  int k_mean_in_ws;        /* 1: k_mean holds every key block's mean */
+} ca_block_sparse_ws;
+
+/* Workspace size of ca_block_sparse_fwd for these sizes and ranges
+ * (have_k_mean: whether k_mean will be given), 0 on invalid arguments
+ * (ca_last_error() says why); `layout` (NULL allowed) receives the offsets. */
+size_t ca_block_sparse_workspace(int B, int H, int Nq, int Nkv, int d, int block, int seg,
+                                 int sink_begin, int sink_count, int hist_begin, int hist_count,
+                                 int C, int local_begin, int local_count, int K, int have_k_mean,
+                                 ca_block_sparse_ws* layout);
+
+int ca_block_sparse_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv,
+                        int d, const int64_t* q_strides, const int64_t* kv_strides,
+                        const int64_t* o_strides, int block, int seg, int sink_begin,
+                        int sink_count, int hist_begin, int hist_count, int C, int local_begin,
+                        int local_count, int K, const float* k_mean, float scale, void* o,
+                        int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * Dual-output chunk attention (ISPA page, section 2 item 1: the dual-stream
  * warmup computes attention over the local tokens — the current frames and
  * the sink — and over the full history side by side).  Block-list mode as in

@@ -38,6 +38,14 @@ SIGNATURES = {
     "ca_chunk_attn_dual_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i32p, _i32p,
                                     _i, _i, _i, _i, _i, _i, _f, _p, _i64p, _p, _p, _i64p, _i,
                                     _p, _p]),
+    "ca_chunk_attn_pbsa_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
+                                    _i32p, _i32p, _i, _i32p, _i32p, _i, _i, _i, _i, _i, _f,
+                                    _p, _i, _p, _p]),
+    "ca_block_sparse_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                        _i, _i, _p]),
+    "ca_block_sparse_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p, _i, _i,
+                                 _i, _i, _i, _i, _i, _i, _i, _i, _p, _f, _p, _i, _p, _p, _sz,
+                                 _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
                                       _i64p, _i64, _i64p, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
@@ -74,6 +82,15 @@ class TopkJob(ctypes.Structure):
                 ("id_offset", ctypes.c_int),
                 ("out_idx", ctypes.c_void_p), ("out_score", ctypes.c_void_p),
                 ("indptr", ctypes.c_void_p), ("indices", ctypes.c_void_p)]
+
+
+class BlockSparseWs(ctypes.Structure):
+    """ctypes mirror of ca_block_sparse_ws (include/chunkattn.h)."""
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "bytes", "q_mean", "k_mean", "k_mean_local", "chunk_mean", "persistent", "local",
+        "shared_indptr", "shared_indices", "local_indptr", "local_indices")] + \
+        [(n, ctypes.c_int) for n in ("window_means", "window_token0", "window_tokens",
+                                     "local_id_base", "k_mean_in_ws")]
 
 
 def header_functions():

@@ -181,6 +181,43 @@ def chunk_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return o, l
 
 
+def chunk_attn_pbsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        shared_indptr: torch.Tensor, shared_indices: torch.Tensor,
+                        local_indptr: torch.Tensor, local_indices: torch.Tensor, *,
+                        kv_block: int = 64, kv_seg: Optional[int] = None, q_block: int = 64,
+                        q_seg: Optional[int] = None, scale: Optional[float] = None,
+                        out_dtype=None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None):
+    """PBSA in one pass: query block qb of head bh = b*H + h attends to the
+    blocks of its head's shared list (CSR row bh: the sink and persistent
+    blocks) together with its own local list (CSR row bh * NQB + qb: its
+    top-K window blocks).  The two lists of a row must be disjoint; q_block
+    at most 64.  Returns (O, LSE)."""
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    _bshd("q", q), _bshd("k", k), _bshd("v", v)
+    B, Nq, H, d = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, d) or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k, v must be [B, Nkv, H, d] matching q, with equal strides")
+    for n, t in (("shared_indptr", shared_indptr), ("shared_indices", shared_indices),
+                 ("local_indptr", local_indptr), ("local_indices", local_indices)):
+        _i32(n, t)
+    if shared_indptr.numel() != B * H + 1:
+        raise ValueError("shared_indptr must have B*H + 1 entries")
+    _check_indptr(local_indptr, B * H, Nq, q_block, q_seg)
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().ca_chunk_attn_pbsa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d, _st(q), _st(k), _st(o),
+        shared_indptr.data_ptr(), shared_indices.data_ptr(), shared_indices.numel(),
+        local_indptr.data_ptr(), local_indices.data_ptr(), local_indices.numel(), kv_block,
+        kv_seg or max(Nkv, 1), q_block, q_seg or max(Nq, 1), sc, o.data_ptr(), _DT[out_dtype],
+        l.data_ptr(), _stream())
+    check(st)
+    return o, l
+
+
 def chunk_attn_dual_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         kv_indptr: torch.Tensor, kv_indices: torch.Tensor, local_count: int, *,
                         kv_block: int = 64, kv_seg: Optional[int] = None, q_block: int = 64,
@@ -607,92 +644,86 @@ def build_kv_index(B: int, H: int, NQB: int, sink_begin: int, sink_count: int,
     return indptr, indices
 
 
+def block_sparse_workspace(B: int, H: int, Nq: int, Nkv: int, d: int, *, block: int, seg: int,
+                           sink_begin: int, sink_count: int, hist_begin: int, hist_count: int,
+                           C: int, local_begin: int, local_count: int, K: int,
+                           have_k_mean: bool) -> "_lib.BlockSparseWs":
+    """Workspace layout of block_sparse_fwd (sizes and byte offsets)."""
+    layout = _lib.BlockSparseWs()
+    n = lib().ca_block_sparse_workspace(B, H, Nq, Nkv, d, block, seg, sink_begin, sink_count,
+                                        hist_begin, hist_count, C, local_begin, local_count, K,
+                                        int(bool(have_k_mean)), ctypes.byref(layout))
+    if n == 0:
+        check(_lib.CA_EINVAL)
+    return layout
+
+
 def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sink_begin: int,
                      sink_count: int, hist_begin: int, hist_count: int, C: int,
                      local_begin: int, local_count: int, K: int, block: int = 64,
                      seg: Optional[int] = None, k_mean: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, out_dtype=torch.bfloat16,
-                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """The block-sparse path in the Sparse Forcing order: block means of Q and
-    K (and the chunk-mean query), persistent blocks = top-C history blocks
-    against the chunk-mean query, top-K local-window blocks per query block,
-    then PBSA attention: dense over the blocks every query block shares (sink
-    + persistent, one list per head, float32 branch output), continued per
-    query block over its top-K local blocks by resuming from that branch's
-    (O, LSE) state.  The sink, history and local id ranges must be disjoint.
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """The block-sparse path in the Sparse Forcing order, one native call
+    (ca_block_sparse_fwd): block means of Q and K (and the chunk-mean query),
+    persistent blocks = top-C history blocks against the chunk-mean query,
+    top-K local-window blocks per query block, then PBSA in one pass: every
+    query block attends to the blocks its head shares (sink + persistent)
+    together with its own top-K local blocks.  The sink, history and local
+    id ranges must be disjoint.
 
     `k_mean` carries key-block means of the cache kept from earlier steps
-    (resident state, [B, H, NB, d] float32); only the history entries are read
-    from it.  The local window holds the current chunk, so its block means are
-    recomputed here from k (over just that window when it starts on a segment
-    boundary).  Without `k_mean` the means of every cache block are computed.
-    Returns (O, LSE, info) with the selected ids and block lists in `info`;
-    info["local"] holds local-window ids relative to info["local_base"]."""
+    (resident state, [B, H, NB, d] float32); only the history entries are
+    read from it, and the local window's means are recomputed from k.
+    Returns (O, LSE, info); `info` holds views into the workspace: the block
+    means, the selected ids and the block lists (info["local"] holds ids
+    relative to info["local_base"])."""
+    out_dtype = out.dtype if out is not None else out_dtype
+    _bshd("q", q), _bshd("k", k), _bshd("v", v)
     B, Nq, H, d = q.shape
     Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, d) or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k, v must be [B, Nkv, H, d] matching q, with equal strides")
     seg = seg or Nq
-    kv_seg = seg
-    ranges = sorted([(sink_begin, sink_count), (hist_begin, hist_count), (local_begin, local_count)])
-    if any(a[0] + a[1] > b[0] for a, b in zip(ranges, ranges[1:])):
-        raise ValueError("sink, history and local block ranges must be disjoint")
-    bps = -(-kv_seg // block)
-    km_loc, loc_base, qm = None, local_begin, None
-    if k_mean is None:
-        km = block_mean(k, block, kv_seg)
-        km_loc = km
-    else:
-        km = k_mean
-        if K and local_begin % bps == 0:
-            last = local_begin + local_count - 1
-            t0 = (local_begin // bps) * kv_seg
-            t1 = min(Nkv, (last // bps) * kv_seg + min(kv_seg, (last % bps + 1) * block))
-            kw = k[:, t0:t1]
-            if kw.shape == q.shape:
-                # the window holds as many tokens as the chunk: one launch
-                qm, km_loc, cm = block_mean_pair(q, kw, block, seg, with_total=True)
-            else:
-                km_loc = block_mean(kw, block, kv_seg)
-            loc_base = 0
-        elif K:
-            km_loc = block_mean(k, block, kv_seg)
-    if qm is None:
-        qm, cm = block_mean(q, block, seg, with_total=True)
-    # Selection and block lists in one launch each when a list is a prefix
-    # range followed by the selected ids; otherwise a separate merge.
-    nqb = qm.shape[2]
-    loc = None
-    if C and K and sink_begin + sink_count <= hist_begin:
-        # both selections and their block lists in one launch
-        (pers, sh_ptr, sh_idx), (loc, lo_ptr, lo_idx) = block_score_topk_batch([
-            dict(q_mean=cm, k_mean=km, K=C, cand_begin=hist_begin, cand_count=hist_count,
-                 prefix_begin=sink_begin, prefix_count=sink_count, lists=True),
-            dict(q_mean=qm, k_mean=km_loc, K=K, cand_begin=loc_base, cand_count=local_count,
-                 id_offset=local_begin - loc_base, lists=True)])
-    elif C and sink_begin + sink_count <= hist_begin:
-        pers, sh_ptr, sh_idx = block_score_topk_lists(cm, km, C, cand_begin=hist_begin,
-                                                      cand_count=hist_count,
-                                                      prefix_begin=sink_begin,
-                                                      prefix_count=sink_count)
-    else:
-        pers = (block_score_topk(cm, km, C, cand_begin=hist_begin, cand_count=hist_count)
-                if C else None)
-        sh_ptr, sh_idx = build_kv_index(B, H, 1, sink_begin, sink_count,
-                                        None if pers is None else pers[:, :, 0, :].contiguous(),
-                                        None, 0, device=q.device)
-    if K and loc is None:
-        loc, lo_ptr, lo_idx = block_score_topk_lists(qm, km_loc, K, cand_begin=loc_base,
-                                                     cand_count=local_count,
-                                                     id_offset=local_begin - loc_base)
-    elif not K:
-        lo_ptr, lo_idx = build_kv_index(B, H, nqb, 0, 0, None, None, 0, device=q.device)
-    o1, l1 = chunk_attn_fwd(q, k, v, kv_indptr=sh_ptr, kv_indices=sh_idx, kv_block=block,
-                            kv_seg=seg, q_block=Nq, q_seg=Nq, scale=scale,
-                            out_dtype=torch.float32)
-    o, l = chunk_attn_fwd(q, k, v, kv_indptr=lo_ptr, kv_indices=lo_idx, kv_block=block,
-                          kv_seg=seg, q_block=block, q_seg=seg, scale=scale,
-                          out_dtype=out.dtype if out is not None else out_dtype, out=out,
-                          lse=lse, o_init=o1, lse_init=l1)
-    return o, l, {"q_mean": qm, "k_mean": km, "k_mean_local": km_loc, "chunk_mean": cm,
-                  "persistent": pers, "local": loc, "local_base": local_begin - loc_base,
-                  "shared_indptr": sh_ptr, "shared_indices": sh_idx,
-                  "local_indptr": lo_ptr, "local_indices": lo_idx}
+    nkb, nqb = num_blocks(Nkv, block, seg), num_blocks(Nq, block, seg)
+    if k_mean is not None:
+        if k_mean.dtype != torch.float32 or tuple(k_mean.shape) != (B, H, nkb, d) or \
+                not k_mean.is_contiguous() or not k_mean.is_cuda:
+            raise ValueError(f"k_mean must be a contiguous float32 GPU tensor [B, H, {nkb}, d]")
+    ranges = dict(sink_begin=sink_begin, sink_count=sink_count, hist_begin=hist_begin,
+                  hist_count=hist_count, C=C, local_begin=local_begin, local_count=local_count, K=K)
+    lay = block_sparse_workspace(B, H, Nq, Nkv, d, block=block, seg=seg,
+                                 have_k_mean=k_mean is not None, **ranges)
+    if workspace is None:
+        workspace = torch.empty(lay.bytes, dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    o = _out(B, Nq, H, d, out_dtype, q.device, out)
+    l = _lse_out(B, H, Nq, q.device, lse)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().ca_block_sparse_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Nq, Nkv, d, _st(q), _st(k), _st(o), block,
+        seg, sink_begin, sink_count, hist_begin, hist_count, C, local_begin, local_count, K,
+        _ptr(k_mean), sc, o.data_ptr(), _DT[out_dtype], l.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream())
+    check(st)
+
+    def view(off, dtype, shape):
+        n = int(np.prod(shape))
+        size = torch.tensor([], dtype=dtype).element_size()
+        return workspace[off:off + n * size].view(dtype).view(*shape)
+    f32, i32t = torch.float32, torch.int32
+    km = view(lay.k_mean, f32, (B, H, nkb, d)) if lay.k_mean_in_ws else k_mean
+    km_loc = view(lay.k_mean_local, f32, (B, H, local_count, d)) if lay.window_means else km
+    info = {"q_mean": view(lay.q_mean, f32, (B, H, nqb, d)), "k_mean": km,
+            "k_mean_local": km_loc, "chunk_mean": view(lay.chunk_mean, f32, (B, H, 1, d)),
+            "persistent": view(lay.persistent, i32t, (B, H, 1, C)) if C else None,
+            "local": view(lay.local, i32t, (B, H, nqb, K)) if K else None,
+            "local_base": int(lay.local_id_base),
+            "shared_indptr": view(lay.shared_indptr, i32t, (B * H + 1,)),
+            "shared_indices": view(lay.shared_indices, i32t, (B * H * (sink_count + C),)),
+            "local_indptr": view(lay.local_indptr, i32t, (B * H * nqb + 1,)),
+            "local_indices": view(lay.local_indices, i32t, (B * H * nqb * K,)),
+            "workspace": workspace}
+    return o, l, info

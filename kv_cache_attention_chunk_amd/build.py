@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libchunkattn.so")
-SOURCES = ["attn_fwd.hip", "select.hip", "merge.hip", "pack.hip", "mla.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "pbsa.hip", "select.hip", "merge.hip", "pack.hip", "mla.hip",
+           "api.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code (ordinary float

@@ -233,6 +233,39 @@ void fill_blocks(AttnParams& p, int Nq, int Nkv, const int32_t* indptr, const in
   p.nqb = num_blocks(Nq, q_block, q_seg);
 }
 
+// Launch arguments of the one-pass PBSA kernel (checked by the caller).
+PbsaParams pbsa_params(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv,
+                       const int64_t* qs, const int64_t* kvs, const int64_t* os,
+                       const int32_t* sh_ptr, const int32_t* sh_idx, int sh_nnz,
+                       const int32_t* lo_ptr, const int32_t* lo_idx, int lo_nnz, int kv_block,
+                       int kv_seg, int q_block, int q_seg, float scale, void* o, float* lse) {
+  PbsaParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.qs_b = qs[0]; p.qs_n = qs[1]; p.qs_h = qs[2];
+  p.ks_b = kvs[0]; p.ks_n = kvs[1]; p.ks_h = kvs[2];
+  p.os_b = os[0]; p.os_n = os[1]; p.os_h = os[2];
+  p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.sh_ptr = sh_ptr; p.sh_idx = sh_idx; p.sh_nnz = sh_nnz;
+  p.lo_ptr = lo_ptr; p.lo_idx = lo_idx; p.lo_nnz = lo_nnz;
+  p.kv_block = kv_block;
+  p.kv_seg = kv_seg;
+  p.kv_bps = (kv_seg + kv_block - 1) / kv_block;
+  p.kv_bps_magic = (uint32_t)((((uint64_t)1) << 32) / (uint64_t)p.kv_bps);
+  p.nkb = num_blocks(Nkv, kv_block, kv_seg);
+  p.q_block = q_block;
+  p.q_seg = q_seg;
+  p.q_bps = (q_seg + q_block - 1) / q_block;
+  p.nqb = num_blocks(Nq, q_block, q_seg);
+  p.groups = (p.nqb + 3) / 4;
+  p.n_items = B * H * p.groups;
+  return p;
+}
+
 std::vector<int> longest_first(const int32_t* cu_host, const std::vector<int>& heads) {
   std::vector<int> order = heads;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
@@ -323,6 +356,35 @@ int ca_chunk_attn_fwd(const void* q, const void* k, const void* v, int B, int H,
   const std::vector<int> tiles(Nkv > 0 ? B * H : 0, (Nkv + kTileKeys - 1) / kTileKeys);
   return launch_range(c, p, words, tiles, split, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream));
+}
+
+int ca_chunk_attn_pbsa_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq,
+                           int Nkv, int d, const int64_t* q_strides, const int64_t* kv_strides,
+                           const int64_t* o_strides, const int32_t* shared_indptr,
+                           const int32_t* shared_indices, int shared_nnz,
+                           const int32_t* local_indptr, const int32_t* local_indices,
+                           int local_nnz, int kv_block, int kv_seg, int q_block, int q_seg,
+                           float scale, void* o, int o_dtype, float* lse, void* stream) {
+  Common c{B, H, Nq, d, q, q_strides, o_strides, o, o_dtype, lse, scale};
+  if (int r = check_common(c)) return r;
+  if (Nkv < 0) return fail(CA_EINVAL, "Nkv < 0");
+  if (Nkv > 0 && (!k || !v)) return fail(CA_EINVAL, "k and v must be non-NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(CA_EINVAL, "k, v must be 16-byte aligned");
+  if (int r = check_strides("kv", kv_strides, 8)) return r;
+  if (kv_strides[1] < d || kv_strides[1] > (1 << 23)) return fail(CA_ERANGE, "kv row stride outside [d, 2^23]");
+  if (int r = check_csr(shared_indptr, shared_indices, shared_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+  if (int r = check_csr(local_indptr, local_indices, local_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+  if (q_block > 64) return fail(CA_ERANGE, "q_block %d above 64 (a query block is served by 64 rows)", q_block);
+  if (int r = check_device()) return r;
+  const int nqb = num_blocks(Nq, q_block, q_seg);
+  if ((int64_t)B * H * ((nqb + 3) / 4) > 0x7FFFFFFF) return fail(CA_ERANGE, "too many work items");
+  if ((int64_t)B * H * Nq == 0) return ok();
+  const PbsaParams p = pbsa_params(q, k, v, B, H, Nq, Nkv, q_strides, kv_strides, o_strides,
+                                   shared_indptr, shared_indices, shared_nnz, local_indptr,
+                                   local_indices, local_nnz, kv_block, kv_seg, q_block, q_seg,
+                                   scale, o, lse);
+  return launched(launch_pbsa(d, o_dtype == CA_F32, p, static_cast<hipStream_t>(stream)),
+                  "pbsa launch");
 }
 
 int ca_chunk_attn_dual_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq,
@@ -784,6 +846,231 @@ int ca_build_kv_index(int B, int H, int NQB, int sink_begin, int sink_count,
                                         C, NQB, K ? topk : nullptr, K, topk_offset, indptr, indices,
                                         static_cast<hipStream_t>(stream)),
                   "build_kv_index launch");
+}
+
+// ---- the block-sparse pipeline (Sparse Forcing page, section 2) -------------
+namespace {
+
+struct SparseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, H, Nq, Nkv, d;
+  const int64_t* qs;
+  const int64_t* kvs;
+  const int64_t* os;
+  int block, seg;
+  int sink_begin, sink_count, hist_begin, hist_count, C, local_begin, local_count, K;
+  const float* k_mean;
+  float scale;
+  void* o;
+  int o_dtype;
+  float* lse;
+};
+
+constexpr size_t kWsAlign = 256;
+
+size_t ws_take(size_t& at, size_t bytes) {
+  const size_t r = at;
+  at += (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
+  return r;
+}
+
+// Pointer and stride checks of the pipeline's tensors.
+int check_sparse_tensors(const SparseArgs& a) {
+  Common c{a.B, a.H, a.Nq, a.d, a.q, a.qs, a.os, a.o, a.o_dtype, a.lse, a.scale};
+  if (int r = check_common(c)) return r;
+  if (a.Nkv > 0 && (!a.k || !a.v)) return fail(CA_EINVAL, "k and v must be non-NULL");
+  if (!aligned16(a.k) || !aligned16(a.v) || !aligned16(a.k_mean))
+    return fail(CA_EINVAL, "k, v, k_mean must be 16-byte aligned");
+  if (int r = check_strides("kv", a.kvs, 8)) return r;
+  if (a.kvs[1] < a.d || a.kvs[1] > (1 << 23)) return fail(CA_ERANGE, "kv row stride outside [d, 2^23]");
+  return CA_OK;
+}
+
+// Checks the sizes and block ranges and lays out the intermediates in a
+// workspace (a.k_mean is only tested for NULL here).
+int plan_sparse(const SparseArgs& a, ca_block_sparse_ws& w) {
+  w = ca_block_sparse_ws{};
+  if (a.B < 0 || a.H < 0 || a.Nq < 0 || a.Nkv < 0) return fail(CA_EINVAL, "negative size");
+  if (a.d != 64 && a.d != 128) return fail(CA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", a.d);
+  if (a.block < 1 || a.block > 64) return fail(CA_ERANGE, "block %d outside 1..64", a.block);
+  if (a.seg < 1) return fail(CA_EINVAL, "seg < 1");
+  if ((int64_t)a.B * a.H > 65535) return fail(CA_ERANGE, "B*H above 65535");
+  const int nkb = num_blocks(a.Nkv, a.block, a.seg);
+  const int nqb = num_blocks(a.Nq, a.block, a.seg);
+  const int rng[3][2] = {{a.sink_begin, a.sink_count}, {a.hist_begin, a.hist_count},
+                         {a.local_begin, a.local_count}};
+  for (int i = 0; i < 3; ++i) {
+    if (rng[i][0] < 0 || rng[i][1] < 0 || (int64_t)rng[i][0] + rng[i][1] > nkb)
+      return fail(CA_ERANGE, "block range %d outside [0, %d)", i, nkb);
+    for (int j = 0; j < i; ++j)
+      if (rng[i][1] && rng[j][1] && rng[i][0] < rng[j][0] + rng[j][1] &&
+          rng[j][0] < rng[i][0] + rng[i][1])
+        return fail(CA_EINVAL, "sink, history and local block ranges must be disjoint");
+  }
+  if (a.C < 0 || a.C > a.hist_count || a.hist_count > 4096)
+    return fail(CA_ERANGE, "C=%d outside 0..hist_count (at most 4096 candidates)", a.C);
+  if (a.K < 0 || a.K > a.local_count || a.local_count > 4096)
+    return fail(CA_ERANGE, "K=%d outside 0..local_count (at most 4096 candidates)", a.K);
+  const int64_t BH = (int64_t)a.B * a.H;
+  if (BH * nqb > 65536) return fail(CA_ERANGE, "more than 65536 query blocks");
+  const int bps = (a.seg + a.block - 1) / a.block;
+  // local-window means over the window alone: the window starts on a segment
+  // boundary and its own tiling has exactly local_count blocks
+  int win_t0 = 0, win_n = 0;
+  bool window = false;
+  if (a.k_mean && a.K > 0 && a.local_begin % bps == 0) {
+    const int last = a.local_begin + a.local_count - 1;
+    win_t0 = (a.local_begin / bps) * a.seg;
+    const int t1 = std::min(a.Nkv, (last / bps) * a.seg + std::min(a.seg, (last % bps + 1) * a.block));
+    win_n = t1 - win_t0;
+    window = win_n > 0 && num_blocks(win_n, a.block, a.seg) == a.local_count;
+  }
+  const bool selects = a.C > 0 || a.K > 0;
+  const bool all_k = selects && (!a.k_mean || (a.K > 0 && !window));
+  size_t at = 0;
+  const size_t f = sizeof(float), i4 = sizeof(int32_t);
+  w.q_mean = ws_take(at, selects ? BH * nqb * a.d * f : 0);
+  w.k_mean = ws_take(at, all_k ? BH * nkb * a.d * f : 0);
+  w.k_mean_local = ws_take(at, window ? BH * a.local_count * a.d * f : 0);
+  w.chunk_mean = ws_take(at, BH * a.d * f);
+  w.persistent = ws_take(at, BH * std::max(a.C, 1) * i4);
+  w.local = ws_take(at, BH * nqb * std::max(a.K, 1) * i4);
+  w.shared_indptr = ws_take(at, (BH + 1) * i4);
+  w.shared_indices = ws_take(at, (BH * ((int64_t)a.sink_count + a.C) + 1) * i4);
+  w.local_indptr = ws_take(at, (BH * nqb + 1) * i4);
+  w.local_indices = ws_take(at, (BH * nqb * a.K + 1) * i4);
+  w.bytes = at;
+  w.window_means = window ? 1 : 0;
+  w.window_token0 = window ? win_t0 : 0;
+  w.window_tokens = window ? win_n : 0;
+  w.local_id_base = window ? a.local_begin : 0;
+  w.k_mean_in_ws = all_k ? 1 : 0;
+  return CA_OK;
+}
+
+// The pipeline on a planned workspace: block means (and the chunk mean),
+// persistent top-C and local top-K with their block lists, then one PBSA
+// launch.  Every intermediate is written before it is read.
+int run_sparse(const SparseArgs& a, const ca_block_sparse_ws& w, char* ws, hipStream_t s) {
+  if (int r = check_device()) return r;
+  if ((int64_t)a.B * a.H * a.Nq == 0) return ok();
+  const int BH = a.B * a.H;
+  const int nkb = num_blocks(a.Nkv, a.block, a.seg);
+  const int nqb = num_blocks(a.Nq, a.block, a.seg);
+  const int bps = (a.seg + a.block - 1) / a.block;
+  float* qm = reinterpret_cast<float*>(ws + w.q_mean);
+  float* km_ws = reinterpret_cast<float*>(ws + w.k_mean);
+  float* km_win = reinterpret_cast<float*>(ws + w.k_mean_local);
+  float* cm = reinterpret_cast<float*>(ws + w.chunk_mean);
+  int32_t* pers = reinterpret_cast<int32_t*>(ws + w.persistent);
+  int32_t* loc = reinterpret_cast<int32_t*>(ws + w.local);
+  int32_t* sh_ptr = reinterpret_cast<int32_t*>(ws + w.shared_indptr);
+  int32_t* sh_idx = reinterpret_cast<int32_t*>(ws + w.shared_indices);
+  int32_t* lo_ptr = reinterpret_cast<int32_t*>(ws + w.local_indptr);
+  int32_t* lo_idx = reinterpret_cast<int32_t*>(ws + w.local_indices);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  float* cm_out = a.C > 0 ? cm : nullptr;
+  hipError_t e = hipSuccess;
+
+  // 1. block representatives: the query blocks (and the chunk mean), the
+  //    local window's key blocks (or every key block)
+  if (a.C > 0 || a.K > 0) {
+    if (w.window_means && w.window_tokens == a.Nq) {
+      // the window holds as many tokens as the chunk: one launch for both
+      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, cm_out, s,
+                            k + (int64_t)w.window_token0 * a.kvs[1], a.kvs, km_win);
+    } else {
+      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, cm_out, s);
+      if (e == hipSuccess && w.window_means)
+        e = launch_block_mean(k + (int64_t)w.window_token0 * a.kvs[1], a.B, w.window_tokens, a.H,
+                              a.d, a.kvs, a.block, a.seg, bps, a.local_count, km_win, nullptr, s);
+      if (e == hipSuccess && w.k_mean_in_ws)
+        e = launch_block_mean(k, a.B, a.Nkv, a.H, a.d, a.kvs, a.block, a.seg, bps, nkb, km_ws,
+                              nullptr, s);
+    }
+    if (e != hipSuccess) return launched(e, "block mean launch");
+  }
+
+  // 2. selections, writing the block lists where each row is a prefix range
+  //    followed by the selected ids
+  const float* km_hist = a.k_mean ? a.k_mean : km_ws;
+  const bool fused_shared = a.C > 0 && a.sink_begin + a.sink_count <= a.hist_begin;
+  TopkJobDesc jobs[2];
+  int nj = 0;
+  if (a.C > 0)
+    jobs[nj++] = TopkJobDesc{cm, km_hist, a.B, a.H, 1, nkb, a.d, a.hist_begin, a.hist_count, a.C,
+                             a.sink_begin, a.sink_count, 0, pers, nullptr,
+                             fused_shared ? sh_ptr : nullptr, fused_shared ? sh_idx : nullptr};
+  if (a.K > 0) {
+    const float* km_loc = w.window_means ? km_win : km_ws;
+    const int nkb_loc = w.window_means ? a.local_count : nkb;
+    const int cand0 = w.window_means ? 0 : a.local_begin;
+    jobs[nj++] = TopkJobDesc{qm, km_loc, a.B, a.H, nqb, nkb_loc, a.d, cand0, a.local_count, a.K,
+                             0, 0, w.local_id_base, loc, nullptr, lo_ptr, lo_idx};
+  }
+  if (nj > 0) {
+    e = launch_score_topk_batch(jobs, nj, s);
+    if (e != hipSuccess) return launched(e, "selection launch");
+  }
+  if (!fused_shared) {
+    // sink range above the history, or no persistent blocks: a general merge
+    e = launch_build_kv_index(BH, a.sink_begin, a.sink_count, a.C > 0 ? pers : nullptr, a.C, 1,
+                              nullptr, 0, 0, sh_ptr, sh_idx, s);
+    if (e != hipSuccess) return launched(e, "block list launch");
+  }
+  if (a.K == 0) {
+    e = launch_build_kv_index(BH * nqb, 0, 0, nullptr, 0, nqb, nullptr, 0, 0, lo_ptr, lo_idx, s);
+    if (e != hipSuccess) return launched(e, "block list launch");
+  }
+
+  // 3. attention over the union of each query block's two lists
+  const PbsaParams p = pbsa_params(a.q, a.k, a.v, a.B, a.H, a.Nq, a.Nkv, a.qs, a.kvs, a.os, sh_ptr,
+                                   sh_idx, BH * (a.sink_count + a.C), lo_ptr, lo_idx,
+                                   BH * nqb * a.K, a.block, a.seg, a.block, a.seg, a.scale, a.o,
+                                   a.lse);
+  return launched(launch_pbsa(a.d, a.o_dtype == CA_F32, p, s), "pbsa launch");
+}
+
+}  // namespace
+
+size_t ca_block_sparse_workspace(int B, int H, int Nq, int Nkv, int d, int block, int seg,
+                                 int sink_begin, int sink_count, int hist_begin, int hist_count,
+                                 int C, int local_begin, int local_count, int K, int have_k_mean,
+                                 ca_block_sparse_ws* layout) {
+  static const int64_t dummy[3] = {0, 0, 0};
+  const SparseArgs a{nullptr, nullptr, nullptr, B, H, Nq, Nkv, d, dummy, dummy, dummy, block, seg,
+                     sink_begin, sink_count, hist_begin, hist_count, C, local_begin, local_count,
+                     K, have_k_mean ? reinterpret_cast<const float*>(kWsAlign) : nullptr, 1.f,
+                     nullptr, CA_BF16, nullptr};
+  ca_block_sparse_ws w;
+  if (plan_sparse(a, w) != CA_OK) return 0;
+  if (layout) *layout = w;
+  ok();
+  return w.bytes;
+}
+
+int ca_block_sparse_fwd(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv,
+                        int d, const int64_t* q_strides, const int64_t* kv_strides,
+                        const int64_t* o_strides, int block, int seg, int sink_begin,
+                        int sink_count, int hist_begin, int hist_count, int C, int local_begin,
+                        int local_count, int K, const float* k_mean, float scale, void* o,
+                        int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const SparseArgs a{q, k, v, B, H, Nq, Nkv, d, q_strides, kv_strides, o_strides, block, seg,
+                     sink_begin, sink_count, hist_begin, hist_count, C, local_begin, local_count,
+                     K, k_mean, scale, o, o_dtype, lse};
+  if (int r = check_sparse_tensors(a)) return r;
+  ca_block_sparse_ws w;
+  if (int r = plan_sparse(a, w)) return r;
+  if (!workspace || !aligned16(workspace)) return fail(CA_EINVAL, "workspace must be non-NULL and 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign)
+    return fail(CA_EINVAL, "workspace must be %zu-byte aligned", kWsAlign);
+  if (workspace_bytes < w.bytes)
+    return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, w.bytes);
+  return run_sparse(a, w, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -85,6 +85,33 @@ struct AttnParams {
   uint16_t heads[kMaxHeadsPerLaunch];
 };
 
+// Kernel arguments of the one-pass PBSA kernel (pbsa.hip): query block qb of
+// head bh = b*H + h attends to the blocks of shared CSR row bh and of local
+// CSR row bh * nqb + qb; one workgroup per four query blocks of a head.
+struct PbsaParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  int64_t qs_b, qs_n, qs_h;
+  int64_t ks_b, ks_n, ks_h;
+  int64_t os_b, os_n, os_h;
+  int B, H, Nq, Nkv;
+  float scale_log2;           // softmax scale * log2(e)
+  const int32_t* sh_ptr;      // shared lists: row bh
+  const int32_t* sh_idx;
+  int sh_nnz;
+  const int32_t* lo_ptr;      // local lists: row bh * nqb + qb
+  const int32_t* lo_idx;
+  int lo_nnz;
+  int kv_block, kv_seg, kv_bps, nkb;
+  uint32_t kv_bps_magic;      // floor(2^32 / kv_bps)
+  int q_block, q_seg, q_bps, nqb;
+  int groups;                 // workgroups per head: ceil(nqb / 4)
+  int n_items;                // B * H * groups
+};
+
 // First unit of workgroup g under the balanced schedule, and the workgroup
 // that owns unit u (exact integer forms: g_of_unit(u) = g iff
 // unit_begin(g) <= u < unit_begin(g + 1), for 1 <= n_wgs <= n_units).
@@ -98,6 +125,8 @@ __host__ __device__ __forceinline__ int g_of_unit(int u, int n_units, int n_wgs)
 // Launchers implemented in attn_fwd.hip / select.hip / merge.hip.
 hipError_t launch_attention(int mode, int d, int nwaves, bool out_f32,
                             const AttnParams& p, hipStream_t stream);
+// The one-pass PBSA kernel (pbsa.hip), d = 64 or 128.
+hipError_t launch_pbsa(int d, bool out_f32, const PbsaParams& p, hipStream_t stream);
 // Combines the float32 partials of the query tiles the balanced schedule
 // split across workgroups (runs after launch_attention on the same stream).
 hipError_t launch_split_merge(int d, bool out_f32, const AttnParams& p, hipStream_t stream);

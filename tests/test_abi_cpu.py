@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 22
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -75,6 +75,62 @@ def test_attention_argument_errors(L):
     assert fwd(L, split=3) == CA_EINVAL                          # unknown split policy
     fwd(L, d=96)
     assert b"head dim 96" in L.ca_last_error()
+
+
+def pbsa(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=12, Nq=4680, Nkv=32760, d=128, qs=S, kvs=S, os=S,
+             sp=FAKE, si=FAKE, sn=684, lp=FAKE, li=FAKE, ln=9000, kb=64, ks=1560, qb=64,
+             qseg=1560, scale=0.088, o=FAKE, odt=0, lse=FAKE, stream=None)
+    a.update(kw)
+    return L.ca_chunk_attn_pbsa_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["Nq"], a["Nkv"],
+                                    a["d"], a["qs"], a["kvs"], a["os"], a["sp"], a["si"], a["sn"],
+                                    a["lp"], a["li"], a["ln"], a["kb"], a["ks"], a["qb"],
+                                    a["qseg"], a["scale"], a["o"], a["odt"], a["lse"],
+                                    a["stream"])
+
+
+def test_pbsa_argument_errors(L):
+    assert pbsa(L, sp=None) == CA_EINVAL                 # shared list missing
+    assert pbsa(L, li=None) == CA_EINVAL                 # local indices missing
+    assert pbsa(L, qb=65) == CA_ERANGE                   # a query block above 64 rows
+    assert b"q_block" in L.ca_last_error()
+    assert pbsa(L, kb=65) == CA_ERANGE
+    assert pbsa(L, ln=-1) == CA_EINVAL
+    assert pbsa(L, d=80) == CA_EUNSUPPORTED
+    assert pbsa(L, k=FAKE + 4) == CA_EINVAL
+    assert pbsa(L, scale=0.0) == CA_EINVAL
+
+
+def test_block_sparse_workspace_layout(L):
+    """Workspace sizes and offsets of the block-sparse pipeline at the Wan
+    shape: query-block means, window means (resident history means) or every
+    key block's means, ids and lists, each 256-byte aligned and disjoint."""
+    ws = _lib.BlockSparseWs()
+    args = (1, 12, 4680, 32760, 128, 64, 1560, 0, 25, 25, 425, 32, 450, 75, 10)
+    n = L.ca_block_sparse_workspace(*args, 1, ctypes.byref(ws))
+    assert n == ws.bytes > 0
+    assert ws.window_means == 1 and ws.window_token0 == 18 * 1560 and ws.window_tokens == 4680
+    assert ws.local_id_base == 450 and ws.k_mean_in_ws == 0
+    offs = [ws.q_mean, ws.k_mean_local, ws.chunk_mean, ws.persistent, ws.local,
+            ws.shared_indptr, ws.shared_indices, ws.local_indptr, ws.local_indices]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert ws.k_mean_local - ws.q_mean >= 12 * 75 * 128 * 4
+    assert ws.bytes < (2 << 20)                    # about 1 MB at this shape
+    ws2 = _lib.BlockSparseWs()
+    n2 = L.ca_block_sparse_workspace(*args, 0, ctypes.byref(ws2))
+    assert ws2.k_mean_in_ws == 1 and ws2.window_means == 0 and ws2.local_id_base == 0
+    assert n2 - n >= 12 * 525 * 128 * 4 - 12 * 75 * 128 * 4
+    # overlapping ranges, K above the window, block above 64: rejected
+    bad = list(args)
+    bad[10] = 430                                  # history overlaps the local window
+    assert L.ca_block_sparse_workspace(*bad, 1, None) == 0
+    assert b"disjoint" in L.ca_last_error()
+    bad = list(args)
+    bad[14] = 76
+    assert L.ca_block_sparse_workspace(*bad, 1, None) == 0
+    bad = list(args)
+    bad[5] = 65
+    assert L.ca_block_sparse_workspace(*bad, 1, None) == 0
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="a GPU is visible")
