@@ -246,6 +246,28 @@ int ca_block_sparse_fwd(const void* q, const void* k, const void* v, int B, int 
                         void* stream);
 
 /*
+ * ca_block_sparse_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results, without the workspace: the
+ * intermediates live in a device array the library holds, CA_SCRATCH_BYTES
+ * (16 MiB) per GPU, for the lifetime of the process (about 1 MB suffices for
+ * the 12-head Wan layer with resident key means, 4.3 MB without).  Sizes
+ * whose ca_block_sparse_workspace exceeds it return CA_ERANGE.  No call
+ * allocates or frees anything.  Every call on one GPU uses the same array:
+ * calls that overlap on a GPU (different streams, or host threads) race and
+ * must be ordered by the caller; every intermediate is rewritten by each call
+ * before it is read, so nothing carries over between calls.
+ */
+#define CA_SCRATCH_BYTES ((size_t)16 << 20)
+int ca_block_sparse_fwd_noalloc(const void* q, const void* k, const void* v, int B, int H, int Nq,
+                                int Nkv, int d, const int64_t* q_strides,
+                                const int64_t* kv_strides, const int64_t* o_strides, int block,
+                                int seg, int sink_begin, int sink_count, int hist_begin,
+                                int hist_count, int C, int local_begin, int local_count, int K,
+                                const float* k_mean, float scale, void* o, int o_dtype,
+                                float* lse, void* stream);
+
+/*
  * Dual-output chunk attention (ISPA page, section 2 item 1: the dual-stream
  * warmup computes attention over the local tokens — the current frames and
  * the sink — and over the full history side by side).  Block-list mode as in

@@ -17,6 +17,7 @@ CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
 CA_BF16, CA_F32 = 0, 1
 CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
 CA_SPLIT_AUTO, CA_SPLIT_NEVER, CA_SPLIT_ALWAYS = 0, 1, 2
+CA_SCRATCH_BYTES = 16 << 20     # device scratch of ca_block_sparse_fwd_noalloc, per GPU
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -46,6 +47,9 @@ SIGNATURES = {
     "ca_block_sparse_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p, _i, _i,
                                  _i, _i, _i, _i, _i, _i, _i, _i, _p, _f, _p, _i, _p, _p, _sz,
                                  _p]),
+    "ca_block_sparse_fwd_noalloc": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
+                                         _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _f, _p, _i,
+                                         _p, _p]),
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
                                       _i64p, _i64, _i64p, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -1034,6 +1035,35 @@ int run_sparse(const SparseArgs& a, const ca_block_sparse_ws& w, char* ws, hipSt
   return launched(launch_pbsa(a.d, a.o_dtype == CA_F32, p, s), "pbsa launch");
 }
 
+// Device scratch of the allocation-free pipeline (one copy per GPU, held
+// until the process ends).  Host code never passes the array's name to a
+// kernel: it is a host-side stand-in, and the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = CA_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+char* scratch_ptr(int& status) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    status = fail(CA_ENODEV, "no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      status = fail(CA_EHIP, "scratch address: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  status = CA_OK;
+  return static_cast<char*>(ptrs[dev]);
+}
+
 }  // namespace
 
 size_t ca_block_sparse_workspace(int B, int H, int Nq, int Nkv, int d, int block, int seg,
@@ -1071,6 +1101,29 @@ int ca_block_sparse_fwd(const void* q, const void* k, const void* v, int B, int 
   if (workspace_bytes < w.bytes)
     return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, w.bytes);
   return run_sparse(a, w, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int ca_block_sparse_fwd_noalloc(const void* q, const void* k, const void* v, int B, int H, int Nq,
+                                int Nkv, int d, const int64_t* q_strides,
+                                const int64_t* kv_strides, const int64_t* o_strides, int block,
+                                int seg, int sink_begin, int sink_count, int hist_begin,
+                                int hist_count, int C, int local_begin, int local_count, int K,
+                                const float* k_mean, float scale, void* o, int o_dtype,
+                                float* lse, void* stream) {
+  const SparseArgs a{q, k, v, B, H, Nq, Nkv, d, q_strides, kv_strides, o_strides, block, seg,
+                     sink_begin, sink_count, hist_begin, hist_count, C, local_begin, local_count,
+                     K, k_mean, scale, o, o_dtype, lse};
+  if (int r = check_sparse_tensors(a)) return r;
+  ca_block_sparse_ws w;
+  if (int r = plan_sparse(a, w)) return r;
+  if (w.bytes > kScratchBytes)
+    return fail(CA_ERANGE, "the pipeline needs %zu bytes of scratch; the library holds %zu",
+                w.bytes, kScratchBytes);
+  if (int r = check_device()) return r;
+  int st = CA_OK;
+  char* ws = scratch_ptr(st);
+  if (!ws) return st;
+  return run_sparse(a, w, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

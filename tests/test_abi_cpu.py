@@ -21,10 +21,17 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_header_constants_match_the_binding():
+    text = open(_lib.HEADER).read()
+    assert f"#define CA_ABI_VERSION {_lib.ABI_VERSION}" in text
+    assert "#define CA_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert _lib.CA_SCRATCH_BYTES == 16 << 20
 
 
 def test_status_strings_and_version(L):
