@@ -18,7 +18,17 @@ One step = one pass over every step of the path on that batch:
 `value` is the step's algorithmic attention FLOPs (4 d per query-key score
 over every key set attended) divided by the step time.  The roofline entry
 is the dense attention kernel (the dominant kernel), timed with HIP events on
-the launch stream over the timed steps.  Prints one JSON line.
+the launch stream over the timed steps, against the datasheet peak and
+against the peaks measured here (an MFMA-loop probe, a large GEMM).
+
+After the step, every other workload is timed on its own (warm, and cold
+over rotating input copies), and its outputs at sampled query rows are
+kept.  The CPU leg then times the float64 oracle on the full dense layer
+(the baseline's value), compares every element of the step's dense output
+with it, and recomputes each kept sample: max |dO|, max |dLSE|, elements
+that needed the relaxed bf16 bound, and for the block-sparse workloads the
+top-K rows that differ from the oracle's selection and its near-tie rows.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -37,7 +47,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ATTN_SRC = os.path.join(ROOT, "kv_cache_attention_chunk_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "kv_cache_attention_chunk_amd", "csrc")
+ATTN_SRC = [os.path.join(CSRC, f) for f in ("attn_fwd.hip", "attn_tile.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_dense_wan_counters.json")
 
 
@@ -45,15 +56,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash() -> str:
-    """Hash of the attention kernel's code: attn_fwd.hip with // comments,
-    surrounding whitespace and blank lines removed, so that counters stay
-    attached to the code they were taken on and not to its comments."""
+def src_hash(paths=None) -> str:
+    """Hash of a kernel's code (by default the dense attention kernel:
+    attn_fwd.hip and its tile loop attn_tile.h) with // comments, surrounding
+    whitespace and blank lines removed, so that counters stay attached to the
+    code they were taken on and not to its comments."""
     lines = []
-    for line in open(ATTN_SRC, encoding="utf-8").read().splitlines():
-        code = line.split("//", 1)[0].strip()
-        if code:
-            lines.append(code)
+    for path in paths or ATTN_SRC:
+        for line in open(path, encoding="utf-8").read().splitlines():
+            code = line.split("//", 1)[0].strip()
+            if code:
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
@@ -85,36 +98,217 @@ def effective_schedule(ca, q, k, v, scale, policy):
     return "unknown"
 
 
-def cpu_baseline(w):
-    """Time the CPU oracle, as it stands, on a bounded sample of the same
-    workload: the full dense layer (all 12 heads, all 4680 query rows vs
-    32760 keys) plus the oracle's local and history branches and their LSE
-    merge over the first 1560 query rows (one latent frame).  Returns the
-    baseline record with the achieved algorithmic TFLOP/s."""
-    import numpy as np
-    import oracle
+def _cpu_info():
+    """The host CPU model, the threads the oracle's numpy BLAS runs with,
+    and which BLAS library that is."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads, blas = len(os.sched_getaffinity(0)), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            threads = max(int(i.get("num_threads", 1)) for i in libs)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return model, threads, blas
+
+
+def _o_stats(og, o_ref, bf16_out):
+    """max |dO| and, against the O bar (1e-2; for a bf16 output from
+    |O_ref| = 2 on 1e-2 plus the output's half-ulp), the elements that
+    needed the relaxed bound and those beyond any bound."""
+    og = np.asarray(og, np.float64)
+    err = np.abs(og - o_ref)
+    ax = np.abs(o_ref)
+    hu = np.where(ax > 0, 2.0 ** (np.floor(np.log2(np.where(ax > 0, ax, 1.0))) - 8), 0.0)
+    bound = np.where(bf16_out & (ax >= 2.0), 1e-2 + hu, 1e-2)
+    return {"max_abs_dO": float(np.nanmax(err)) if err.size else 0.0,
+            "o_elements": int(err.size),
+            "o_relaxed_bound": int(np.sum((err > 1e-2) & (err <= bound))),
+            "o_over_bar": int(np.sum(~(err <= bound)))}
+
+
+def _lse_stats(lg, l_ref):
+    """max |dLSE| over finite entries, entries beyond 1e-3, and whether the
+    -inf entries (empty key sets) coincide."""
+    lg = np.asarray(lg, np.float64)
+    fin = np.isfinite(l_ref)
+    err = np.abs(lg[fin] - l_ref[fin])
+    return {"max_abs_dLSE": float(np.nanmax(err)) if err.size else 0.0,
+            "lse_over_bar": int(np.sum(~(err <= 1e-3))),
+            "lse_neginf_match": bool(np.array_equal(np.isneginf(lg), np.isneginf(l_ref)))}
+
+
+def _topk_stats(ig, ref, eps=1e-4):
+    """Selected-id rows that differ from the oracle's; those whose differing
+    ids are not explained by a near-tie (the K-th/(K+1)-th score gap below
+    eps, the set holding every candidate above the tie band and nothing
+    below it); and the oracle's near-tie rows."""
+    ig = np.asarray(ig)
+    diff = np.any(ig != ref["idx"], axis=-1)
+    unexplained = 0
+    for pos in zip(*np.nonzero(diff)):
+        ok = bool(ref["gap"][pos] < eps)
+        if ok:
+            score_of = {int(c): float(x) for c, x in zip(ref["cand"][pos], ref["cand_score"][pos])
+                        if c >= 0}
+            kth = float(ref["kth"][pos])
+            got = [int(x) for x in ig[pos] if x >= 0]
+            must = {c for c, x in score_of.items() if x > kth + eps}
+            ok = must <= set(got) and all(c in score_of and score_of[c] >= kth - eps for c in got)
+        unexplained += not ok
+    return {"rows": int(diff.size), "rows_differing": int(diff.sum()),
+            "rows_differing_outside_tie_band": int(unexplained),
+            "near_tie_rows": int(np.sum(ref["gap"] < eps))}
+
+
+def _oracle_for(oracle, spec, rows):
+    """The oracle's O and LSE at `rows` for a probe's workload, and what it
+    decided on the way (block selections), as the pages define them."""
+    kind, extra = spec["kind"], {}
+    if kind in ("dense", "merge", "local", "sparse"):
+        w = spec["w"]
+        Q, K, V = w.q.f32, w.k.f32, w.v.f32
+    if kind == "dense":
+        O, L = oracle.chunk_attn_dense(Q, K, V, w.scale, rows=rows)
+    elif kind in ("merge", "local"):
+        spans = oracle.block_spans(w.Nkv, 64, spec.get("seg", 1560))
+        br = []
+        for key in ("local_blocks", "history_blocks")[:1 if kind == "local" else 2]:
+            tok = oracle.block_tokens(spans, w.meta[key])
+            br.append(oracle.chunk_attn_dense(Q[:, rows], K[:, tok], V[:, tok], w.scale))
+        O, L = br[0] if kind == "local" else oracle.lse_merge_bshd(br[0][0], br[0][1],
+                                                                     br[1][0], br[1][1])
+    elif kind == "sparse":
+        sel = oracle.sparse_selection(Q, K, 64, 1560, 64, 1560, spec["lay"])
+        extra["sel"] = sel
+        O, L = oracle.chunk_attn_blocks(Q, K, V, sel["indptr"], sel["indices"], 64, 1560, 64,
+                                        1560, w.scale, rows=rows)
+    elif kind == "varlen":
+        w = spec["w"]
+        O, L = oracle.chunk_attn_varlen(w.q.f32, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens,
+                                        w.scale, rows=rows)
+    elif kind == "mixed":
+        w, lay, hs = spec["w"], spec["lay"], spec["sparse_heads"]
+        Q, K, V = w.q.f32, w.k.f32, w.v.f32
+        sel = oracle.sparse_selection(Q[:, :, hs], K[:, :, hs], 64, 1560, 64, 1560, lay)
+        extra["sel"] = sel
+        O = np.zeros((w.B, len(rows), w.H, w.d))
+        L = np.zeros((w.B, w.H, len(rows)))
+        for mode in range(3):
+            heads = [h for h in range(w.H) if w.head_mode[h] == mode]
+            if mode == 0:
+                o, l = oracle.chunk_attn_dense(Q, K, V, w.scale, rows=rows, heads=heads)
+            elif mode == 1:
+                o, l = oracle.chunk_attn_blocks(Q[:, :, hs], K[:, :, hs], V[:, :, hs],
+                                                sel["indptr"], sel["indices"], 64, 1560, 64,
+                                                1560, w.scale, rows=rows)
+            else:
+                o, l = oracle.chunk_attn_varlen(Q, w.k_flat.f32, w.v_flat.f32, w.cu_seqlens,
+                                                w.scale, rows=rows, heads=heads)
+            O[:, :, heads], L[:, heads] = o, l
+    else:
+        raise ValueError(kind)
+    return O, L, extra
+
+
+def cpu_baseline(w, dense_o=None, dense_l=None, probes=None):
+    """The CPU oracle, as it stands, on a bounded sample of the workload,
+    timed on this host, and its comparison with the GPU outputs.
+
+    `value`: the full dense Wan layer (12 heads, all 4680 query rows vs 32760
+    keys) in float64 numpy, as algorithmic TFLOP/s; with the step's dense
+    output (dense_o, dense_l) every one of its elements is compared.  Then,
+    per probe the GPU leg stored: the oracle's time, max |dO| and max |dLSE|
+    at the sampled rows with the elements that needed the relaxed bf16 bound
+    and those beyond any bound, and for the block-sparse workloads the
+    top-K rows that differ from the oracle's selection and its near-tie rows
+    (ties within 1e-4 of the K-th score)."""
+    import oracle
+    model, threads, blas = _cpu_info()
     Q, K, V = w.q.f32, w.k.f32, w.v.f32
     oracle.chunk_attn_dense(Q, K, V, w.scale, rows=np.arange(8), heads=[0])    # warm-up
     t0 = time.perf_counter()
-    oracle.chunk_attn_dense(Q, K, V, w.scale)
-    rows = np.arange(1560)
-    tok = {key: oracle.block_tokens(oracle.block_spans(w.Nkv, 64, 1560), w.meta[key])
-           for key in ("local_blocks", "history_blocks")}
-    br = [oracle.chunk_attn_dense(Q[:, rows], K[:, tok[key]], V[:, tok[key]], w.scale)
-          for key in ("local_blocks", "history_blocks")]
-    oracle.lse_merge_bshd(br[0][0], br[0][1], br[1][0], br[1][1])
+    O, L = oracle.chunk_attn_dense(Q, K, V, w.scale)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.d * w.H * (w.Nq + len(rows)) * w.Nkv
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    flops = 4.0 * w.d * w.H * w.Nq * w.Nkv
+    per = {}
+    if dense_o is not None:
+        per["wan_dense_whole_layer"] = {"oracle_ms": round(dt * 1e3, 1), "rows": int(w.Nq),
+                                        **_o_stats(dense_o, O, True), **_lse_stats(dense_l, L)}
+    del O, L
+    t_all = dt
+    for name, pr in (probes or {}).items():
+        spec = pr["spec"]
+        t0 = time.perf_counter()
+        rec = {}
+        if spec["kind"] == "pack":
+            ww = spec["w"]
+            frames = [ww.ragged_frames[bh] for bh in range(ww.B * ww.H)]
+            ptr = np.zeros(len(frames) + 1, np.int64)
+            src = []
+            for bh, fl in enumerate(frames):
+                for fr in fl:
+                    src.append((int(fr[0]), int(fr[1])) if isinstance(fr, (tuple, list))
+                               else (int(fr), -1))
+                ptr[bh + 1] = len(src)
+            rk, rv, rcu = oracle.pack_ragged(ww.k.bits, ww.v.bits, ptr,
+                                             np.array(src, np.int64).reshape(-1, 2), 1560)
+            rec = {"elements": int(rk.size + rv.size),
+                   "elements_differing": int(np.sum(rk != pr["k"]) + np.sum(rv != pr["v"])),
+                   "cu_seqlens_equal": bool(np.array_equal(rcu, pr["cu"]))}
+        elif spec["kind"] == "persistent":
+            ww, lay = spec["w"], spec["lay"]
+            qm = oracle.chunk_mean_query(ww.q.f32).astype(np.float32)
+            km = oracle.block_mean(ww.k.f32, 64, 1560).astype(np.float32)
+            pers = oracle.block_score_topk(qm, km, lay["hist_begin"], lay["hist_count"], lay["C"])
+            ref = oracle.persistent_update(qm, km, pers["idx"][:, :, 0, :], lay["local_begin"],
+                                           lay["local_count"], lay["C"])
+            rec = {"topk": _topk_stats(pr["ids"], ref)}
+        elif spec["kind"] == "mla":
+            m = spec["m"]
+            kv = m["kv_lat"].f32
+            o_err, l_err = [], []
+            for h, r in spec["rows_by_head"].items():
+                Or, Lr = oracle.mla_chunk_attn(m["q"].f32, kv[..., :192], kv[..., 192:],
+                                               m["w_uk"].f32, m["w_uv"].f32, m["scale"],
+                                               rows=r, heads=[h])
+                o_err.append(_o_stats(pr["o"][h], Or, True))
+                l_err.append(_lse_stats(pr["lse"][h], Lr))
+            rec = {"rows": int(sum(len(r) for r in spec["rows_by_head"].values())),
+                   "max_abs_dO": max(x["max_abs_dO"] for x in o_err),
+                   "o_elements": sum(x["o_elements"] for x in o_err),
+                   "o_relaxed_bound": sum(x["o_relaxed_bound"] for x in o_err),
+                   "o_over_bar": sum(x["o_over_bar"] for x in o_err),
+                   "max_abs_dLSE": max(x["max_abs_dLSE"] for x in l_err),
+                   "lse_over_bar": sum(x["lse_over_bar"] for x in l_err),
+                   "lse_neginf_match": all(x["lse_neginf_match"] for x in l_err)}
+        else:
+            O, L, extra = _oracle_for(oracle, spec, pr["rows"])
+            rec = {"rows": int(len(pr["rows"])), **_o_stats(pr["o"], O, pr["bf16_out"]),
+                   **_lse_stats(pr["lse"], L)}
+            if "sel" in extra:
+                sel = extra["sel"]
+                rec["topk_persistent"] = _topk_stats(pr["persistent"], sel["persistent"])
+                rec["topk_local"] = _topk_stats(pr["local"], sel["local"])
+        dt_p = time.perf_counter() - t0
+        t_all += dt_p
+        per[name] = {"oracle_ms": round(dt_p * 1e3, 1), **rec}
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"full dense layer ({w.H} heads x {w.Nq} queries x {w.Nkv} keys) + "
-                      f"local/history branches and LSE merge for the first {len(rows)} queries, "
-                      f"float64 numpy oracle, {dt:.1f} s"}
+            "sample": f"full dense layer ({w.H} heads x {w.Nq} queries x {w.Nkv} keys), "
+                      f"float64 numpy oracle, {dt:.1f} s; then the per-workload parity "
+                      f"samples ({t_all - dt:.1f} s)",
+            "cpu_model": model, "blas": blas, "oracle_s_total": round(t_all, 1),
+            "parity": per}
 
 
 class _Timing(float):
@@ -171,8 +365,34 @@ def _time_calls(torch, fn, reps=20, warmup_s=0.2):
 
 
 def measured_roofs(torch):
-    """Roofs measured on this GPU: a large bf16 GEMM (torch.matmul, 8192^3,
-    contiguous operands) and a 1 GiB device-to-device copy."""
+    """Roofs measured on this GPU: the bf16 matrix-core peak from an
+    MFMA-loop probe (four independent v_mfma_f32_32x32x16_bf16 chains per
+    wave, 16 waves per CU, held for about 0.5 s so that the clock settles
+    under load), the HBM read bandwidth from a streaming-read probe over
+    4 GiB, and for reference a large bf16 GEMM (torch.matmul, 8192^3) and a
+    1 GiB device-to-device copy."""
+    import ctypes
+    roofs_lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_attention_chunk_amd",
+                                         "libchunkattn_roofs.so"))
+    roofs_lib.ca_roof_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    roofs_lib.ca_roof_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(1 << 20, device="cuda", dtype=torch.float32)
+    grid, iters = 1024, 20000
+    flop = grid * 4 * iters * 4 * 32768.0
+    mfma = lambda: roofs_lib.ca_roof_mfma(grid, iters, sink.data_ptr(), stream)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        mfma()
+        torch.cuda.synchronize()
+    ms_m = _time_ms(torch, mfma, 20, warmup_s=0.0, spread=False)
+    n_read = 4 << 30
+    x = torch.empty(n_read // 2, device="cuda", dtype=torch.bfloat16)
+    read = lambda: roofs_lib.ca_roof_read(x.data_ptr(), n_read, 8192, sink.data_ptr(), stream)
+    ms_r = _time_ms(torch, read, 20, spread=False)
+    del x
     a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
@@ -183,9 +403,51 @@ def measured_roofs(torch):
     y = torch.empty_like(x)
     ms_c = _time_ms(torch, lambda: y.copy_(x), 20, spread=False)
     del x, y
-    return {"bf16_gemm_tflops": round(2.0 * 8192 ** 3 / (ms_g * 1e-3) / 1e12, 1),
+    return {"mfma_loop_tflops": round(flop / (ms_m * 1e-3) / 1e12, 1),
+            "hbm_read_GBs": round(n_read / (ms_r * 1e-3) / 1e9, 1),
+            "bf16_gemm_tflops": round(2.0 * 8192 ** 3 / (ms_g * 1e-3) / 1e12, 1),
             "copy_GBs": round(2.0 * (1 << 30) / (ms_c * 1e-3) / 1e9, 1),
+            "mfma_loop": "4 chains of v_mfma_f32_32x32x16_bf16 per wave, 1024 x 4 waves, "
+                         "after 0.5 s under load",
+            "hbm_read": "4 GiB streamed once, 16-byte coalesced loads",
             "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB read + 1 GiB written"}
+
+
+def _sample_rows(Nq, block=None, seg=None, seed=0):
+    """Query rows for the parity samples: one random row in every 32-row
+    slice of the 256-row query tiles (every wave of every dense / ragged
+    workgroup) and, with a query-block tiling, in every 32-row slice of
+    every query block (block-list workgroups), plus the first and last."""
+    rng = np.random.default_rng(seed)
+    rows = {0, Nq - 1}
+    for s0 in range(0, Nq, 32):
+        rows.add(int(rng.integers(s0, min(s0 + 32, Nq))))
+    if block:
+        bps = -(-seg // block)
+        for j in range(-(-Nq // seg) * bps):
+            f, r = divmod(j, bps)
+            s0 = f * seg + r * block
+            ln = min(block, seg - r * block, Nq - s0)
+            for o in range(0, max(ln, 0), 32):
+                rows.add(int(rng.integers(s0 + o, s0 + min(o + 32, ln))))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _probe(o, lse, rows, spec, bf16_out=True, **extra):
+    """GPU outputs O [B, R, H, d] and LSE [B, H, R] at the sampled rows R,
+    kept with the workload description `spec` for the CPU leg's comparison
+    (extra: the block ids the GPU selected, as host arrays)."""
+    d = {"rows": rows, "o": o[:, rows].float().cpu().numpy(), "lse": lse[:, :, rows].cpu().numpy(),
+         "spec": spec, "bf16_out": bf16_out}
+    d.update(extra)
+    return d
+
+
+def _time_cold(torch, fn_of_set, n_sets, reps=30):
+    """Median and minimum of single calls that rotate over n_sets input
+    copies, so that no call finds its K/V in the Infinity Cache or L2."""
+    t = _time_calls(torch, lambda i=0: fn_of_set(i % n_sets), reps)
+    return round(float(np.median(t)), 4), round(float(t.min()), 4)
 
 
 def _block_len(ids, block=64, seg=1560):
@@ -207,12 +469,49 @@ def _rec(ms, flops, kv_bytes, **extra):
     return r
 
 
-def per_config(reps=10, wan=None, names=None):
-    """Time every configured workload once on the GPU (inputs resident):
-    tiny dense + merge, Wan dense + merge, block-sparse at three top-K ratios,
-    ragged 12-head, mixed 40-head.  FLOPs are algorithmic (4 d per score of
-    every key set attended); kv bytes are the distinct K/V bytes the call
-    must read.  `names` restricts the run to those entries (for per-workload
+def _cold_sets(touched_bytes):
+    """Input copies a cold timing rotates over: enough that the other copies'
+    K/V bytes read between two uses of one copy exceed twice the 256 MB
+    Infinity Cache (at least 3 copies, at most 12)."""
+    return int(min(12, max(3, 1 + math.ceil(2 * 256e6 / max(touched_bytes, 1.0)))))
+
+
+def _add_cold(torch, rec, flops, call, n_sets, reps=30):
+    """Cold timing of call(i) (i = the input copy) added to a record."""
+    med, mn = _time_cold(torch, call, n_sets, reps)
+    rec.update(cold_ms_median=med, cold_ms_min=mn, cold_sets=n_sets,
+               cold_tflops_median=round(flops / (med * 1e-3) / 1e12, 1))
+
+
+def counters(name, sources):
+    """A workload's committed rocprofv3 counter summary
+    (profiles/<name>_counters.json) if it was taken on the current code of
+    `sources` (paths under csrc/); else None."""
+    try:
+        c = json.load(open(os.path.join(ROOT, "profiles", f"{name}_counters.json")))
+    except (OSError, ValueError):
+        return None
+    if c.get("code_sha256_16") != src_hash([os.path.join(CSRC, s) for s in sources]):
+        return None
+    return c
+
+
+SPARSE_SOURCES = ("pbsa.hip", "attn_tile.h", "select.hip", "api.hip")
+
+
+def per_config(reps=10, wan=None, names=None, probes=None):
+    """Time every configured workload on the GPU (inputs resident): tiny dense
+    + merge, Wan dense / merge / dual output, block-sparse at three top-K
+    ratios, persistent update, ragged, ragged packing, latent-KV (MLA),
+    mixed 40-head.  FLOPs are algorithmic (4 d per score of every key set
+    attended); kv bytes are the distinct K/V bytes the call must read.
+    Attention workloads also get a cold timing over rotating input copies
+    (no K/V left in the Infinity Cache or L2 from the call before).
+
+    With `probes` (a dict), each workload's outputs at sampled query rows
+    (every wave slice of every workgroup), its selected block ids and what
+    an oracle needs to recompute them are stored there, for the CPU leg to
+    compare.  `names` restricts the run to those entries (for per-workload
     counter collection); their inputs are still built."""
     import torch
     import kv_cache_attention_chunk_amd as ca
@@ -220,18 +519,17 @@ def per_config(reps=10, wan=None, names=None):
     want = lambda n: names is None or n in names
     dev = lambda t: torch.from_numpy(t.bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    probes = {} if probes is None else probes
     out = {}
 
-    def merged_fn(q, k, v, w, seg):
+    def merged_fn(q, k, v, w, seg, om, lm):
         br = []
         for key in ("local_blocks", "history_blocks"):
             blocks = np.array(w.meta[key], np.int32)
             BH = w.B * w.H
             br.append((i32(np.arange(BH + 1) * len(blocks)), i32(np.tile(blocks, BH)),
-                       torch.empty((w.B, w.Nq, w.H, w.d), dtype=torch.float32, device="cuda"),
-                       torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")))
-        om = torch.empty_like(q)
-        lm = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+                       f32(w.B, w.Nq, w.H, w.d), f32(w.B, w.H, w.Nq)))
 
         def fn():
             for ip, ix, ob, lb in br:
@@ -245,62 +543,82 @@ def per_config(reps=10, wan=None, names=None):
     w = wl.tiny_dense(seed=0)
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
     f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
-    kvb = 2.0 * w.Nkv * w.H * w.d * 2
     if want("tiny_dense"):
-        ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps)
-        ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv), reps)
+        od, ld = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        om, lm = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=od, lse=ld),
+                        reps)
+        ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv, om, lm), reps)
         out["tiny_dense"] = {"dense_us": round(ms_d * 1e3, 1),
-                             "local_history_merge_us": round(ms_m * 1e3, 1), "gflop": round(f / 1e9, 3)}
-    # Wan-1.3B layer: dense and local/history merge
+                             "local_history_merge_us": round(ms_m * 1e3, 1),
+                             "gflop": round(f / 1e9, 3)}
+        rows = np.arange(w.Nq)
+        probes["tiny_dense"] = _probe(od, ld, rows, {"kind": "dense", "w": w})
+        probes["tiny_merge"] = _probe(om, lm, rows, {"kind": "merge", "w": w, "seg": w.Nkv})
+
+    # Wan-1.3B layer: dense, local/history merge, dual output
     w = wan or wl.wan_dense(seed=0)
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
-    f = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
+    f_dense = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
     kvb = 2.0 * w.Nkv * w.H * w.d * 2
+    rows = _sample_rows(w.Nq, 64, 1560, seed=1)
+    ms_dense = None
     if want("wan_dense"):
-        out["wan_dense"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale), reps),
-                                f, kvb)
-    # per-call spread, warm (one K/V set, resident in the 256 MB Infinity
-    # Cache) and cold (three K/V copies in rotation: 603 MB, more than the
-    # Infinity Cache and L2 hold, so each call reads its K/V from HBM)
-    if want("wan_dense"):
-        o_w = torch.empty_like(q)
-        l_w = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-        warm = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_w, lse=l_w),
-                           30)
-        sets = [(k, v), (k.clone(), v.clone()), (k.clone(), v.clone())]
-        cold = _time_calls(torch, lambda i=0: ca.chunk_attn_fwd(
-            q, sets[i % 3][0], sets[i % 3][1], scale=w.scale, out=o_w, lse=l_w), 30)
+        o_w, l_w = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        rec = _rec(_time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=o_w,
+                                                             lse=l_w), reps), f_dense, kvb)
+        n = _cold_sets(kvb)
+        sets = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n - 1)]
+        _add_cold(torch, rec, f_dense, lambda i=0: ca.chunk_attn_fwd(
+            q, sets[i][0], sets[i][1], scale=w.scale, out=o_w, lse=l_w), n)
         del sets
-        for name, t in (("warm", warm), ("cold", cold)):
-            out["wan_dense"][f"{name}_ms_median"] = round(float(np.median(t)), 4)
-            out["wan_dense"][f"{name}_ms_min"] = round(float(t.min()), 4)
-        out["wan_dense"]["cold_tflops_median"] = round(f / (float(np.median(cold)) * 1e-3) / 1e12, 1)
-        out["wan_dense"]["cold_kv_GBs_median"] = round(kvb / (float(np.median(cold)) * 1e-3) / 1e9, 1)
+        out["wan_dense"] = rec
+        ms_dense = rec["ms"]
     if want("wan_merge_variant"):
-        out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560), reps), f, kvb)
+        om, lm = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        out["wan_merge_variant"] = _rec(_time_ms(torch, merged_fn(q, k, v, w, 1560, om, lm), reps),
+                                        f_dense, kvb)
+        probes["wan_merge_variant"] = _probe(om, lm, rows, {"kind": "merge", "w": w, "seg": 1560})
     # local (sink + chunk frames) and full attention from one pass over each head's list
     row = np.array(w.meta["local_blocks"] + w.meta["history_blocks"], np.int32)
     dip, dix = i32(np.arange(w.B * w.H + 1) * len(row)), i32(np.tile(row, w.B * w.H))
     n_loc = len(w.meta["local_blocks"])
     f_loc = 4.0 * w.d * w.Nq * w.B * w.H * float(_block_len(w.meta["local_blocks"]).sum())
     if want("wan_dual_output"):
+        ol, ll = f32(w.B, w.Nq, w.H, w.d), f32(w.B, w.H, w.Nq)
+        of, lf = f32(w.B, w.Nq, w.H, w.d), f32(w.B, w.H, w.Nq)
         out["wan_dual_output"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_dual_fwd(
             q, k, v, dip, dix, n_loc, kv_block=64, kv_seg=1560, q_block=w.Nq, q_seg=w.Nq,
-            scale=w.scale, out_dtype=torch.float32), reps), f, kvb,
+            scale=w.scale, out_local=ol, lse_local=ll, out=of, lse=lf), reps), f_dense, kvb,
             local_gflop_shared=round(f_loc / 1e9, 2))
+        probes["wan_dual_full"] = _probe(of, lf, rows, {"kind": "dense", "w": w}, bf16_out=False)
+        probes["wan_dual_local"] = _probe(ol, ll, rows, {"kind": "local", "w": w},
+                                          bf16_out=False)
+
     # block-sparse path at the three top-K ratios (selection included)
     km = ca.block_mean(k, 64, 1560)
     nqb = ca.num_blocks(w.Nq, 64, 1560)
     qlen = np.tile(_block_len(np.arange(nqb)), w.B * w.H)
+    cnt = counters("block_sparse_wan", SPARSE_SOURCES)
     for ratio in (0.25, 0.125, 0.0625):
         lay = wl.sparse_layout(w, ratio)
-        if not want(f"sparse_K{lay['K']}"):
+        name = f"sparse_K{lay['K']}"
+        if not want(name):
             continue
-        fn = lambda: ca.block_sparse_fwd(
-            q, k, v, sink_begin=0, sink_count=lay["sink_count"], hist_begin=lay["hist_begin"],
-            hist_count=lay["hist_count"], C=lay["C"], local_begin=lay["local_begin"],
-            local_count=lay["local_count"], K=lay["K"], block=64, seg=1560, k_mean=km,
-            scale=w.scale)
+        o_s, l_s = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        args = dict(sink_begin=0, sink_count=lay["sink_count"], hist_begin=lay["hist_begin"],
+                    hist_count=lay["hist_count"], C=lay["C"], local_begin=lay["local_begin"],
+                    local_count=lay["local_count"], K=lay["K"], block=64, seg=1560, k_mean=km,
+                    scale=w.scale)
+        ws = torch.empty(ca.block_sparse_workspace(w.B, w.H, w.Nq, w.Nkv, w.d, block=64,
+                                                   seg=1560, have_k_mean=True,
+                                                   **{a: args[a] for a in (
+                                                       "sink_begin", "sink_count", "hist_begin",
+                                                       "hist_count", "C", "local_begin",
+                                                       "local_count", "K")}).bytes,
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda kk=k, vv=v: ca.block_sparse_fwd(q, kk, vv, out=o_s, lse=l_s, workspace=ws,
+                                                    **args)
         _, _, info = fn()
         torch.cuda.synchronize()
         sp, sx = info["shared_indptr"].cpu().numpy(), info["shared_indices"].cpu().numpy()
@@ -310,12 +628,41 @@ def per_config(reps=10, wan=None, names=None):
         f = 4.0 * w.d * (float(sh.sum()) * w.Nq + float((lo * qlen).sum()))
         uniq = sum(_block_len(np.union1d(sx[sp[h]:sp[h + 1]], lx[lp[h * nqb]:lp[(h + 1) * nqb]])).sum()
                    for h in range(w.B * w.H))
-        kvb = 2.0 * float(uniq) * w.d * 2
+        kvb_s = 2.0 * float(uniq) * w.d * 2
+        # bytes the PBSA kernel streams from L2 into LDS: each workgroup (four
+        # query blocks of a head) reads its head's shared list once, and each
+        # query block its own local list
+        groups = -(-nqb // 4)
+        gathered = 2.0 * w.d * 2 * (groups * float(sh.sum()) + float(lo.sum()))
         ms = _time_ms(torch, fn, reps)
-        # dense-equivalent rate: the dense layer's FLOPs over the sparse path's time
-        f_dense = 4.0 * w.d * w.Nq * w.Nkv * w.B * w.H
-        out[f"sparse_K{lay['K']}"] = _rec(ms, f, kvb, ratio=ratio,
-                                          dense_equiv_tflops=round(f_dense / (ms * 1e-3) / 1e12, 1))
+        # PBSA alone, on the lists the path built
+        o_p, l_p = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        lists = [info[x].clone() for x in ("shared_indptr", "shared_indices", "local_indptr",
+                                          "local_indices")]
+        ms_p = _time_ms(torch, lambda: ca.chunk_attn_pbsa_fwd(
+            q, k, v, *lists, kv_block=64, kv_seg=1560, q_block=64, q_seg=1560, scale=w.scale,
+            out=o_p, lse=l_p), reps)
+        rec = _rec(ms, f, kvb_s, ratio=ratio, K=lay["K"], C=lay["C"],
+                   pbsa_ms=round(ms_p, 4), selection_ms=round(ms - ms_p, 4),
+                   pbsa_tflops=round(f / (ms_p * 1e-3) / 1e12, 1),
+                   gathered_MB=round(gathered / 1e6, 2),
+                   gathered_GBs_pbsa=round(gathered / (ms_p * 1e-3) / 1e9, 1))
+        if ms_dense is not None:
+            rec["speedup_vs_dense"] = round(ms_dense / ms, 2)
+        n = _cold_sets(kvb_s)
+        sets = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n - 1)]
+        _add_cold(torch, rec, f, lambda i=0: fn(*sets[i]), n)
+        del sets
+        if cnt is not None and name in cnt.get("per_workload", {}):
+            c = cnt["per_workload"][name]
+            rec["rocprof"] = {"l2_fill_read_MB": c["read_MB"], "write_MB": c["write_MB"],
+                              "pbsa_read_MB": c["pbsa_read_MB"],
+                              "pbsa_read_over_gathered": round(c["pbsa_read_MB"] * 1e6 / gathered, 3)}
+        out[name] = rec
+        probes[name] = _probe(o_s, l_s, rows, {"kind": "sparse", "w": w, "lay": lay},
+                              persistent=info["persistent"].cpu().numpy(),
+                              local=(info["local"] + info["local_base"]).cpu().numpy())
+        del ws, o_p, l_p, lists
     # persistent-memory update when the window slides: the chunk's 75 local
     # blocks are evicted into the candidates of each head's 32 persistent blocks
     lay = wl.sparse_layout(w, 0.125)
@@ -323,11 +670,15 @@ def per_config(reps=10, wan=None, names=None):
     pers = ca.block_score_topk(cm, km, lay["C"], cand_begin=lay["hist_begin"],
                                cand_count=lay["hist_count"])[:, :, 0, :].contiguous()
     if want("persistent_update"):
+        pn = torch.empty_like(pers)
         ms = _time_ms(torch, lambda: ca.persistent_update(cm, km, pers, lay["local_begin"],
-                                                          lay["local_count"], lay["C"]), reps)
+                                                          lay["local_count"], lay["C"], out=pn),
+                      reps)
         out["persistent_update"] = {"us": round(ms * 1e3, 1), "us_median": round(ms.median * 1e3, 1),
                                     "us_min": round(ms.minimum * 1e3, 1), "candidates_per_head":
                                     lay["C"] + lay["local_count"], "C": lay["C"], "heads": w.H}
+        probes["persistent_update"] = {"spec": {"kind": "persistent", "w": w, "lay": lay},
+                                       "ids": pn.cpu().numpy()}
     del q, k, v, km
     # ragged per-head caches
     w = wl.ragged(seed=0)
@@ -336,20 +687,35 @@ def per_config(reps=10, wan=None, names=None):
     f = 4.0 * w.d * w.Nq * tot
     kvb = 2.0 * tot * w.d * 2
     if want("ragged"):
-        out["ragged"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_varlen_fwd(
-            q, kf, vf, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
-            sum_len=tot, lengths_frames=w.meta["n_frames"])
+        o_r, l_r = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        call = lambda i=0, kk=kf, vv=vf: ca.chunk_attn_varlen_fwd(
+            q, kk, vv, cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale, out=o_r, lse=l_r)
+        rec = _rec(_time_ms(torch, call, reps), f, kvb, sum_len=tot,
+                   lengths_frames=w.meta["n_frames"])
+        n = _cold_sets(kvb)
+        sets = [(kf, vf)] + [(kf.clone(), vf.clone()) for _ in range(n - 1)]
+        _add_cold(torch, rec, f, lambda i=0: call(0, *sets[i]), n)
+        del sets
+        out["ragged"] = rec
+        probes["ragged"] = _probe(o_r, l_r, _sample_rows(w.Nq, seed=3), {"kind": "varlen", "w": w})
     # packing those ragged caches from the dense per-head cache (HBM-bound:
     # every packed K/V row read once and written once)
     kd, vd = dev(w.k), dev(w.v)
     plan = ca.pack_plan([w.ragged_frames[bh] for bh in range(w.B * w.H)], kd.device)
     if want("ragged_pack"):
-        ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, plan, 1560), reps)
+        pk, pv = torch.empty_like(kf), torch.empty_like(vf)
+        pcu = torch.empty_like(cu)
+        ms = _time_ms(torch, lambda: ca.pack_ragged(kd, vd, plan, 1560, out_k=pk, out_v=pv,
+                                                    out_cu=pcu), reps)
         moved = 2.0 * 2.0 * tot * w.d * 2
         out["ragged_pack"] = {"us": round(ms * 1e3, 1), "us_median": round(ms.median * 1e3, 1),
                               "us_min": round(ms.minimum * 1e3, 1), "bytes_moved_MB": round(moved / 1e6, 1),
                               "GBs": round(moved / (ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        probes["ragged_pack"] = {"spec": {"kind": "pack", "w": w},
+                                 "k": pk.view(torch.int16).cpu().numpy().view(np.uint16),
+                                 "v": pv.view(torch.int16).cpu().numpy().view(np.uint16),
+                                 "cu": pcu.cpu().numpy()}
     del q, kf, vf, kd, vd
     # latent KV cache (d_c = 192, d_rope = 32): absorbed query, latent
     # attention, per-head up-projection
@@ -357,16 +723,33 @@ def per_config(reps=10, wan=None, names=None):
     mq, mwk, mwv = dev(m["q"]), dev(m["w_uk"]), dev(m["w_uv"])
     mkv = ca.cast_bf16_to_f16(dev(m["kv_lat"]))
     if want("wan_mla"):
-        ms_all = _time_ms(torch, lambda: ca.mla_chunk_attn(mq, mkv, mwk, mwv, scale=m["scale"]), reps)
-        rows = m["Nq"] * m["H"]
-        f_att = 2.0 * rows * m["Nkv"] * (224 + 192)
-        f_proj = 2.0 * rows * (96 * 192 + 192 * 128)
+        o_m, l_m = torch.empty_like(mq), f32(1, m["H"], m["Nq"])
+        o_lat = f32(1, m["Nq"], m["H"], 192)
+        ms_all = _time_ms(torch, lambda: ca.mla_chunk_attn(mq, mkv, mwk, mwv, scale=m["scale"],
+                                                           out=o_m, lse=l_m, o_lat=o_lat), reps)
+        rows_m = m["Nq"] * m["H"]
+        f_att = 2.0 * rows_m * m["Nkv"] * (224 + 192)
+        f_proj = 2.0 * rows_m * (96 * 192 + 192 * 128)
         kvb = m["Nkv"] * 224 * 2.0
         out["wan_mla"] = _rec(ms_all, f_att + f_proj, kvb, attention_gflop=round(f_att / 1e9, 1),
                               projection_gflop=round(f_proj / 1e9, 1),
                               kv_bytes_vs_dense=round(kvb / (2.0 * m["Nkv"] * m["H"] * 128 * 2), 4))
+        # one (query, head) row of every 32-row wave slice of the flattened
+        # (query, head) rows the latent kernel tiles
+        rng = np.random.default_rng(6)
+        flat = [int(rng.integers(s, min(s + 32, rows_m))) for s in range(0, rows_m, 32)]
+        by_head = {}
+        for r in flat:
+            by_head.setdefault(r % m["H"], set()).add(r // m["H"])
+        og, lg = o_m.float().cpu().numpy(), l_m.cpu().numpy()
+        sel = {h: np.array(sorted(rs)) for h, rs in by_head.items()}
+        probes["wan_mla"] = {"spec": {"kind": "mla", "m": m, "rows_by_head": sel},
+                             "o": {h: og[:, r, h:h + 1] for h, r in sel.items()},
+                             "lse": {h: lg[:, h:h + 1, r] for h, r in sel.items()},
+                             "bf16_out": True}
     del mq, mwk, mwv, mkv
-    # mixed 40-head layer (dense / block lists / ragged per head)
+    # mixed 40-head layer (dense / block lists / ragged per head); the
+    # block-sparse heads' lists come from the selection calls on those heads
     w = wl.mixed(seed=0)
     lay = w.meta["sparse"]
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
@@ -378,6 +761,7 @@ def per_config(reps=10, wan=None, names=None):
     loc = ca.block_score_topk(qm, kms, lay["K"], cand_begin=lay["local_begin"], cand_count=lay["local_count"])
     ip_s, ix_s = ca.build_kv_index(1, len(hs), nqb, 0, lay["sink_count"], pers[:, :, 0, :].contiguous(), loc, 0)
     ip_s, ix_s = ip_s.cpu().numpy(), ix_s.cpu().numpy()
+    sel_gpu = {"persistent": pers.cpu().numpy(), "local": loc.cpu().numpy()}
     del qs, ks
     lists, f, kvb = [], 0.0, 0.0
     for h in range(w.H):
@@ -404,11 +788,22 @@ def per_config(reps=10, wan=None, names=None):
     ip = i32(ip)
     kf, vf, cu = dev(w.k_flat), dev(w.v_flat), i32(w.cu_seqlens)
     if want("mixed_40h"):
-        out["mixed_40h"] = _rec(_time_ms(torch, lambda: ca.chunk_attn_mixed_fwd(
-            q, w.head_mode, k=k, v=v, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
-            q_block=64, q_seg=1560, k_flat=kf, v_flat=vf, cu_seqlens=cu,
-            cu_seqlens_host=w.cu_seqlens, scale=w.scale), reps), f, kvb,
-            heads_dense_sparse_ragged=[int((w.head_mode == m).sum()) for m in range(3)])
+        o_x, l_x = torch.empty_like(q), f32(w.B, w.H, w.Nq)
+        call = lambda i=0, kk=k, vv=v, kkf=kf, vvf=vf: ca.chunk_attn_mixed_fwd(
+            q, w.head_mode, k=kk, v=vv, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
+            q_block=64, q_seg=1560, k_flat=kkf, v_flat=vvf, cu_seqlens=cu,
+            cu_seqlens_host=w.cu_seqlens, scale=w.scale, out=o_x, lse=l_x)
+        rec = _rec(_time_ms(torch, call, reps), f, kvb,
+                   heads_dense_sparse_ragged=[int((w.head_mode == mm).sum()) for mm in range(3)])
+        n = _cold_sets(kvb)
+        sets = [(k, v, kf, vf)] + [(k.clone(), v.clone(), kf.clone(), vf.clone())
+                                   for _ in range(n - 1)]
+        _add_cold(torch, rec, f, lambda i=0: call(0, *sets[i]), n)
+        del sets
+        out["mixed_40h"] = rec
+        probes["mixed_40h"] = _probe(o_x, l_x, _sample_rows(w.Nq, 64, 1560, seed=4),
+                                     {"kind": "mixed", "w": w, "lay": lay, "sparse_heads": hs},
+                                     **sel_gpu)
     return out
 
 
@@ -506,12 +901,19 @@ def main():
 
     k_mean_resident = ca.block_mean(k, 64, 1560)
 
+    sparse_ranges = {key: lay[key] for key in ("sink_begin", "sink_count", "hist_begin",
+                                               "hist_count", "C", "local_begin", "local_count",
+                                               "K")}
+    sparse_ws = torch.empty(ca.block_sparse_workspace(B, H, Nq, Nkv, d, block=64, seg=1560,
+                                                      have_k_mean=True, **sparse_ranges).bytes,
+                            dtype=torch.uint8, device="cuda")
+    o_sparse = torch.empty_like(q)
+    l_sparse = torch.empty_like(l_dense)
+
     def sparse():
-        return ca.block_sparse_fwd(q, k, v, sink_begin=0, sink_count=lay["sink_count"],
-                                   hist_begin=lay["hist_begin"], hist_count=lay["hist_count"],
-                                   C=lay["C"], local_begin=lay["local_begin"],
-                                   local_count=lay["local_count"], K=lay["K"], block=64,
-                                   seg=1560, k_mean=k_mean_resident, scale=w.scale)
+        return ca.block_sparse_fwd(q, k, v, block=64, seg=1560, k_mean=k_mean_resident,
+                                   scale=w.scale, out=o_sparse, lse=l_sparse,
+                                   workspace=sparse_ws, **sparse_ranges)
 
     # algorithmic FLOPs: 4 d per (query, key) score of every key set attended
     f_dense = 4.0 * d * Nq * Nkv * B * H
@@ -583,6 +985,9 @@ def main():
         res["sparse_path_ms"] = sum(e[2].elapsed_time(e[3]) for e in ev) / n
     log(f"timed {n} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / n:.3f}), {res}")
 
+    # the step's dense output, all of it, for the CPU leg's comparison
+    dense_host = (o_dense.float().cpu().numpy(), l_dense.cpu().numpy())
+    probes = {}
     achieved = f_dense / (t_dense * 1e-3) / 1e12
     kv_bytes = 2.0 * Nkv * H * d * 2 * B
     traffic = traffic_from_counters()
@@ -619,14 +1024,15 @@ def main():
         out["phase_tflops"]["sparse_path"] = round(f_sparse / (res["sparse_path_ms"] * 1e-3) / 1e12, 1)
     if args.only == "step" and not args.no_configs:
         t0 = time.perf_counter()
-        out["configs"] = per_config(wan=w)
+        out["configs"] = per_config(wan=w, probes=probes)
         roofs = measured_roofs(torch)
         out["measured_roofs"] = roofs
+        out["roofline"]["frac_of_measured_mfma"] = round(achieved / roofs["mfma_loop_tflops"], 4)
         out["roofline"]["frac_of_measured_gemm"] = round(achieved / roofs["bf16_gemm_tflops"], 4)
         log(f"per-workload timings in {time.perf_counter() - t0:.1f} s")
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, dense_host[0], dense_host[1], probes)
         log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
     else:
         out["cpu_baseline"] = None

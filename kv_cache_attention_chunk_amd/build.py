@@ -16,6 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libchunkattn.so")
+# roof probes timed by the benchmark (bf16 MFMA peak, HBM read), kept out of
+# the chunk-attention library
+ROOFS_SRC = "roofs.hip"
+ROOFS_LIB = os.path.join(PKG, "libchunkattn_roofs.so")
 SOURCES = ["attn_fwd.hip", "pbsa.hip", "select.hip", "merge.hip", "pack.hip", "mla.hip",
            "api.hip"]
 ARCH = "gfx950"
@@ -43,19 +47,27 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every HIP source and link libchunkattn.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every HIP source and link libchunkattn.so (and the
+    benchmark's roof probes, libchunkattn_roofs.so); returns the main
+    library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [ROOFS_SRC]
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], ROOFS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {ROOFS_LIB}")
     return LIB
 
 
