@@ -38,6 +38,7 @@ constexpr int kMlaDR = 32;                // position key
 constexpr int kMlaDK = kMlaDC + kMlaDR;   // 224 cached values per token
 constexpr int kMlaRowB = 512;             // LDS bytes per latent row (448 used)
 constexpr int kMlaNW = 8;                 // 256 rows per workgroup, one per CU
+constexpr int kMlaQLds = 2;               // Q^T fragments per wave kept in LDS
 constexpr float kLn2f = 0.6931471805599453f;
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
@@ -97,6 +98,12 @@ void mla_attn_kernel(const MlaParams p) {
   static_assert(NLD >= 1 && NLD * 1024 * kMlaNW == kMlaStageB, "the loads must fill a stage");
   static_assert(NST == 14 && NDT == 6, "the segment plan below is laid out for 224 / 192");
   __shared__ __attribute__((aligned(1024))) char lat[kMlaStages * kMlaStageB];
+  // the last NQL Q^T fragments (the position part q^R) of each wave, read
+  // back from LDS in the segments that use them, when the score and P
+  // registers of the step are already free: kept in registers for the whole
+  // loop they would push it past 256 VGPRs into scratch spills
+  constexpr int NQR = NST - kMlaQLds;
+  __shared__ __attribute__((aligned(16))) char qx[kMlaNW * kMlaQLds * 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,13 +119,19 @@ void mla_attn_kernel(const MlaParams p) {
   const int64_t rglob = (int64_t)b * p.rows_per_b + rloc;
 
   // Q^T operands: row rloc, values 16 st + 8 hg .. + 8
-  f16x8_t qreg[NST];
+  f16x8_t qreg[NQR];
+  char* const qxw = qx + (wave * kMlaQLds * 64 + lane) * 16;   // this lane's fragments
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
     u32x4_t x = {0u, 0u, 0u, 0u};
     if (qvalid) x = *reinterpret_cast<const u32x4_t*>(p.q + rglob * kMlaDK + 16 * st + 8 * hg);
-    qreg[st] = __builtin_bit_cast(f16x8_t, x);
+    if (st < NQR)
+      qreg[st] = __builtin_bit_cast(f16x8_t, x);
+    else
+      *reinterpret_cast<u32x4_t*>(qxw + (st - NQR) * 1024) = x;
   }
+  // (each lane reads back only what it wrote: no barrier needed)
+  auto qlds = [&](int st) { return *reinterpret_cast<const f16x8_t*>(qxw + (st - NQR) * 1024); };
 
   // Loads of half-tile u into stage u % 4: lane i of wave w's instruction j
   // fills physical row pr = 2 (NLD w + j) + i / 32 of the stage, slot i % 32,
@@ -225,9 +238,10 @@ void mla_attn_kernel(const MlaParams p) {
     }
     const float m_use = m == -INFINITY ? 0.f : m;
 
-    f16x8_t kr[2], v0[2], v1[2];
+    f16x8_t kr[2], v0[2], v1[2], qf[2];
     auto fetch = [&](int s1) {
       if (s1 < NST) kr[s1 & 1] = kfrag(ks, s1);
+      if (s1 >= NQR && s1 < NST) qf[s1 & 1] = qlds(s1);
       if (s1 >= 4 && s1 < 10) v0[s1 & 1] = vfrag(vs, 0, s1 - 4);
       if (s1 >= 8 && s1 < 14) v1[s1 & 1] = vfrag(vs, 1, s1 - 8);
     };
@@ -250,7 +264,8 @@ void mla_attn_kernel(const MlaParams p) {
       }
       if (s >= 4 && s < 10) acc[s - 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0[s & 1], pb0, acc[s - 4], 0, 0, 0);
       if (s >= 8) acc[s - 8] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1[s & 1], pb1, acc[s - 8], 0, 0, 0);
-      nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[s & 1], qreg[s], nx, 0, 0, 0);
+      nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[s & 1], s < NQR ? qreg[s] : qf[s & 1], nx,
+                                                  0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     rawmax = -INFINITY;
@@ -278,7 +293,8 @@ void mla_attn_kernel(const MlaParams p) {
     f32x16_t sa = f32x16_t{}, sb;
 #pragma unroll
     for (int st = 0; st < NST; ++st)
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag(0, st), qreg[st], sa, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag(0, st), st < NQR ? qreg[st] : qlds(st),
+                                                  sa, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, sa[i]);
     for (int u = 0; u < nh; u += kMlaStages) {
