@@ -368,7 +368,9 @@ def measured_roofs(torch):
     """Roofs measured on this GPU: the bf16 matrix-core peak from an
     MFMA-loop probe (four independent v_mfma_f32_32x32x16_bf16 chains per
     wave, 16 waves per CU, held for about 0.5 s so that the clock settles
-    under load), the HBM read bandwidth from a streaming-read probe over
+    under load), the MFMA rate of the attention tile loop's instruction mix
+    with nothing else in the way (its ceiling on this chip), the HBM read
+    bandwidth from a streaming-read probe over
     4 GiB, and for reference a large bf16 GEMM (torch.matmul, 8192^3) and a
     1 GiB device-to-device copy."""
     import ctypes
@@ -378,6 +380,8 @@ def measured_roofs(torch):
                                        ctypes.c_void_p]
     roofs_lib.ca_roof_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    roofs_lib.ca_roof_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     sink = torch.empty(1 << 20, device="cuda", dtype=torch.float32)
     grid, iters = 1024, 20000
@@ -388,6 +392,10 @@ def measured_roofs(torch):
         mfma()
         torch.cuda.synchronize()
     ms_m = _time_ms(torch, mfma, 20, warmup_s=0.0, spread=False)
+    grid_x, iters_x = 512, 20000
+    flop_x = grid_x * 4 * iters_x * 4 * 32768.0
+    mix = lambda: roofs_lib.ca_roof_mix(grid_x, iters_x, sink.data_ptr(), stream)
+    ms_x = _time_ms(torch, mix, 20, warmup_s=0.3, spread=False)
     n_read = 4 << 30
     x = torch.empty(n_read // 2, device="cuda", dtype=torch.bfloat16)
     read = lambda: roofs_lib.ca_roof_read(x.data_ptr(), n_read, 8192, sink.data_ptr(), stream)
@@ -404,11 +412,15 @@ def measured_roofs(torch):
     ms_c = _time_ms(torch, lambda: y.copy_(x), 20, spread=False)
     del x, y
     return {"mfma_loop_tflops": round(flop / (ms_m * 1e-3) / 1e12, 1),
+            "tile_mix_tflops": round(flop_x / (ms_x * 1e-3) / 1e12, 1),
             "hbm_read_GBs": round(n_read / (ms_r * 1e-3) / 1e9, 1),
             "bf16_gemm_tflops": round(2.0 * 8192 ** 3 / (ms_g * 1e-3) / 1e12, 1),
             "copy_GBs": round(2.0 * (1 << 30) / (ms_c * 1e-3) / 1e9, 1),
             "mfma_loop": "4 chains of v_mfma_f32_32x32x16_bf16 per wave, 1024 x 4 waves, "
                          "after 0.5 s under load",
+            "tile_mix": "the attention tile loop's per-MFMA mix (LDS operand reads incl. "
+                        "transposing ones, exp2, FMA, add, max, bf16 pack) without memory "
+                        "traffic, barriers or dependencies, 2 waves per SIMD",
             "hbm_read": "4 GiB streamed once, 16-byte coalesced loads",
             "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB read + 1 GiB written"}
 
@@ -1028,6 +1040,7 @@ def main():
         roofs = measured_roofs(torch)
         out["measured_roofs"] = roofs
         out["roofline"]["frac_of_measured_mfma"] = round(achieved / roofs["mfma_loop_tflops"], 4)
+        out["roofline"]["frac_of_tile_mix"] = round(achieved / roofs["tile_mix_tflops"], 4)
         out["roofline"]["frac_of_measured_gemm"] = round(achieved / roofs["bf16_gemm_tflops"], 4)
         log(f"per-workload timings in {time.perf_counter() - t0:.1f} s")
     if not args.no_cpu_baseline:

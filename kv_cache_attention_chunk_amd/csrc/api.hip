@@ -973,18 +973,18 @@ int run_sparse(const SparseArgs& a, const ca_block_sparse_ws& w, char* ws, hipSt
   int32_t* lo_idx = reinterpret_cast<int32_t*>(ws + w.local_indices);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
-  float* cm_out = a.C > 0 ? cm : nullptr;
   hipError_t e = hipSuccess;
 
-  // 1. block representatives: the query blocks (and the chunk mean), the
-  //    local window's key blocks (or every key block)
+  // 1. block representatives: the query blocks, the local window's key
+  //    blocks (or every key block); the chunk mean is formed from the query
+  //    block means inside the selection launch
   if (a.C > 0 || a.K > 0) {
     if (w.window_means && w.window_tokens == a.Nq) {
       // the window holds as many tokens as the chunk: one launch for both
-      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, cm_out, s,
+      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, nullptr, s,
                             k + (int64_t)w.window_token0 * a.kvs[1], a.kvs, km_win);
     } else {
-      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, cm_out, s);
+      e = launch_block_mean(q, a.B, a.Nq, a.H, a.d, a.qs, a.block, a.seg, bps, nqb, qm, nullptr, s);
       if (e == hipSuccess && w.window_means)
         e = launch_block_mean(k + (int64_t)w.window_token0 * a.kvs[1], a.B, w.window_tokens, a.H,
                               a.d, a.kvs, a.block, a.seg, bps, a.local_count, km_win, nullptr, s);
@@ -1004,7 +1004,8 @@ int run_sparse(const SparseArgs& a, const ca_block_sparse_ws& w, char* ws, hipSt
   if (a.C > 0)
     jobs[nj++] = TopkJobDesc{cm, km_hist, a.B, a.H, 1, nkb, a.d, a.hist_begin, a.hist_count, a.C,
                              a.sink_begin, a.sink_count, 0, pers, nullptr,
-                             fused_shared ? sh_ptr : nullptr, fused_shared ? sh_idx : nullptr};
+                             fused_shared ? sh_ptr : nullptr, fused_shared ? sh_idx : nullptr,
+                             qm, a.Nq, a.block, a.seg, nqb};
   if (a.K > 0) {
     const float* km_loc = w.window_means ? km_win : km_ws;
     const int nkb_loc = w.window_means ? a.local_count : nkb;

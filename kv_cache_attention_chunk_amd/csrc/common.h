@@ -151,6 +151,11 @@ struct TopkJobDesc {
   float* out_score;
   int32_t* indptr;
   int32_t* indices;
+  // optional: the query (NQB = 1) is the chunk mean of these query block
+  // means [B*H, cm_nb, d] (tiling cm_block / cm_seg over cm_N tokens),
+  // computed in the launch and written to qm
+  const float* cm_src;
+  int cm_N, cm_block, cm_seg, cm_nb;
 };
 // Up to 4 independent selections in one launch of 512-thread workgroups.
 hipError_t launch_score_topk_batch(const TopkJobDesc* jobs, int n_jobs, hipStream_t stream);

@@ -78,22 +78,22 @@ __global__ __launch_bounds__(kMeanThreads) void block_mean_kernel(
 }
 
 // Mean over all N tokens of each (b, h) from its block means: sum over blocks
-// of len_j * mean_j divided by N.  One workgroup of 1024 threads per (b, h).
-// With G = 1024 / d thread groups, group g sums blocks g, g + G, ... in
-// float32 (independent loads, so many are in flight; the block's frame and
-// position are stepped along instead of divided out per block), then the G
-// partial sums of each column are added in group order.
+// of len_j * mean_j divided by N.  The arithmetic is fixed by G = 1024 / d
+// thread groups whatever the workgroup size: group g sums blocks g, g + G,
+// ... in float32 (independent loads, so many are in flight; the block's frame
+// and position are stepped along instead of divided out per block), then the
+// G partial sums of each column are added in group order.  A workgroup of
+// THREADS threads covers the G * d (group, column) slots in THREADS-strided
+// passes; `red` is 1024 floats of LDS.  Writes the d means to out (global)
+// and, if given, to out_lds.
 constexpr int kTotThreads = 1024;
 
-__global__ __launch_bounds__(kTotThreads) void total_mean_kernel(
-    const float* __restrict__ means, int N, int block, int seg, int bps, int nb, int d,
-    float* __restrict__ out) {
-  __shared__ float red[kTotThreads];
-  const int bh = blockIdx.x;
+template <int THREADS>
+__device__ __forceinline__ void total_mean_row(const float* __restrict__ m, int N, int block,
+                                               int seg, int bps, int nb, int d, float* red,
+                                               float* __restrict__ out, float* out_lds) {
   const int G = kTotThreads / d;
-  const float* m = means + (int64_t)bh * nb * d;
-  const int slot = threadIdx.x;
-  if (slot < G * d) {
+  for (int slot = threadIdx.x; slot < G * d; slot += THREADS) {
     const int g = slot / d, j = slot - (slot / d) * d;
     int fs = g / bps, fj = g - (g / bps) * bps;       // frame and position of block g
     float s = 0.f;
@@ -114,11 +114,23 @@ __global__ __launch_bounds__(kTotThreads) void total_mean_kernel(
     red[slot] = s;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < d; j += kTotThreads) {
+  for (int j = threadIdx.x; j < d; j += THREADS) {
     float t = 0.f;
     for (int g = 0; g < G; ++g) t += red[g * d + j];
-    out[(int64_t)bh * d + j] = N > 0 ? t / (float)N : 0.f;
+    t = N > 0 ? t / (float)N : 0.f;
+    out[j] = t;
+    if (out_lds) out_lds[j] = t;
   }
+}
+
+// One workgroup of 1024 threads per (b, h).
+__global__ __launch_bounds__(kTotThreads) void total_mean_kernel(
+    const float* __restrict__ means, int N, int block, int seg, int bps, int nb, int d,
+    float* __restrict__ out) {
+  __shared__ float red[kTotThreads];
+  const int bh = blockIdx.x;
+  total_mean_row<kTotThreads>(means + (int64_t)bh * nb * d, N, block, seg, bps, nb, d, red,
+                              out + (int64_t)bh * d, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,6 +165,9 @@ struct TopkLists {
   int prefix_begin, prefix_count, id_offset, rows;
 };
 
+// With `cm_src`, the job's query (NQB = 1) is the chunk mean, computed by the
+// job's own workgroup from the head's query block means cm_src [BH, cm_nb, d]
+// (tiling cm_block / cm_seg over cm_N tokens) and also written to qm.
 struct TopkJob {
   const float* qm;
   const float* km;
@@ -160,6 +175,8 @@ struct TopkJob {
   int32_t* out_idx;
   float* out_score;
   TopkLists lists;
+  const float* cm_src;
+  int cm_N, cm_block, cm_seg, cm_nb;
 };
 constexpr int kTopkMaxJobs = 4;
 constexpr int kTopkBatchThreads = 512;
@@ -308,13 +325,13 @@ __device__ void topk_row(const float* __restrict__ qm, const float* __restrict__
                          int NKB, int d, int cand_begin, int n, int K,
                          int32_t* __restrict__ out_idx, float* __restrict__ out_score,
                          const TopkLists& lists, int qb, int bh, float* topk_lds, int* hist,
-                         int* rstate) {
+                         int* rstate, const float* q_given = nullptr) {
   const int n4 = (n + 3) >> 2;
   float* ss = topk_lds;                                          // [4 n4] scores
   int* rk = reinterpret_cast<int*>(ss + 4 * n4);                 // [n] ranks
   int* wcount = rk + n;                                          // [2 THREADS / 64]
   const int tid = threadIdx.x;
-  const float* q = qm + ((int64_t)bh * NQB + qb) * d;
+  const float* q = q_given ? q_given : qm + ((int64_t)bh * NQB + qb) * d;
   const float* kbase = km + ((int64_t)bh * NKB + cand_begin) * d;
   coarse_scores<THREADS>(q, d, n, 4 * n4, [&](int c) { return kbase + (int64_t)c * d; }, ss);
   __syncthreads();
@@ -442,8 +459,21 @@ __global__ __launch_bounds__(kTopkBatchThreads) void score_topk_batch_kernel(con
   const int local = (int)blockIdx.x - jb.wg_begin;
   const int bh = local / jb.NQB;
   const int qb = local - bh * jb.NQB;
+  const float* q_given = nullptr;
+  if (jb.cm_src) {
+    // the chunk-mean query of this head, from its query block means
+    __shared__ float red[kTotThreads];
+    __shared__ __attribute__((aligned(16))) float cmq[kTotThreads];   // d <= 1024
+    const int bps = (jb.cm_seg + jb.cm_block - 1) / jb.cm_block;
+    total_mean_row<kTopkBatchThreads>(jb.cm_src + (int64_t)bh * jb.cm_nb * jb.d, jb.cm_N,
+                                      jb.cm_block, jb.cm_seg, bps, jb.cm_nb, jb.d, red,
+                                      const_cast<float*>(jb.qm) + (int64_t)bh * jb.d, cmq);
+    __syncthreads();
+    q_given = cmq;
+  }
   topk_row<kTopkBatchThreads>(jb.qm, jb.km, jb.NQB, jb.NKB, jb.d, jb.cand_begin, jb.n, jb.K,
-                              jb.out_idx, jb.out_score, jb.lists, qb, bh, topk_lds, hist, rstate);
+                              jb.out_idx, jb.out_score, jb.lists, qb, bh, topk_lds, hist, rstate,
+                              q_given);
 }
 
 // ---------------------------------------------------------------------------
@@ -837,7 +867,8 @@ hipError_t launch_score_topk_batch(const TopkJobDesc* jobs, int n_jobs, hipStrea
     const int rows = a.B * a.H * a.NQB;
     tj.j[i] = TopkJob{a.qm, a.km, a.NQB, a.NKB, a.d, a.cand_begin, a.cand_count, a.K, wgs,
                       a.out_idx, a.out_score,
-                      TopkLists{a.indptr, a.indices, a.prefix_begin, a.prefix_count, a.id_offset, rows}};
+                      TopkLists{a.indptr, a.indices, a.prefix_begin, a.prefix_count, a.id_offset, rows},
+                      a.cm_src, a.cm_N, a.cm_block, a.cm_seg, a.cm_nb};
     wgs += rows;
     n_max = a.cand_count > n_max ? a.cand_count : n_max;
   }
