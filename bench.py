@@ -49,7 +49,6 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "kv_cache_attention_chunk_amd", "csrc")
 ATTN_SRC = [os.path.join(CSRC, f) for f in ("attn_fwd.hip", "attn_tile.h")]
-COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_dense_wan_counters.json")
 
 
 def log(*a):
@@ -71,16 +70,11 @@ def src_hash(paths=None) -> str:
 
 
 def traffic_from_counters():
-    """HBM bytes per dense call (its attention launch plus the split merge of
-    the balanced schedule) from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
-    try:
-        c = json.load(open(COUNTERS))
-    except (OSError, ValueError):
-        return None
-    if c.get("attn_fwd_code_sha256_16") != src_hash():
-        return None
-    return c.get("hbm_bytes_per_call")
+    """Bytes per dense call (its attention launch; the plain grid has no
+    split merge) from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel code; else None."""
+    c = counters("attn_fwd_dense_wan", ("attn_fwd.hip", "attn_tile.h"))
+    return None if c is None else c.get("hbm_bytes_per_call")
 
 
 def effective_schedule(ca, q, k, v, scale, policy):
@@ -508,7 +502,7 @@ def counters(name, sources):
     return c
 
 
-SPARSE_SOURCES = ("pbsa.hip", "attn_tile.h", "select.hip", "api.hip")
+SPARSE_SOURCES = ("pbsa.hip", "attn_tile.h", "select.hip", "common.h")
 
 
 def per_config(reps=10, wan=None, names=None, probes=None):
