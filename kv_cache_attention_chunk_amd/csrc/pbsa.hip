@@ -34,9 +34,14 @@ void pbsa_fwd_kernel(const PbsaParams p) {
   constexpr int NDT = D / 32;
   using G1 = tile::Geom<D, kTileKeys>;   // phase 1: 64-key tiles, all 8 waves
   using G2 = tile::Geom<D, 32>;          // phase 2: 32-key tiles, per pair
-  constexpr int LDS2 = kPbsaPairs * G2::RING;
-  constexpr int LDSB = G1::RING > LDS2 ? G1::RING : LDS2;
-  __shared__ __attribute__((aligned(1024))) char lds[LDSB];
+  // K stages and V stages as two LDS objects (as in attn_fwd_kernel), so that
+  // the reads of each carry the object they come from; each object holds the
+  // phase-1 ring's stages or, in phase 2, every pair's stages
+  constexpr int HALF1 = tile::kStages * G1::TILEB;
+  constexpr int HALF2 = kPbsaPairs * tile::kStages * G2::TILEB;
+  constexpr int HALFB = HALF1 > HALF2 ? HALF1 : HALF2;
+  __shared__ __attribute__((aligned(1024))) char kst[HALFB];
+  __shared__ __attribute__((aligned(1024))) char vst[HALFB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,8 +104,8 @@ void pbsa_fwd_kernel(const PbsaParams p) {
     };
     tile::Loader<D, kTileKeys, kPbsaWaves> ldr1;
     ldr1.init(lane, wave, stride_bytes);
-    tile::run<D, kTileKeys, kPbsaWaves>(rs, ldr1, lds, lds + tile::kStages * G1::TILEB, kh, vh,
-                                        stride_bytes, n1, p.scale_log2, hg, src1, [](int) {});
+    tile::run<D, kTileKeys, kPbsaWaves>(rs, ldr1, kst, vst, kh, vh, stride_bytes, n1,
+                                        p.scale_log2, hg, src1, [](int) {});
   }
 
   // ---- phase 2: each pair's local list, 32-key tiles, per-pair rings -----
@@ -134,9 +139,9 @@ void pbsa_fwd_kernel(const PbsaParams p) {
     };
     tile::Loader<D, 32, 2> ldr2;
     ldr2.init(lane, wave & 1, stride_bytes);
-    char* ring = lds + pair * G2::RING;
-    tile::run<D, 32, 2>(rs, ldr2, ring, ring + tile::kStages * G2::TILEB, kh, vh, stride_bytes,
-                        2 * nmax, p.scale_log2, hg, src2, [](int) {});
+    const int pr = pair * tile::kStages * G2::TILEB;
+    tile::run<D, 32, 2>(rs, ldr2, kst + pr, vst + pr, kh, vh, stride_bytes, 2 * nmax,
+                        p.scale_log2, hg, src2, [](int) {});
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l) ----------------------
