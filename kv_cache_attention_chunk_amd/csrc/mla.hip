@@ -420,14 +420,22 @@ __global__ __launch_bounds__(kProjWaves * 64) void head_proj_kernel(const ProjPa
 
   // W^T into LDS: ws[j * WR + i] = W(h, i, j)
   if (W_IN_MAJOR) {
-    // 16-byte loads of 8 consecutive j for one i, scattered to 8 LDS rows
-    for (int c = tid; c < K * N / 8; c += kProjWaves * 64) {
-      const int i = c / (N / 8), j0 = 8 * (c - i * (N / 8));
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p.w + ((int64_t)h * K + i) * N + j0);
+    // two consecutive i and eight consecutive j per thread: two 16-byte
+    // loads, then eight 4-byte stores of the pairs (W(i, j), W(i + 1, j)).
+    // Consecutive lanes take consecutive i pairs, so the stores of a wave
+    // for one j fill consecutive LDS words (distinct banks) instead of
+    // 2-byte stores 8 rows apart landing in two banks.
+    static_assert(K % 2 == 0 && WR % 2 == 0, "i pairs are 4-byte words");
+    uint32_t* ws32 = reinterpret_cast<uint32_t*>(ws);
+    for (int c = tid; c < K * N / 16; c += kProjWaves * 64) {
+      const int ip = c % (K / 2), j0 = 8 * (c / (K / 2));
+      const int i = 2 * ip;
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(p.w + ((int64_t)h * K + i) * N + j0);
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(p.w + ((int64_t)h * K + i + 1) * N + j0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        ws[(j0 + 2 * e) * WR + i] = (uint16_t)(x[e] & 0xFFFFu);
-        ws[(j0 + 2 * e + 1) * WR + i] = (uint16_t)(x[e] >> 16);
+        ws32[((j0 + 2 * e) * WR + i) / 2] = (x0[e] & 0xFFFFu) | (x1[e] << 16);
+        ws32[((j0 + 2 * e + 1) * WR + i) / 2] = (x0[e] >> 16) | (x1[e] & 0xFFFF0000u);
       }
     }
   } else {
