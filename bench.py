@@ -819,9 +819,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--topk-ratio", type=float, default=0.125)
-    ap.add_argument("--only", choices=["step", "dense", "copy", "configs"], default="step",
+    ap.add_argument("--only", choices=["step", "dense", "copy", "configs", "roofs"],
+                    default="step",
                     help="'dense' times the dense kernel alone (for counter runs); 'copy' "
-                         "runs a plain 1 GiB device copy, the reference for HBM byte counters")
+                         "runs a plain 1 GiB device copy, the reference for HBM byte counters; "
+                         "'roofs' runs the roof probes alone and prints what they measure")
     ap.add_argument("--config", default="",
                     help="with --only configs: comma-separated entries to time (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -867,6 +869,9 @@ def main():
         ms = e0.elapsed_time(e1) / args.steps
         print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes,
                           "ms": ms, "GBps_read+write": 2 * n_bytes / (ms * 1e-3) / 1e9}))
+        return
+    if args.only == "roofs":
+        print(json.dumps(measured_roofs(torch)), flush=True)
         return
     if args.only == "configs":
         names = set(args.config.split(",")) if args.config else None

@@ -46,10 +46,13 @@ void attn_fwd_kernel(const AttnParams p) {
   using G = tile::Geom<D, TK>;
   constexpr int TPE = kTileKeys / TK;   // tiles per list entry (block mode)
   static_assert(MODE == MODE_BLOCKS || TK == kTileKeys, "range mode streams 64-key tiles");
-  // K and V stages as two LDS objects, so that the reads of each carry the
-  // object they come from.
-  __shared__ __attribute__((aligned(1024))) char kst[tile::kStages * G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vst[tile::kStages * G::TILEB];
+  // Ring stages: four for the 8-wave workgroups (one per CU), whose loop then
+  // meets the workgroup barrier every second tile; two for the smaller ones,
+  // which share a CU.  K and V stages are two LDS objects, so that the reads
+  // of each carry the object they come from.
+  constexpr int NS = NW == 8 ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) char kst[NS * G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vst[NS * G::TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -302,7 +305,7 @@ void attn_fwd_kernel(const AttnParams p) {
   const int snap = (MODE == MODE_BLOCKS && p.snap >= 0)
                        ? (p.snap * TPE < ntiles ? p.snap * TPE : ntiles) : -1;
   if (MODE == MODE_BLOCKS && snap == 0) emit_state(true);
-  tile::run<D, TK, NW>(rs, ldr, kst, vst, kh, vh, stride_bytes, ntiles, p.scale_log2, hg,
+  tile::run<D, TK, NW, NS>(rs, ldr, kst, vst, kh, vh, stride_bytes, ntiles, p.scale_log2, hg,
                        tile_src, [&](int t) {
                          if (MODE == MODE_BLOCKS && t == snap - 1) emit_state(true);
                        });

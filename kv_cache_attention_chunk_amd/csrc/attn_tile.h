@@ -212,9 +212,15 @@ struct Rows {
 // Streams `ntiles` tiles of TK keys through the ring at kst (K stages) and
 // vst (V stages) and folds them into the rows' softmax state.  tile_src(t,
 // off, len) gives tile t's element offset from kh / vh and its valid rows; it
-// is called for t = 0, 1, 2, ... in order.  after_tile(t) runs when tile t is
-// complete (all waves have finished reading its stages).
-template <int D, int TK, int NWL, class Src, class After>
+// is called for t = 0, 1, 2, ... in order.  after_tile(t) runs in each wave
+// once tile t has been folded into its rows.
+//
+// NS is the number of K stages and of V stages in the ring (2 or 4, each
+// TK x D).  With 2, every iteration ends with the workgroup barrier; with 4,
+// loads run one tile further ahead and only every second iteration ends with
+// one (the ring then holds the two tiles being read and the two being
+// loaded).
+template <int D, int TK, int NWL, int NS = kStages, class Src, class After>
 __device__ __forceinline__ void run(Rows<D>& rs, const Loader<D, TK, NWL>& ldr, char* kst,
                                     char* vst, const uint16_t* kh, const uint16_t* vh,
                                     uint32_t stride_bytes, int ntiles, float scale_log2, int hg,
@@ -358,15 +364,22 @@ __device__ __forceinline__ void run(Rows<D>& rs, const Loader<D, TK, NWL>& ldr, 
   };
   static_assert((KT == 1 || 2 * SEG + 1 + 4 <= NSEG) && 16 % NDT == 0, "max segments must fit the body");
 
-  // Load pipeline.  K(t) is last read by the QK MFMAs of iteration t-1, so
-  // K(t + 2) goes out at the start of iteration t; V(t) is read in iteration
-  // t, so V(t + 1) goes out at the start of iteration t.  Each iteration
-  // issues its V load before its K load.  The end-of-iteration wait needs
-  // V(t+1) and K(t+2) and leaves every load issued after V(t+1) in flight:
-  // vmcnt counts this wave's loads in issue order.
+  // Load pipeline.  K(t) is last read by the QK MFMAs of iteration t-1 and
+  // V(t) in iteration t.
+  //   NS = 2: K(t + 2) and V(t + 1) go out at the start of iteration t, into
+  //   the stages of K(t) and V(t - 1), read before the previous barrier.  The
+  //   end-of-iteration wait needs V(t+1) and K(t+2) and leaves every load
+  //   issued after V(t+1) in flight (vmcnt counts this wave's loads in issue
+  //   order; each iteration issues its V load before its K load).
+  //   NS = 4: K(t + 3) and V(t + 2) go out at the start of iteration t.  The
+  //   barrier follows the odd iterations only: iterations 2u and 2u + 1 read
+  //   K(2u+1), K(2u+2), V(2u), V(2u+1), all loaded during iterations 2u-2
+  //   and 2u-1, and refill the stages of K(2u-1), K(2u), V(2u-2), V(2u-1),
+  //   all read before the barrier that ends iteration 2u-1; that barrier
+  //   follows a wait for every load in flight.
+  static_assert(NS == 2 || NS == 4, "two or four stages");
   constexpr int NIK = Loader<D, TK, NWL>::NI;    // load instructions per wave per tile
-  constexpr int KA = kStages, VA = kStages - 1;  // K / V load lead in tiles
-  static_assert(KA >= 2 && VA >= 1, "K(t+2) and V(t+1) must already be on their way");
+  constexpr int KA = NS == 2 ? 2 : 3, VA = KA - 1;  // K / V load lead in tiles
   auto wait_vm = [&](int groups_after) {
     // s_waitcnt vmcnt(n): vmcnt[3:0] | expcnt 7 << 4 | lgkmcnt 0 << 8 | vmcnt[5:4] << 14
 #define CA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
@@ -393,19 +406,18 @@ __device__ __forceinline__ void run(Rows<D>& rs, const Loader<D, TK, NWL>& ldr, 
   // One iteration: the first operand reads of the fused body go out right
   // after the barrier, ahead of the load issue and the rescale.
   float rawmax = -INFINITY;     // raw row max of the tile in `cur`
-  // `par` = t % 2 as a compile-time constant (the loop below is unrolled by
-  // two), which makes every stage index a constant offset.
-  static_assert(kStages == 2, "stage indices below assume two stages");
+  // `par` = t % NS as a compile-time constant (the loop below is unrolled by
+  // NS), which makes every stage index a constant offset.
   auto step = [&](int t, auto par, f32x16_t (&cur)[2], f32x16_t (&nx)[2]) {
     constexpr int P = decltype(par)::value;
-    constexpr int ks = (P + 1) % 2, vs = P;
+    constexpr int ks = (P + 1) % NS, vs = P;
 #pragma unroll
     for (int s1 = 0; s1 < PD; ++s1) fetch(s1, ks, vs);
     if (t + VA < ntiles)
-      ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((P + VA) % 2) * G::TILEB);
+      ldr.issue_v(vh + doff[VA], dlen[VA], stride_bytes, vst + ((P + VA) % NS) * G::TILEB);
     if (t + KA < ntiles) {
       tile_src(t + KA, doff[KA], dlen[KA]);
-      ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((P + KA) % 2) * G::TILEB);
+      ldr.issue_k(kh + doff[KA], dlen[KA], stride_bytes, kst + ((P + KA) % NS) * G::TILEB);
     }
     prep(cur, dlen[0], rawmax);
     fused(cur, ks, vs, nx, rawmax);
@@ -413,6 +425,11 @@ __device__ __forceinline__ void run(Rows<D>& rs, const Loader<D, TK, NWL>& ldr, 
     for (int j = 0; j < KA; ++j) {
       doff[j] = doff[j + 1];
       dlen[j] = dlen[j + 1];
+    }
+    if (NS == 4) {
+      if (P % 2 == 1) wait_vm(0);
+      after_tile(t);
+      return;
     }
     // Tile loads issued after the later of V(t+1) and K(t+2), which may stay
     // in flight.  V(t+1) went out in iteration t + 1 - VA and K(t+2) in
@@ -447,13 +464,21 @@ __device__ __forceinline__ void run(Rows<D>& rs, const Loader<D, TK, NWL>& ldr, 
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) rawmax = fmaxf(rawmax, sa[kt][i]);
-    // iteration 0 refills K stage 0, which every wave has just read
+    // iteration 0 (NS = 2) or 1 (NS = 4) refills K stage 0, which every wave
+    // has just read
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     block_sync();
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = 0; t < ntiles; t += NS) {
       step(t, std::integral_constant<int, 0>{}, sa, sb);
       if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{}, sb, sa);
+      if (NS == 4) {
+        if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2 % NS>{}, sa, sb);
+        if (t + 3 < ntiles) step(t + 3, std::integral_constant<int, 3 % NS>{}, sb, sa);
+      }
     }
+    // with four stages an even last iteration ends without the barrier that
+    // orders the ring's LDS against whatever the caller does next
+    if (NS == 4 && ntiles % 2 == 1) wait_vm(0);
   }
 }
 

@@ -36,8 +36,9 @@ void pbsa_fwd_kernel(const PbsaParams p) {
   using G2 = tile::Geom<D, 32>;          // phase 2: 32-key tiles, per pair
   // K stages and V stages as two LDS objects (as in attn_fwd_kernel), so that
   // the reads of each carry the object they come from; each object holds the
-  // phase-1 ring's stages or, in phase 2, every pair's stages
-  constexpr int HALF1 = tile::kStages * G1::TILEB;
+  // phase-1 ring's four stages or, in phase 2, every pair's two stages
+  constexpr int NS1 = 4;
+  constexpr int HALF1 = NS1 * G1::TILEB;
   constexpr int HALF2 = kPbsaPairs * tile::kStages * G2::TILEB;
   constexpr int HALFB = HALF1 > HALF2 ? HALF1 : HALF2;
   __shared__ __attribute__((aligned(1024))) char kst[HALFB];
@@ -104,7 +105,7 @@ void pbsa_fwd_kernel(const PbsaParams p) {
     };
     tile::Loader<D, kTileKeys, kPbsaWaves> ldr1;
     ldr1.init(lane, wave, stride_bytes);
-    tile::run<D, kTileKeys, kPbsaWaves>(rs, ldr1, kst, vst, kh, vh, stride_bytes, n1,
+    tile::run<D, kTileKeys, kPbsaWaves, NS1>(rs, ldr1, kst, vst, kh, vh, stride_bytes, n1,
                                         p.scale_log2, hg, src1, [](int) {});
   }
 
