@@ -2,8 +2,8 @@
 //
 // One workgroup owns NW*32 query rows of one (b, h) and streams that head's
 // key set in 64-token tiles (32-token tiles for 2-wave workgroups) through
-// the tile loop of attn_tile.h: buffer->LDS loads into a double-buffered
-// swizzled ring, S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16,
+// the tile loop of attn_tile.h: buffer->LDS loads into a swizzled ring of
+// K and V stages, S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16,
 // online softmax in the log2 domain, software-pipelined so that the softmax of
 // tile t overlaps the QK MFMAs of tile t+1.  Epilogue: O = acc / l, LSE =
 // ln2 * (m + log2 l); an empty key set gives O = 0, LSE = -inf.
@@ -21,11 +21,12 @@ namespace {
 
 using tile::kLn2;
 
-// LDS ring of K and V tile stages: K x2 and V x2 (64 KB at d = 128).  An
-// 8-wave workgroup (256 query rows) holds a CU's 8 waves, so each K/V tile
-// goes from L2 to LDS once per CU for 256 rows.  With two stages each, the
-// stage of every read is a compile-time constant in the two-iteration
-// unrolled loop.
+// LDS ring of K and V tile stages.  An 8-wave workgroup (256 query rows)
+// holds a CU's 8 waves, so each K/V tile goes from L2 to LDS once per CU for
+// 256 rows; it keeps four K and four V stages (128 KB at d = 128) and meets
+// the workgroup barrier every second tile.  Smaller workgroups share a CU and
+// keep two of each.  The stage of every read is a compile-time constant in
+// the loop unrolled by the stage count.
 //
 // 2-wave workgroups (64-row query blocks, the per-query-block lists) stream
 // 32-key tiles instead: each list entry (a block of up to 64 tokens) becomes

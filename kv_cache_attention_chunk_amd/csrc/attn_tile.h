@@ -5,8 +5,10 @@
 //   * K and V tiles go straight from global memory to LDS with buffer loads
 //     (buffer_load_dwordx4 ... lds, 1 KB per wave instruction, the NWL waves
 //     of the group each filling their share): no staging registers, and the
-//     buffer range check returns zeros for rows past a partial tile.  K and V
-//     are double-buffered: K(t+2) and V(t+1) are loaded during iteration t.
+//     buffer range check returns zeros for rows past a partial tile.  With
+//     two K and two V stages, K(t+2) and V(t+1) are loaded during iteration
+//     t; with four, K(t+3) and V(t+2), and the barrier comes every second
+//     iteration.
 //   * LDS rows are unpadded and XOR-swizzled by 16-byte chunk so that every
 //     read pattern below is free of bank conflicts: K chunk c of row r sits at
 //     c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64); V chunk c at
@@ -38,7 +40,7 @@ namespace tile {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, gfx9 family
-constexpr int kStages = 2;                 // K stages and V stages of the ring
+constexpr int kStages = 2;                 // K and V stages of a ring, unless a caller asks for 4
 
 // physical 16-byte chunk of logical chunk c in row r: c ^ swz_k(r) for K,
 // c ^ swz_v(r) for V

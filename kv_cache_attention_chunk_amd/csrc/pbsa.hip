@@ -9,10 +9,11 @@
 // four query blocks of one head with 8 waves, a pair of waves (64 rows) per
 // query block, and keeps their softmax state in registers across both lists:
 //   phase 1  the shared list, as 64-key tiles streamed through one LDS ring
-//            by all 8 waves (each K/V tile goes from L2 to LDS once for the
-//            four query blocks);
+//            of four K and four V stages by all 8 waves (each K/V tile goes
+//            from L2 to LDS once for the four query blocks);
 //   phase 2  each pair's local list, as 32-key tiles (two per block) through
-//            a ring of its own, all four pairs stepping together (the loop's
+//            a ring of two K and two V stages of its own, in the same LDS,
+//            all four pairs stepping together (the loop's
 //            barriers are workgroup-wide, so a shorter list is padded with
 //            empty tiles up to the longest of the four).
 // Both phases run the tile loop of attn_tile.h.  Nothing is written between
