@@ -247,3 +247,32 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ca.chunk_attn_fwd(q, q, q)
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """The header compiles as C99 (no C++ in the interface) and a C program
+    that calls through it links against the library and runs its host-only
+    entry points."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text('#include "chunkattn.h"\n#include <stdio.h>\n'
+                   'int main(void) {\n'
+                   '  if (ca_abi_version() != CA_ABI_VERSION) return 1;\n'
+                   '  if (ca_num_blocks(1560, 64, 1560) != 25) return 2;\n'
+                   '  printf("%s\\n", ca_status_str(CA_ERANGE));\n'
+                   '  return 0;\n}\n')
+    exe = tmp_path / "abi"
+    pkg = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I",
+                        os.path.join(os.path.dirname(pkg), "include"), str(src), "-L", pkg,
+                        "-lchunkattn", f"-Wl,-rpath,{pkg}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip() == "value out of range"
