@@ -788,17 +788,29 @@ def per_config(reps=10, wan=None, names=None, probes=None):
             L = int(w.cu_seqlens[h + 1] - w.cu_seqlens[h])
             f += 4.0 * w.d * w.Nq * L
             kvb += 2.0 * L * w.d * 2
-    ip = np.zeros(len(lists) + 1, np.int32)
-    ip[1:] = np.cumsum([len(x) for x in lists])
-    ix = i32(np.concatenate(lists))
-    ip = i32(ip)
+    # the block-sparse heads run one-pass PBSA: per head the sink and
+    # persistent blocks (shared by its query blocks), per query block its
+    # top-K window blocks; the union of the two is the key set of `lists`
+    pn, ln = sel_gpu["persistent"], sel_gpu["local"]
+    sink = np.arange(lay["sink_count"], dtype=np.int32)
+    shared, local = [], []
+    for h in range(w.H):
+        si = hs.index(h) if w.head_mode[h] == 1 else -1
+        shared.append(np.concatenate([sink, pn[0, si, 0]]) if si >= 0 else np.zeros(0, np.int32))
+        for qb in range(nqb):
+            local.append(ln[0, si, qb] if si >= 0 else np.zeros(0, np.int32))
+    csr = lambda rows: (i32(np.concatenate([[0], np.cumsum([len(x) for x in rows])])),
+                        i32(np.concatenate(rows)))
+    sp, sx = csr(shared)
+    lp, lx = csr(local)
     kf, vf, cu = dev(w.k_flat), dev(w.v_flat), i32(w.cu_seqlens)
     if want("mixed_40h"):
         o_x, l_x = torch.empty_like(q), f32(w.B, w.H, w.Nq)
         call = lambda i=0, kk=k, vv=v, kkf=kf, vvf=vf: ca.chunk_attn_mixed_fwd(
-            q, w.head_mode, k=kk, v=vv, kv_indptr=ip, kv_indices=ix, kv_block=64, kv_seg=1560,
-            q_block=64, q_seg=1560, k_flat=kkf, v_flat=vvf, cu_seqlens=cu,
-            cu_seqlens_host=w.cu_seqlens, scale=w.scale, out=o_x, lse=l_x)
+            q, w.head_mode, k=kk, v=vv, kv_indptr=lp, kv_indices=lx, kv_shared_indptr=sp,
+            kv_shared_indices=sx, kv_block=64, kv_seg=1560, q_block=64, q_seg=1560, k_flat=kkf,
+            v_flat=vvf, cu_seqlens=cu, cu_seqlens_host=w.cu_seqlens, scale=w.scale, out=o_x,
+            lse=l_x)
         rec = _rec(_time_ms(torch, call, reps), f, kvb,
                    heads_dense_sparse_ragged=[int((w.head_mode == mm).sum()) for mm in range(3)])
         n = _cold_sets(kvb)

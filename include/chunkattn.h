@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CA_ABI_VERSION 3
+#define CA_ABI_VERSION 4
 
 enum ca_status {
   CA_OK = 0,
@@ -355,13 +355,21 @@ int ca_pack_ragged(const void* k, const void* v, int B, int N, int H, int d,
  * mode no head uses may be NULL.  Dense and ragged heads share one launch
  * (balanced across them when a workspace is given and the ragged lengths are
  * known on the host); block-list heads follow in a second launch.
+ * With kv_shared_indptr / kv_shared_indices (device, a CSR of B*H rows, row
+ * b*H + h; NULL for none) the block-list heads run one-pass PBSA instead (as
+ * ca_chunk_attn_pbsa_fwd, Sparse Forcing page, section 2 item 3): each of
+ * their query blocks attends to its head's shared row together with its own
+ * row of kv_indptr / kv_indices (its local list); the two lists of a row must
+ * be disjoint and q_block at most 64 (CA_ERANGE otherwise).
  */
 int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v,
                             int B, int H, int Nq, int Nkv, int d,
                             const int64_t* q_strides, const int64_t* kv_strides,
                             const int64_t* o_strides, const int32_t* head_mode,
                             const int32_t* kv_indptr, const int32_t* kv_indices,
-                            int kv_nnz, int kv_block, int kv_seg, int q_block, int q_seg,
+                            int kv_nnz, const int32_t* kv_shared_indptr,
+                            const int32_t* kv_shared_indices, int kv_shared_nnz,
+                            int kv_block, int kv_seg, int q_block, int q_seg,
                             const void* k_flat, const void* v_flat,
                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                             int total_kv, int64_t kv_row_stride, float scale,

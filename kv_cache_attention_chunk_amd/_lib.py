@@ -12,7 +12,7 @@ import re
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libchunkattn.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "chunkattn.h")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_ENODEV, CA_EHIP = range(6)
 CA_BF16, CA_F32 = 0, 1
 CA_MODE_DENSE, CA_MODE_BLOCKS, CA_MODE_VARLEN = 0, 1, 2
@@ -53,7 +53,8 @@ SIGNATURES = {
     "ca_chunk_attn_varlen_fwd": (_i, [_p, _p, _p, _i32p, _i32p, _i, _i, _i, _i, _i,
                                       _i64p, _i64, _i64p, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_chunk_attn_mixed_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i64p, _i64p, _i64p,
-                                     _i32p, _i32p, _i32p, _i, _i, _i, _i, _i, _p, _p,
+                                     _i32p, _i32p, _i32p, _i, _i32p, _i32p, _i, _i, _i, _i, _i,
+                                     _p, _p,
                                      _i32p, _i32p, _i, _i64, _f, _p, _i, _p, _i, _p, _sz, _p]),
     "ca_lse_merge": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i,
                           _i64p, _i64p, _i64p, _p]),

@@ -293,13 +293,18 @@ def chunk_attn_varlen_fwd(q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.T
 
 
 def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indptr=None,
-                         kv_indices=None, kv_block: int = 64, kv_seg: Optional[int] = None,
+                         kv_indices=None, kv_shared_indptr=None, kv_shared_indices=None,
+                         kv_block: int = 64, kv_seg: Optional[int] = None,
                          q_block: int = 64, q_seg: Optional[int] = None, k_flat=None, v_flat=None,
                          cu_seqlens=None, cu_seqlens_host=None, scale: Optional[float] = None,
                          out_dtype=None, out=None, lse=None, balanced: bool = True,
                          workspace: Optional[torch.Tensor] = None):
     """Per-head cache modes (0 dense, 1 block lists, 2 ragged) in one call;
-    dense and ragged heads share one (balanced) launch."""
+    dense and ragged heads share one (balanced) launch.  With
+    kv_shared_indptr / kv_shared_indices (a CSR of B*H rows) the block-list
+    heads run one-pass PBSA: each query block attends to its head's shared
+    row together with its own kv_indptr / kv_indices row (disjoint lists,
+    q_block at most 64)."""
     out_dtype = out_dtype or (out.dtype if out is not None else torch.bfloat16)
     _bshd("q", q)
     B, Nq, H, d = q.shape
@@ -313,7 +318,10 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
         if k.stride() != v.stride():
             raise ValueError("k and v must share strides")
     _i32("kv_indptr", kv_indptr), _i32("kv_indices", kv_indices), _i32("cu_seqlens", cu_seqlens)
+    _i32("kv_shared_indptr", kv_shared_indptr), _i32("kv_shared_indices", kv_shared_indices)
     _check_indptr(kv_indptr, B * H, Nq, q_block, q_seg)
+    if kv_shared_indptr is not None and kv_shared_indptr.numel() != B * H + 1:
+        raise ValueError("kv_shared_indptr must have B*H + 1 entries")
     if cu_seqlens is not None and cu_seqlens.numel() != B * H + 1:
         raise ValueError("cu_seqlens must have B*H + 1 entries")
     host = None if cu_seqlens_host is None else np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
@@ -326,7 +334,9 @@ def chunk_attn_mixed_fwd(q: torch.Tensor, head_mode, *, k=None, v=None, kv_indpt
     st = lib().ca_chunk_attn_mixed_fwd(
         q.data_ptr(), _ptr(k), _ptr(v), B, H, Nq, Nkv, d, _st(q), kvs,
         _st(o), mode.ctypes.data, _ptr(kv_indptr), _ptr(kv_indices),
-        0 if kv_indices is None else kv_indices.numel(), kv_block, kv_seg or max(Nkv, 1),
+        0 if kv_indices is None else kv_indices.numel(), _ptr(kv_shared_indptr),
+        _ptr(kv_shared_indices), 0 if kv_shared_indices is None else kv_shared_indices.numel(),
+        kv_block, kv_seg or max(Nkv, 1),
         q_block, q_seg or max(Nq, 1), _ptr(k_flat), _ptr(v_flat), _ptr(cu_seqlens),
         None if host is None else host.ctypes.data,
         0 if k_flat is None else k_flat.shape[0], d if k_flat is None else k_flat.stride(0),

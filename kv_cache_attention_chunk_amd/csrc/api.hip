@@ -477,7 +477,8 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
                             int Nkv, int d, const int64_t* q_strides, const int64_t* kv_strides,
                             const int64_t* o_strides, const int32_t* head_mode,
                             const int32_t* kv_indptr, const int32_t* kv_indices, int kv_nnz,
-                            int kv_block, int kv_seg, int q_block, int q_seg,
+                            const int32_t* kv_shared_indptr, const int32_t* kv_shared_indices,
+                            int kv_shared_nnz, int kv_block, int kv_seg, int q_block, int q_seg,
                             const void* k_flat, const void* v_flat, const int32_t* cu_seqlens,
                             const int32_t* cu_seqlens_host, int total_kv, int64_t kv_row_stride,
                             float scale, void* o, int o_dtype, float* lse, int split,
@@ -504,6 +505,13 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
   }
   if (!hb.empty()) {
     if (int r = check_csr(kv_indptr, kv_indices, kv_nnz, kv_block, kv_seg, q_block, q_seg)) return r;
+    if (kv_shared_indptr || kv_shared_indices) {
+      if (int r = check_csr(kv_shared_indptr, kv_shared_indices, kv_shared_nnz, kv_block, kv_seg,
+                            q_block, q_seg)) return r;
+      if (q_block > 64) return fail(CA_ERANGE, "q_block %d above 64 (a query block is served by 64 rows)", q_block);
+      const int nqb = num_blocks(Nq, q_block, q_seg);
+      if ((int64_t)hb.size() * ((nqb + 3) / 4) > 0x7FFFFFFF) return fail(CA_ERANGE, "too many work items");
+    }
   }
   if (!hv.empty()) {
     if (!k_flat || !v_flat || !cu_seqlens) return fail(CA_EINVAL, "k_flat, v_flat, cu_seqlens must be non-NULL");
@@ -547,7 +555,22 @@ int ca_chunk_attn_mixed_fwd(const void* q, const void* k, const void* v, int B, 
     }
     if (int r = launch_range(c, p, words, tiles, split, workspace, workspace_bytes, s)) return r;
   }
-  if (!hb.empty()) {
+  if (!hb.empty() && kv_shared_indptr) {
+    // one-pass PBSA over the block-list heads, in launches of at most
+    // kMaxHeadsPerLaunch heads
+    static thread_local PbsaParams pp;
+    pp = pbsa_params(q, k, v, B, H, Nq, Nkv, q_strides, kv_strides, o_strides, kv_shared_indptr,
+                     kv_shared_indices, kv_shared_nnz, kv_indptr, kv_indices, kv_nnz, kv_block,
+                     kv_seg, q_block, q_seg, scale, o, lse);
+    const int groups = pp.groups;
+    for (size_t h0 = 0; h0 < hb.size(); h0 += kMaxHeadsPerLaunch) {
+      const int n = (int)std::min<size_t>(kMaxHeadsPerLaunch, hb.size() - h0);
+      pp.use_list = 1;
+      for (int i = 0; i < n; ++i) pp.heads[i] = (uint16_t)hb[h0 + i];
+      pp.n_items = n * groups;
+      if (int r = launched(launch_pbsa(d, o_dtype == CA_F32, pp, s), "pbsa launch")) return r;
+    }
+  } else if (!hb.empty()) {
     p = AttnParams{};
     fill_common(p, c);
     p.k = static_cast<const uint16_t*>(k);

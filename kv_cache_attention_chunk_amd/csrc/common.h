@@ -109,7 +109,9 @@ struct PbsaParams {
   uint32_t kv_bps_magic;      // floor(2^32 / kv_bps)
   int q_block, q_seg, q_bps, nqb;
   int groups;                 // workgroups per head: ceil(nqb / 4)
-  int n_items;                // B * H * groups
+  int n_items;                // heads of this launch * groups
+  int use_list;               // 0: head i of the launch is b*H + h = i; 1: heads[i]
+  uint16_t heads[kMaxHeadsPerLaunch];
 };
 
 // First unit of workgroup g under the balanced schedule, and the workgroup

@@ -54,8 +54,9 @@ void pbsa_fwd_kernel(const PbsaParams p) {
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= p.n_items) return;
-  const int bh = item / p.groups;
-  const int grp = item - bh * p.groups;
+  const int hi = item / p.groups;
+  const int grp = item - hi * p.groups;
+  const int bh = p.use_list ? (int)p.heads[hi] : hi;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
 

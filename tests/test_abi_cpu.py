@@ -35,7 +35,7 @@ def test_header_constants_match_the_binding():
 
 
 def test_status_strings_and_version(L):
-    assert L.ca_abi_version() == 3
+    assert L.ca_abi_version() == 4
     for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"range"),
                        (4, b"device"), (5, b"HIP")]:
         assert word in L.ca_status_str(code)
@@ -167,14 +167,23 @@ def test_varlen_host_checks(L):
 def test_mixed_mode_checks(L):
     bad = np.array([0, 3], dtype=np.int32)
     st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, bad.ctypes.data,
-                                   None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
-                                   0.1, FAKE, 0, FAKE, 0, None, 0, None)
+                                   None, None, 0, None, None, 0, 64, 64, 64, 64, None, None, None,
+                                   None, 0, 64, 0.1, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL
     blocks = np.array([1, 1], dtype=np.int32)
     st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, blocks.ctypes.data,
-                                   None, None, 0, 64, 64, 64, 64, None, None, None, None, 0, 64,
-                                   0.1, FAKE, 0, FAKE, 0, None, 0, None)
+                                   None, None, 0, None, None, 0, 64, 64, 64, 64, None, None, None,
+                                   None, 0, 64, 0.1, FAKE, 0, FAKE, 0, None, 0, None)
     assert st == CA_EINVAL        # block heads without a CSR
+    # shared lists for one-pass PBSA: both pointers, and query blocks of at most 64
+    st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, blocks.ctypes.data,
+                                   FAKE, FAKE, 1, FAKE, None, 0, 64, 64, 64, 64, None, None, None,
+                                   None, 0, 64, 0.1, FAKE, 0, FAKE, 0, None, 0, None)
+    assert st == CA_EINVAL        # shared indptr without shared indices
+    st = L.ca_chunk_attn_mixed_fwd(FAKE, FAKE, FAKE, 1, 2, 16, 64, 64, S, S, S, blocks.ctypes.data,
+                                   FAKE, FAKE, 1, FAKE, FAKE, 1, 64, 64, 128, 128, None, None,
+                                   None, None, 0, 64, 0.1, FAKE, 0, FAKE, 0, None, 0, None)
+    assert st == CA_ERANGE        # q_block above 64 with shared lists
 
 
 def test_workspace_size_query(L):

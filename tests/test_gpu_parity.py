@@ -699,8 +699,9 @@ def test_ragged_full_size():
     assert_lse(l[:, :, rows], Lr, "ragged")
 
 
-def test_mixed_40_heads_full_size():
-    say("mixed 40 heads")
+@pytest.mark.parametrize("pbsa", [False, True])
+def test_mixed_40_heads_full_size(pbsa):
+    say(f"mixed 40 heads, block-list heads as {'one-pass PBSA' if pbsa else 'union lists'}")
     w = wl.mixed(seed=0)
     lay = w.meta["sparse"]
     q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
@@ -727,9 +728,29 @@ def test_mixed_40_heads_full_size():
     ip = np.zeros(len(lists) + 1, np.int32)
     ip[1:] = np.cumsum([len(x) for x in lists])
     ix = np.concatenate(lists).astype(np.int32)
+    extra = {}
+    if pbsa:
+        # the same key sets split as PBSA takes them: per head the sink and
+        # persistent blocks, per query block its top-K window blocks
+        pn, ln = pers.cpu().numpy(), loc.cpu().numpy()
+        sink = np.arange(lay["sink_count"], dtype=np.int32)
+        shared, local = [], []
+        for h in range(w.H):
+            si = sparse_heads.index(h) if w.head_mode[h] == 1 else -1
+            shared.append(np.concatenate([sink, pn[0, si, 0]]) if si >= 0 else np.zeros(0, np.int32))
+            for qb in range(75):
+                local.append(ln[0, si, qb] if si >= 0 else np.zeros(0, np.int32))
+        sp = np.zeros(w.H + 1, np.int32)
+        sp[1:] = np.cumsum([len(x) for x in shared])
+        lp = np.zeros(len(local) + 1, np.int32)
+        lp[1:] = np.cumsum([len(x) for x in local])
+        extra = dict(kv_shared_indptr=i32(sp), kv_shared_indices=i32(np.concatenate(shared)))
+        call_ip, call_ix = i32(lp), i32(np.concatenate(local))
+    else:
+        call_ip, call_ix = i32(ip), i32(ix)
     o, l = nan_out(1, w.Nq, w.H, w.d), nan_lse(1, w.H, w.Nq)
-    ca.chunk_attn_mixed_fwd(q, w.head_mode, k=k, v=v, kv_indptr=i32(ip), kv_indices=i32(ix),
-                            kv_block=64, kv_seg=1560, q_block=64, q_seg=1560,
+    ca.chunk_attn_mixed_fwd(q, w.head_mode, k=k, v=v, kv_indptr=call_ip, kv_indices=call_ix,
+                            kv_block=64, kv_seg=1560, q_block=64, q_seg=1560, **extra,
                             k_flat=to_dev(w.k_flat), v_flat=to_dev(w.v_flat),
                             cu_seqlens=i32(w.cu_seqlens), cu_seqlens_host=w.cu_seqlens,
                             scale=w.scale, out=o, lse=l)

@@ -221,6 +221,62 @@ def test_random_mixed(case):
 
 
 @pytest.mark.parametrize("case", range(N_CASES))
+def test_random_mixed_pbsa(case):
+    """Mixed modes with the block-list heads as one-pass PBSA (shared row per
+    head + local row per query block, disjoint)."""
+    rng = np.random.default_rng(7600 + case)
+    B, H, d = 1, int(rng.integers(2, 7)), int(rng.choice([64, 128]))
+    Nq, Nkv = int(rng.integers(1, 300)), int(rng.integers(1, 1200))
+    mode = rng.integers(0, 3, size=B * H).astype(np.int32)
+    kvb, kvs = _tiling(rng, Nkv, 64)
+    qb, qs = _tiling(rng, Nq, 64)
+    nkb, nqb = len(orc.block_spans(Nkv, kvb, kvs)), len(orc.block_spans(Nq, qb, qs))
+    shared, local, union = [], [], []
+    for _ in range(B * H):
+        perm = rng.permutation(nkb)
+        ns = int(rng.integers(0, min(nkb, 20) + 1))
+        shared.append(perm[:ns])
+        for _ in range(nqb):
+            loc = rng.permutation(perm[ns:])[:int(rng.integers(0, min(nkb - ns, 10) + 1))]
+            local.append(loc)
+            union.append(np.concatenate([perm[:ns], loc]))
+    sp, sx = _csr(shared)
+    lp, lx = _csr(local)
+    up, ux = _csr(union)
+    lens = rng.integers(0, 900, size=B * H)
+    cu = np.zeros(B * H + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    total = int(cu[-1])
+    policy = str(rng.choice(["never", "always", "auto"]))
+    odt = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    say(f"random mixed PBSA #{case}: H={H} d={d} Nq={Nq} Nkv={Nkv} modes={mode.tolist()} kv tiling "
+        f"({kvb},{kvs}) q tiling ({qb},{qs}) shared nnz={int(sp[-1])} local nnz={int(lp[-1])} "
+        f"schedule={policy} out={odt}")
+    Q, K, V = _tensors(rng, B, Nq, Nkv, H, d)
+    Kf, Vf = _bf(rng, (max(total, 1), d), 1.0), _bf(rng, (max(total, 1), d), 1.0)
+    Kf, Vf = wl.Bf16Tensor(Kf.bits[:total]), wl.Bf16Tensor(Vf.bits[:total])
+    q, k, v = _views(rng, Q, K, V)
+    o, l = nan_out(B, Nq, H, d, odt), nan_lse(B, H, Nq)
+    ca.chunk_attn_mixed_fwd(q, mode, k=k, v=v, kv_indptr=i32(lp), kv_indices=i32(lx),
+                            kv_shared_indptr=i32(sp), kv_shared_indices=i32(sx), kv_block=kvb,
+                            kv_seg=kvs, q_block=qb, q_seg=qs, k_flat=to_dev(Kf), v_flat=to_dev(Vf),
+                            cu_seqlens=i32(cu), cu_seqlens_host=cu, out=o, lse=l, balanced=policy)
+    torch.cuda.synchronize()
+    assert_written("random mixed PBSA", o, l)
+    og, lg = o.float().cpu().numpy(), l.cpu().numpy()
+    sc = 1 / math.sqrt(d)
+    for h in range(H):
+        if mode[h] == 0:
+            Or, Lr = orc.chunk_attn_dense(Q.f32, K.f32, V.f32, sc, heads=[h])
+        elif mode[h] == 1:
+            Or, Lr = orc.chunk_attn_blocks(Q.f32, K.f32, V.f32, up, ux, kvb, kvs, qb, qs, sc, heads=[h])
+        else:
+            Or, Lr = orc.chunk_attn_varlen(Q.f32, Kf.f32, Vf.f32, cu, sc, heads=[h])
+        assert_o(og[:, :, h:h + 1], Or, odt == torch.bfloat16, f"random mixed PBSA #{case} head {h}")
+        assert_lse(lg[:, h:h + 1], Lr, f"random mixed PBSA #{case} head {h}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
 def test_random_merge_and_block_means(case):
     rng = np.random.default_rng(7500 + case)
     B, H, d = int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.choice([64, 128]))
