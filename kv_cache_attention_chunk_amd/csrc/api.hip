@@ -106,6 +106,11 @@ void fill_common(AttnParams& p, const Common& c) {
 
 constexpr int kDenseWaves = 8;            // 256 query rows per workgroup (range mode)
 constexpr int kMinUnitsPerWg = 8;         // balanced schedule: key tiles per workgroup, at least
+// Balanced schedule: the fixed cost of a segment in key-tile units.  Measured
+// on the Wan shapes with per-workgroup timestamps: a segment takes about
+// 15 us beyond its ~1.85 us per key tile (loading its query tile, filling and
+// draining the tile ring, writing its state), about 8 tiles' worth.
+constexpr int kSegmentCost = 8;
 
 // Block mode: one workgroup per query block (or row slice of one), over a
 // list of heads (all heads when `heads` is empty), in launches of at most
@@ -168,18 +173,23 @@ int launch_range(const Common& c, AttnParams& p, const std::vector<uint16_t>& wo
       }
       const int64_t units = tsum * p.n_qtiles;
       const int64_t items = (int64_t)ns * p.n_qtiles;
-      const int64_t g = std::min<int64_t>(slots, units / kMinUnitsPerWg);
-      const int64_t est_plain = (items + slots - 1) / slots * (int64_t)max_nt;
-      const int64_t est_bal = g > 0 ? (units + g - 1) / g + 2 : INT64_MAX;
+      const int64_t vunits = units + items * kSegmentCost;
+      // (every workgroup's virtual range longer than kSegmentCost: no empty range)
+      const int64_t g = std::min<int64_t>(std::min<int64_t>(slots, units / kMinUnitsPerWg),
+                                          vunits / (kSegmentCost + 1));
+      const int64_t est_plain = (items + slots - 1) / slots * (int64_t)(max_nt + kSegmentCost);
+      const int64_t est_bal = g > 0 ? (vunits + g - 1) / g + kSegmentCost + 2 : INT64_MAX;
       // (the merge grid has 32 workgroups per query tile; keep it in range)
       const bool worth = split == CA_SPLIT_ALWAYS || est_bal * 5 < est_plain * 4;
-      if (units <= 0x7FFFFFFF && items * 32 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
+      if (vunits <= 0x7FFFFFFF && items * 32 <= 0x7FFFFFFF && g >= 1 && est_plain >= 64 && worth) {
         if (ws_bytes < workspace_bytes((int)g, c.d))
           return fail(CA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
                       ws_bytes, workspace_bytes((int)g, c.d));
         n = ns;
         p.sched = 1;
         p.n_units = (int)units;
+        p.n_vunits = (int)vunits;
+        p.seg_cost = kSegmentCost;
         p.n_wgs = (int)g;
         p.ws = static_cast<float*>(ws);
         p.tprefix[0] = 0;

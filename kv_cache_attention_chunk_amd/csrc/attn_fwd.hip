@@ -80,8 +80,8 @@ void attn_fwd_kernel(const AttnParams p) {
   int deferred = 0;     // 1: the first segment is still to run, at the end
   if (MODE == MODE_RANGE && p.sched) {
     g_self = xcd_remap(blockIdx.x, gridDim.x);
-    u_first = unit_begin(g_self, p.n_units, p.n_wgs);
-    u_end = unit_begin(g_self + 1, p.n_units, p.n_wgs);
+    u_first = sched_real(p, unit_begin(g_self, p.n_vunits, p.n_wgs));
+    u_end = sched_real(p, unit_begin(g_self + 1, p.n_vunits, p.n_wgs));
     // head holding u_first (binary search over the prefix)
     int lo = 0, hi = p.n_heads - 1;
     while (lo < hi) {
@@ -340,8 +340,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p) {
   const int qt = item - sel * p.n_qtiles;
   const int nt = p.tprefix[sel + 1] - p.tprefix[sel];
   const int u0 = p.n_qtiles * p.tprefix[sel] + qt * nt;
-  const int g0 = g_of_unit(u0, p.n_units, p.n_wgs);
-  const int g1 = g_of_unit(u0 + nt - 1, p.n_units, p.n_wgs);
+  const int g0 = g_of_unit(sched_virtual(p, u0), p.n_vunits, p.n_wgs);
+  const int g1 = g_of_unit(sched_virtual(p, u0 + nt - 1), p.n_vunits, p.n_wgs);
   if (g0 == g1) return;
   const int row0 = qt * BM;
   const int r = rg * RPW + (int)threadIdx.x / C4;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p) {
   const int h = bh - b * p.H;
   // the tile is the last segment of g0 when g0's range starts before it,
   // else g0's first; it is the first segment of every later workgroup
-  const int slot0 = unit_begin(g0, p.n_units, p.n_wgs) < u0 ? 2 * g0 + 1 : 2 * g0;
+  const int slot0 = sched_real(p, unit_begin(g0, p.n_vunits, p.n_wgs)) < u0 ? 2 * g0 + 1 : 2 * g0;
   const int np = g1 - g0 + 1;
   auto part = [&](int j) {
     return p.ws + (int64_t)(j == 0 ? slot0 : 2 * (g0 + j)) * BM * (D + 1);

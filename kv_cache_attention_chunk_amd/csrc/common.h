@@ -72,13 +72,21 @@ struct AttnParams {
   // Balanced schedule (range mode, sched = 1): the launch's work is
   // n_units = n_qtiles * tprefix[n_heads] units of one (query tile, key tile)
   // pair, ordered head, query tile, key tile; head i has tprefix[i+1] -
-  // tprefix[i] >= 1 key tiles.  Workgroup g (of n_wgs) takes units
-  // [g*n_units/n_wgs, (g+1)*n_units/n_wgs).  A query tile whose units fall to
-  // more than one workgroup is written as float32 partials (O / l, LSE) into
-  // ws: slot 2g holds a workgroup's first segment, slot 2g+1 its last; each
-  // slot is kRangeRows x d floats of O followed by kRangeRows LSE values.
+  // tprefix[i] >= 1 key tiles.  The units are dealt out by cost: every query
+  // tile is preceded by seg_cost virtual units, the fixed cost of a segment
+  // (loading the query tile, filling and draining the tile ring, writing the
+  // state) in key-tile units, so the n_vunits = n_qtiles * (tprefix[n_heads]
+  // + seg_cost * n_heads) virtual units are split evenly: workgroup g (of
+  // n_wgs) takes virtual units [g*n_vunits/n_wgs, (g+1)*n_vunits/n_wgs) and
+  // with them the real units they cover (sched_real / sched_virtual).  A
+  // query tile whose units fall to more than one workgroup is written as
+  // float32 partials (O / l, LSE) into ws: slot 2g holds a workgroup's first
+  // segment, slot 2g+1 its last; each slot is kRangeRows x d floats of O
+  // followed by kRangeRows LSE values.
   int sched;
   int n_units;
+  int n_vunits;
+  int seg_cost;
   int n_wgs;
   float* ws;
   int32_t tprefix[kMaxSchedHeads + 1];
@@ -122,6 +130,41 @@ __host__ __device__ __forceinline__ int unit_begin(int g, int n_units, int n_wgs
 }
 __host__ __device__ __forceinline__ int g_of_unit(int u, int n_units, int n_wgs) {
   return (int)((((int64_t)u + 1) * n_wgs - 1) / n_units);
+}
+
+// Real unit at virtual unit v of the balanced schedule: the virtual units of
+// a query tile are seg_cost leading ones (mapped to the tile's first unit)
+// followed by one per unit; v >= n_vunits maps to n_units.  Monotone, and
+// sched_real(v) <= u iff v <= sched_virtual(u), so workgroup g owns unit u
+// iff g_of_unit(sched_virtual(u), n_vunits, n_wgs) = g.  A workgroup's range
+// is never empty when n_vunits / n_wgs > seg_cost.
+__host__ __device__ inline int sched_real(const AttnParams& p, int v) {
+  if (v >= p.n_vunits) return p.n_units;
+  const int S = p.seg_cost;
+  int lo = 0, hi = p.n_heads - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (p.n_qtiles * (p.tprefix[mid + 1] + S * (mid + 1)) <= v) lo = mid + 1; else hi = mid;
+  }
+  const int nt = p.tprefix[lo + 1] - p.tprefix[lo];
+  const int rel = v - p.n_qtiles * (p.tprefix[lo] + S * lo);
+  const int qt = rel / (nt + S);
+  const int o = rel - qt * (nt + S);
+  return p.n_qtiles * p.tprefix[lo] + qt * nt + (o > S ? o - S : 0);
+}
+// Virtual unit of real unit u (0 <= u < n_units): the tile's leading
+// seg_cost virtual units come before it.
+__host__ __device__ inline int sched_virtual(const AttnParams& p, int u) {
+  const int S = p.seg_cost;
+  int lo = 0, hi = p.n_heads - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (p.n_qtiles * p.tprefix[mid + 1] <= u) lo = mid + 1; else hi = mid;
+  }
+  const int nt = p.tprefix[lo + 1] - p.tprefix[lo];
+  const int rel = u - p.n_qtiles * p.tprefix[lo];
+  const int qt = rel / nt;
+  return p.n_qtiles * (p.tprefix[lo] + S * lo) + qt * (nt + S) + S + (rel - qt * nt);
 }
 
 // Launchers implemented in attn_fwd.hip / select.hip / merge.hip.
