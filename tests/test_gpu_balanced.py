@@ -122,6 +122,36 @@ def test_balanced_mixed_dense_ragged_blocks():
         assert_lse(l[:, hs], Lr, f"balanced mixed mode {m}")
 
 
+@pytest.mark.parametrize("B,H,Nq,maxlen,seed", [
+    (1, 300, 300, 2000, 13),    # 300 heads: two launches (at most 256 heads each)
+    (2, 37, 513, 4000, 14),     # three query tiles, the last of one row
+])
+def test_balanced_many_short_heads(B, H, Nq, maxlen, seed):
+    """Many short heads (0 to tens of key tiles, some empty) under the forced
+    balanced schedule: runs cross many query tiles, so workgroup ranges start
+    and end inside the per-tile cost charge, on tiny tiles and at key tails;
+    the whole output is compared."""
+    say(f"balanced many short heads B={B} H={H} Nq={Nq} maxlen={maxlen}")
+    d = 64
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, maxlen + 1, size=B * H)
+    lens[rng.integers(0, B * H, size=3)] = 0
+    cu = np.zeros(B * H + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    Q = _gen(seed + 1, (B, Nq, H, d), 1.2)
+    Kf, Vf = _gen(seed + 2, (int(cu[-1]), d), 1.2), _gen(seed + 3, (int(cu[-1]), d))
+    ws = _nan_ws(d)
+    o, l = ca.chunk_attn_varlen_fwd(to_dev(Q), to_dev(Kf), to_dev(Vf), i32(cu),
+                                    cu_seqlens_host=cu, balanced="always", workspace=ws,
+                                    out=nan_out(B, Nq, H, d), lse=nan_lse(B, H, Nq))
+    torch.cuda.synchronize()
+    assert _touched(ws), "balanced schedule not taken"
+    assert_written("balanced many short heads", o, l)
+    Or, Lr = orc.chunk_attn_varlen(Q.f32, Kf.f32, Vf.f32, cu, 1 / math.sqrt(d))
+    assert_o(o, Or, True, "balanced many short heads")
+    assert_lse(l, Lr, "balanced many short heads")
+
+
 def test_workspace_too_small_is_rejected():
     say("workspace too small")
     B, H, Nq, Nkv, d = 1, 2, 256, 8192, 128
