@@ -81,13 +81,16 @@ int ca_num_blocks(int n_tokens, int block_size, int seg_len);
  * With a workspace (caller-owned device memory, 16-byte aligned, at least this
  * size) a dense or ragged launch may take the balanced schedule: its grid is
  * the number of workgroups the device holds at once, and each workgroup takes
- * an equal share of the (query tile, 64-key tile) pairs of all heads, in head
- * order.  A query tile whose key range is split between workgroups is
+ * an equal share of the cost of the (query tile, 64-key tile) pairs of all
+ * heads, in head order, where every query tile a workgroup touches also
+ * costs a fixed charge of 8 key tiles (loading its queries, filling and
+ * draining the tile pipeline, writing its state).  A query tile whose key
+ * range is split between workgroups is
  * finished by an LSE merge of the float32 partial results (O/l, LSE) that
  * the workgroups leave in the workspace: attention over consecutive key
  * ranges recombined through the LSE state (ISPA page, section 2 item 1).
  * The result is the same attention up to float32 rounding.  The schedule is
- * taken only when it shortens the launch by more than a fifth by tile count
+ * taken only when it shortens the launch by more than a fifth by that cost
  * (chiefly heads of unequal length); it needs every head's key count on the
  * host (always for the dense cache; for ragged heads only with
  * cu_seqlens_host).  Calls sharing one workspace
