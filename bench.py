@@ -337,6 +337,23 @@ def _time_ms(torch, fn, reps=10, warmup_s=0.2, spread=True):
     return t
 
 
+def _graphed(torch, fn):
+    """fn's launches captured once into a HIP graph (torch.cuda.CUDAGraph),
+    after an eager warm-up on a side stream; returns the replay function.
+    The library's calls launch kernels only, so they capture as they are."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g.replay
+
+
 def _time_calls(torch, fn, reps=20, warmup_s=0.2):
     """Per-call HIP-event times of fn() in ms (one event pair per call, on the
     current stream), after about warmup_s seconds of untimed calls."""
@@ -552,11 +569,18 @@ def per_config(reps=10, wan=None, names=None, probes=None):
     if want("tiny_dense"):
         od, ld = torch.empty_like(q), f32(w.B, w.H, w.Nq)
         om, lm = torch.empty_like(q), f32(w.B, w.H, w.Nq)
-        ms_d = _time_ms(torch, lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=od, lse=ld),
-                        reps)
-        ms_m = _time_ms(torch, merged_fn(q, k, v, w, w.Nkv, om, lm), reps)
+        dense_fn = lambda: ca.chunk_attn_fwd(q, k, v, scale=w.scale, out=od, lse=ld)
+        merge_fn = merged_fn(q, k, v, w, w.Nkv, om, lm)
+        ms_d = _time_ms(torch, dense_fn, reps)
+        ms_m = _time_ms(torch, merge_fn, reps)
+        # the same calls replayed from a HIP graph: the launch-latency scale
+        # without the per-call host work (argument checks, ctypes, launch)
+        ms_dg = _time_ms(torch, _graphed(torch, dense_fn), reps)
+        ms_mg = _time_ms(torch, _graphed(torch, merge_fn), reps)
         out["tiny_dense"] = {"dense_us": round(ms_d * 1e3, 1),
                              "local_history_merge_us": round(ms_m * 1e3, 1),
+                             "dense_graph_us": round(ms_dg * 1e3, 1),
+                             "local_history_merge_graph_us": round(ms_mg * 1e3, 1),
                              "gflop": round(f / 1e9, 3)}
         rows = np.arange(w.Nq)
         probes["tiny_dense"] = _probe(od, ld, rows, {"kind": "dense", "w": w})
